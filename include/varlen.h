@@ -1,0 +1,202 @@
+/*
+ * varlen.h - C ABI of libvarlen, causal attention over packed variable-length
+ * sequences on AMD Instinct MI355X (gfx950), with the per-GPU pieces of the
+ * Ulysses and ring sequence-parallel schemes.
+ *
+ * Conventions shared by every entry point
+ *   - Tensors are caller-owned, contiguous device buffers (any allocator);
+ *     the library never frees them.  Layouts are row-major and named
+ *     outermost first: [T, H, d] means d fastest, then head, then token.
+ *   - cu_seqlens arrays are HOST int32 arrays of n_docs + 1 entries: entry 0
+ *     is 0, entries never decrease and the last one equals the total token
+ *     count (packing leaves no padding between documents).
+ *   - Every call validates its arguments first.  On failure nothing is
+ *     enqueued, a negative VL_E* code is returned and varlen_last_error()
+ *     describes it.  No C++ exception leaves the library.
+ *   - Device work is enqueued on `stream` (a hipStream_t; NULL = the null
+ *     stream) and the call returns without waiting, except the first call
+ *     with a new cu_seqlens pattern, which uploads that pattern's work list
+ *     synchronously and caches it (see varlen_cache_clear).
+ *   - bf16 values are IEEE binary32 truncated to the top 16 bits; results are
+ *     rounded to nearest-even.  Scores, softmax and accumulation are fp32.
+ */
+#ifndef VARLEN_H
+#define VARLEN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#if defined(__GNUC__)
+#define VL_API __attribute__((visibility("default")))
+#else
+#define VL_API
+#endif
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* element types */
+enum { VL_BF16 = 0, VL_F32 = 1 };
+
+/* status codes */
+enum {
+  VL_OK = 0,
+  VL_EINVAL = -1,       /* null pointer, bad enum or non-positive size      */
+  VL_ESHAPE = -2,       /* head counts / dims / degrees that do not fit      */
+  VL_ESEQLENS = -3,     /* cu_seqlens not a valid cumulative-length array    */
+  VL_EUNSUPPORTED = -4, /* valid but not implemented (e.g. head_dim 96)      */
+  VL_EHIP = -5,         /* a HIP runtime call or kernel launch failed        */
+  VL_EWORKSPACE = -6    /* workspace missing or smaller than required        */
+};
+
+/*
+ * varlen_attn_fwd - softmax attention of every query over the keys of its own
+ * document, optionally causal.
+ *
+ * Computes, for each document b, query row i < Lq(b) and q head h with kv head
+ * g = h / (Hq / Hkv):  S_ij = scale * q_i . k_j,  LSE_i = ln sum_j exp(S_ij),
+ * O_i = sum_j exp(S_ij - LSE_i) v_j over the visible keys j of the same
+ * document (scaled dot-product attention: BASP page, Section II-A; HSAP page,
+ * Section 2.2.1; documents kept apart by cumulative lengths: HSAP page,
+ * Section 2.1, and the segmented mask of packing, NSP page, Section 2.2).
+ * With causal != 0 key j is visible iff j <= i + (Lk - Lq) (diagonal aligned
+ * to the bottom-right).  A query with no visible key gets O = 0, LSE = -inf.
+ *
+ *   q            bf16 [total_q, n_heads_q, head_dim]
+ *   k, v         bf16 [total_k, n_heads_kv, head_dim]
+ *   cu_seqlens_q, cu_seqlens_k  host int32 [n_docs + 1]
+ *   head_dim     64 or 128; n_heads_q a multiple of n_heads_kv
+ *   softmax_scale  <= 0 selects 1/sqrt(head_dim)
+ *   out_dtype    VL_BF16 or VL_F32 (fp32 partials for a later attn_lse_merge)
+ *   out          [total_q, n_heads_q, head_dim] of out_dtype
+ *   lse          fp32 [n_heads_q, total_q], natural log
+ * Errors: VL_EINVAL, VL_ESHAPE, VL_ESEQLENS, VL_EUNSUPPORTED, VL_EHIP.
+ */
+VL_API int varlen_attn_fwd(const void* q, const void* k, const void* v,
+                    const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
+                    int32_t n_docs, int64_t total_q, int64_t total_k,
+                    int32_t n_heads_q, int32_t n_heads_kv, int32_t head_dim,
+                    float softmax_scale, int32_t causal, int32_t out_dtype,
+                    void* out, float* lse, void* stream);
+
+/*
+ * varlen_attn_bwd_workspace_size - bytes of device workspace varlen_attn_bwd
+ * needs for these sizes (fp32 per-row terms and kv-gradient accumulators).
+ */
+VL_API size_t varlen_attn_bwd_workspace_size(int64_t total_q, int64_t total_k,
+                                      int32_t n_heads_q, int32_t n_heads_kv,
+                                      int32_t head_dim);
+
+/*
+ * varlen_attn_bwd - exact gradients of the forward above for an upstream dO.
+ *
+ * The pages do not write the backward; it is the analytic gradient of the
+ * forward, with P recomputed from the saved LSE (the activation recompute the
+ * NSP page discusses in Sections 2.3 and 4.2.2):
+ *   D_i = dO_i . O_i,  P_ij = exp(S_ij - LSE_i),  dP_ij = dO_i . v_j,
+ *   dS_ij = P_ij (dP_ij - D_i),  dq_i = scale sum_j dS_ij k_j,
+ *   dk_j = scale sum_{h,i} dS_ij q_i,  dv_j = sum_{h,i} P_ij dO_i,
+ * the kv sums running over the q heads that share kv head g.
+ *
+ *   q, k, v, cu_*, sizes, scale, causal   exactly as passed to the forward
+ *   out          bf16 [total_q, n_heads_q, head_dim], the forward's O
+ *   dout         bf16 [total_q, n_heads_q, head_dim]
+ *   lse          fp32 [n_heads_q, total_q], the forward's LSE
+ *   dq           bf16 [total_q, n_heads_q, head_dim]
+ *   dk, dv       bf16 [total_k, n_heads_kv, head_dim]
+ *   workspace    device memory of at least varlen_attn_bwd_workspace_size()
+ *                bytes, 256-byte aligned; contents on entry are ignored
+ * Errors: as the forward, plus VL_EWORKSPACE.
+ */
+VL_API int varlen_attn_bwd(const void* q, const void* k, const void* v,
+                    const void* out, const void* dout, const float* lse,
+                    const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
+                    int32_t n_docs, int64_t total_q, int64_t total_k,
+                    int32_t n_heads_q, int32_t n_heads_kv, int32_t head_dim,
+                    float softmax_scale, int32_t causal,
+                    void* dq, void* dk, void* dv,
+                    void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * attn_lse_merge - combine partial attention results computed over disjoint
+ * key sets (the online combination of ring-style attention: HSAP page,
+ * Section 2.2.1; its copy/rescale step, Section 3.1 Table 1; BASP page,
+ * Section VII).  Per (row t, head h): M = max_k LSE_k, w_k = exp(LSE_k - M),
+ * LSE = M + ln sum_k w_k, O = sum_k w_k O_k / sum_k w_k; all LSE_k = -inf
+ * gives O = 0, LSE = -inf.
+ *
+ *   n_parts      1 .. 64
+ *   o_parts      HOST array of n_parts device pointers, each
+ *                [n_rows, n_heads, head_dim] of in_dtype (VL_BF16 / VL_F32)
+ *   lse_parts    HOST array of n_parts device pointers, each fp32 [n_heads, n_rows]
+ *   o_out        [n_rows, n_heads, head_dim] of out_dtype; may alias no input
+ *   lse_out      fp32 [n_heads, n_rows]
+ *   head_dim     a power of two from 4 to 256
+ * Errors: VL_EINVAL, VL_ESHAPE, VL_EUNSUPPORTED, VL_EHIP.
+ */
+VL_API int attn_lse_merge(int32_t n_parts, const void* const* o_parts,
+                   const float* const* lse_parts, int32_t in_dtype,
+                   int64_t n_rows, int32_t n_heads, int32_t head_dim,
+                   void* o_out, float* lse_out, int32_t out_dtype, void* stream);
+
+/*
+ * sp_seq2head - the local pack of the Ulysses layout change (HSAP page,
+ * Section 2.2.2, IntraSP: an n x H x d shard becomes N x H/P x d after the
+ * all-to-all; BASP page, Section II-C; NSP page, Section 2.1).
+ *   y[p, t, j, :] = x[t, p*h + j, :],  h = n_heads / sp_degree,
+ * so chunk p of y ([n_tokens, h, head_dim], contiguous) is what goes to rank p.
+ *
+ *   x            [n_tokens, n_heads, head_dim], elements of elem_bytes (2 or 4)
+ *   y            [sp_degree, n_tokens, n_heads / sp_degree, head_dim]
+ *   sp_degree    >= 1 and dividing n_heads
+ * x and y must not overlap.  Bit-exact copy.
+ * Errors: VL_EINVAL, VL_ESHAPE, VL_EHIP.
+ */
+VL_API int sp_seq2head(const void* x, void* y, int64_t n_tokens, int32_t n_heads,
+                int32_t head_dim, int32_t sp_degree, int32_t elem_bytes, void* stream);
+
+/*
+ * sp_head2seq - the inverse unpack after the output all-to-all:
+ *   x[t, p*h + j, :] = y[p, t, j, :].
+ * Arguments as sp_seq2head, with y the source and x the destination.
+ */
+VL_API int sp_head2seq(const void* y, void* x, int64_t n_tokens, int32_t n_heads,
+                int32_t head_dim, int32_t sp_degree, int32_t elem_bytes, void* stream);
+
+/*
+ * varlen_schedule_export - host-only: the work list the kernels run for these
+ * cu_seqlens (no GPU needed).  Documents are cut into query tiles of *bq rows
+ * and key tiles of *bk rows, never crossing a document; tile pairs holding no
+ * visible pair are skipped (the "N" blocks of the HSAP page, Figure 3).
+ *
+ *   pass 0 (forward):  items[4*i..] = (doc, q_tile, first kv tile, kv tiles)
+ *   pass 1 (backward): items[4*i..] = (doc, kv_tile, first q tile, q tiles)
+ *   ordered by decreasing tile count, then doc, then tile.
+ *   items        host int32 [4 * cap], or NULL to query *n_items only
+ *   useful_pairs visible (query, key) pairs per head
+ *   issued_pairs pairs covered by the issued tiles per head (tile area)
+ *   bq, bk       the tile sizes used for this head_dim and pass
+ * Errors: VL_EINVAL, VL_ESEQLENS, VL_EUNSUPPORTED, VL_EWORKSPACE (cap too small).
+ */
+VL_API int varlen_schedule_export(const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
+                           int32_t n_docs, int32_t causal, int32_t pass, int32_t head_dim,
+                           int32_t* items, int64_t cap, int64_t* n_items,
+                           int64_t* useful_pairs, int64_t* issued_pairs,
+                           int32_t* bq, int32_t* bk);
+
+/* Message of the last failed call on this thread ("" if none). */
+VL_API const char* varlen_last_error(void);
+
+/* Free the cached device work lists.  The caller guarantees no launched
+ * kernel still reads them (e.g. after a device or stream synchronize). */
+VL_API void varlen_cache_clear(void);
+
+/* ABI version, currently 1. */
+VL_API int varlen_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* VARLEN_H */

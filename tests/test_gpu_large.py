@@ -1,0 +1,161 @@
+"""GPU parity at full workload sizes, in the launch configuration the benchmark
+times, on seeded samples the oracle computes row by row, plus properties that
+hold at any size.
+
+  * one GPU's Ulysses share of a 393216-token sequence (4 q heads, 1 kv head);
+  * the ring share: query chunk 7 of a 262144-token sequence against its 8 key
+    chunks, merged with attn_lse_merge, versus full attention of those rows;
+  * the 131072-token Pareto batch (32/4 heads, Q x 3).
+Sampling: 512 query rows per q head (numpy default_rng(1), without
+replacement, heads in order); for dK/dV 512 key rows per kv head drawn from
+the keys at most `TAIL` positions before their document's end, whose exact
+gradient needs the forward of at most `TAIL` query rows.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import variable_length_sequence_amd as vl
+import workloads
+from gpu_helpers import (GRAD_REL_FRO, LSE_MAX_ABS, O_MAX_ABS, f64, lse_err, max_abs, rel_fro,
+                         require_gpu, say)
+
+pytestmark = pytest.mark.gpu
+
+N_SAMPLE = 512
+TAIL = 512
+
+
+def _np32(t):
+    return t.float().numpy()
+
+
+def _query_sample(total, hq, rng_seed=1):
+    rng = np.random.default_rng(rng_seed)
+    rows, heads = [], []
+    for h in range(hq):
+        r = np.sort(rng.choice(total, size=min(N_SAMPLE, total), replace=False))
+        rows.append(r)
+        heads.append(np.full(len(r), h))
+    return np.concatenate(rows), np.concatenate(heads)
+
+
+def _key_sample(cu, hkv, rng_seed=2):
+    cu = np.asarray(cu, np.int64)
+    cand = np.concatenate([np.arange(max(cu[i], cu[i + 1] - TAIL), cu[i + 1])
+                           for i in range(len(cu) - 1)])
+    rng = np.random.default_rng(rng_seed)
+    rows, heads = [], []
+    for g in range(hkv):
+        r = np.sort(rng.choice(cand, size=min(N_SAMPLE, len(cand)), replace=False))
+        rows.append(r)
+        heads.append(np.full(len(r), g))
+    return np.concatenate(rows), np.concatenate(heads)
+
+
+def _doc_sums(dk, dv, do, cu, grp):
+    """Properties at any size: per document and kv head, sum_j dK_j = 0 and
+    sum_j dV_j = sum over the group's q heads of sum_i dO_i."""
+    cu = np.asarray(cu, np.int64)
+    dk = dk.double()
+    dv = dv.double()
+    do = do.double()
+    worst_k = worst_v = 0.0
+    for i in range(len(cu) - 1):
+        s, e = int(cu[i]), int(cu[i + 1])
+        if e == s:
+            continue
+        L = e - s
+        for g in range(dk.shape[1]):
+            sk = dk[s:e, g].sum(0)
+            bound = GRAD_REL_FRO * np.sqrt(L) * float(dk[s:e, g].norm())
+            worst_k = max(worst_k, float(sk.norm()) / max(bound, 1e-30))
+            sv = dv[s:e, g].sum(0)
+            ref = do[s:e, g * grp:(g + 1) * grp].sum((0, 1))
+            bound = GRAD_REL_FRO * np.sqrt(L) * float(dv[s:e, g].norm())
+            worst_v = max(worst_v, float((sv - ref).norm()) / max(bound, 1e-30))
+    return worst_k, worst_v
+
+
+def _fwd_bwd(w, dev):
+    q, k, v, do = workloads.make_tensors(w)
+    cu = w.cu
+    qd, kd, vd, dod = q.to(dev), k.to(dev), v.to(dev), do.to(dev)
+    o, lse = vl.varlen_attn_fwd(qd, kd, vd, cu, cu, causal=True)
+    dq, dk, dv = vl.varlen_attn_bwd(qd, kd, vd, o, dod, lse, cu, cu, causal=True)
+    torch.cuda.synchronize()
+    return (q, k, v, do), dict(o=o.cpu(), lse=lse.cpu(), dq=dq.cpu(), dk=dk.cpu(), dv=dv.cpu())
+
+
+def _check_sampled(w, inputs, res):
+    q, k, v, do = inputs
+    cu = w.cu
+    qn, kn, vn, don = _np32(q), _np32(k), _np32(v), _np32(do)
+    rows, heads = _query_sample(w.total, w.hq)
+    say(f"{w.name}: oracle on {len(rows)} sampled query rows")
+    dq_r, o_r, lse_r = oracle.attn_bwd_dq_rows(qn, kn, vn, don, cu, cu, rows, heads)
+    eo = max_abs(f64(res["o"][rows, heads]), o_r)
+    el = lse_err(f64(res["lse"][heads, rows]), lse_r)
+    eq = rel_fro(f64(res["dq"][rows, heads]), dq_r)
+    krows, kheads = _key_sample(cu, w.hkv)
+    say(f"{w.name}: oracle on {len(krows)} sampled key rows")
+    dk_r, dv_r = oracle.attn_bwd_dkv_rows(qn, kn, vn, don, cu, cu, krows, kheads)
+    ek = rel_fro(f64(res["dk"][krows, kheads]), dk_r)
+    ev = rel_fro(f64(res["dv"][krows, kheads]), dv_r)
+    sk, sv = _doc_sums(res["dk"], res["dv"], do, cu, w.hq // w.hkv)
+    msg = (f"{w.name}: O {eo:.3e} LSE {el:.3e} dQ {eq:.3e} dK {ek:.3e} dV {ev:.3e} "
+           f"sum-dK {sk:.3f} sum-dV {sv:.3f} (of bound)")
+    say(msg)
+    assert eo <= O_MAX_ABS and el <= LSE_MAX_ABS, msg
+    assert max(eq, ek, ev) <= GRAD_REL_FRO, msg
+    assert sk <= 1.0 and sv <= 1.0, msg
+
+
+def test_ulysses_384k_share():
+    dev = require_gpu()
+    w = workloads.ulysses_384k()
+    say(f"{w.name}: T={w.total} hq={w.hq} hkv={w.hkv}")
+    inputs, res = _fwd_bwd(w, dev)
+    _check_sampled(w, inputs, res)
+
+
+def test_mixed_128k_pareto():
+    dev = require_gpu()
+    w = workloads.mixed_128k()
+    say(f"{w.name}: {len(w.lengths)} docs, max {max(w.lengths)}")
+    inputs, res = _fwd_bwd(w, dev)
+    _check_sampled(w, inputs, res)
+
+
+def test_ring_256k_chunk7_merge():
+    dev = require_gpu()
+    w = workloads.ring_256k()
+    n, c, qc = w.extra["n_chunks"], w.extra["chunk"], w.extra["q_chunk"]
+    q, k, v, _ = workloads.make_tensors(w, with_do=False)
+    say(f"{w.name}: query chunk {qc} of {n} x {c}")
+    qd = q[qc * c:(qc + 1) * c].contiguous().to(dev)
+    kd, vd = k.to(dev), v.to(dev)
+    one = np.array([0, c], np.int32)
+    parts_o, parts_l = [], []
+    for j in range(n):
+        o, l = vl.varlen_attn_fwd(qd, kd[j * c:(j + 1) * c], vd[j * c:(j + 1) * c], one, one,
+                                  causal=(j == qc), out_dtype=torch.float32)
+        parts_o.append(o)
+        parts_l.append(l)
+    om, lm = vl.attn_lse_merge(parts_o, parts_l, out_dtype=torch.bfloat16)
+    # the same rows as one call: bottom-right causal over all preceding keys
+    od, ld = vl.varlen_attn_fwd(qd, kd[:(qc + 1) * c], vd[:(qc + 1) * c], one,
+                                np.array([0, (qc + 1) * c], np.int32), causal=True)
+    torch.cuda.synchronize()
+    om, lm, od, ld = om.cpu(), lm.cpu(), od.cpu(), ld.cpu()
+    assert max_abs(f64(om), f64(od)) <= O_MAX_ABS
+    rows, heads = _query_sample(c, w.hq)
+    full_cu = np.array([0, n * c], np.int32)
+    o_r, lse_r = oracle.attn_fwd_rows(_np32(q), _np32(k), _np32(v), full_cu, full_cu,
+                                      rows + qc * c, heads)
+    eo = max_abs(f64(om[rows, heads]), o_r)
+    el = lse_err(f64(lm[heads, rows]), lse_r)
+    eo2 = max_abs(f64(od[rows, heads]), o_r)
+    say(f"{w.name}: merged O {eo:.3e} LSE {el:.3e}; single-call O {eo2:.3e}")
+    assert eo <= O_MAX_ABS and el <= LSE_MAX_ABS and eo2 <= O_MAX_ABS

@@ -1,0 +1,159 @@
+"""CPU tests of the C ABI: the library loads, exports what the header declares,
+the host scheduler matches the oracle bit for bit, and bad arguments are
+rejected with the documented codes before any GPU work."""
+import ctypes
+import os
+import re
+import subprocess
+
+import numpy as np
+import pytest
+
+import variable_length_sequence_amd as vl
+import workloads
+from oracle import schedule as osched
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "varlen.h")
+
+
+def _declared():
+    txt = open(HEADER).read()
+    return sorted(set(re.findall(r"VL_API\s+[\w\s\*]+?\b(\w+)\s*\(", txt)))
+
+
+def test_header_declares_the_boundary():
+    names = _declared()
+    assert set(names) == set(vl.EXPORTS)
+    for n in ("varlen_attn_fwd", "varlen_attn_bwd", "attn_lse_merge", "sp_seq2head", "sp_head2seq"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol():
+    L = vl.lib()
+    for n in _declared():
+        assert hasattr(L, n), n
+    out = subprocess.run(["nm", "-D", "--defined-only", vl.LIB_PATH], capture_output=True, text=True)
+    exported = {ln.split()[-1] for ln in out.stdout.splitlines() if " T " in ln}
+    assert exported == set(_declared())
+    assert vl.version() == 1
+
+
+def _cu(lengths):
+    return workloads.cu_seqlens(lengths)
+
+
+def _check_against_oracle(cq, ck, causal, d):
+    for p in (0, 1):
+        r = vl.varlen_schedule_export(cq, ck, causal, p, d)
+        fn = osched.fwd_items if p == 0 else osched.bwd_items
+        ref = fn(cq, ck, causal, r["bq"], r["bk"])
+        assert np.array_equal(r["items"], ref.reshape(-1, 4)), (p, causal)
+        assert r["useful_pairs"] == osched.visible_pairs(cq, ck, causal)
+        assert r["issued_pairs"] == osched.issued_pairs(ref, r["bq"], r["bk"])
+
+
+@pytest.mark.parametrize("name", ["tiny_256", "longtail_16k", "ulysses_384k", "mixed_128k"])
+def test_schedule_matches_oracle_on_workloads(name):
+    w = workloads.ALL[name]()
+    cu = w.cu
+    _check_against_oracle(cu, cu, True, w.d)
+
+
+def test_schedule_matches_oracle_ring_chunks():
+    c = 32768
+    _check_against_oracle(np.array([0, c], np.int32), np.array([0, c], np.int32), False, 128)
+    _check_against_oracle(np.array([0, c], np.int32), np.array([0, 8 * c], np.int32), True, 128)
+
+
+def test_schedule_matches_oracle_random(rng):
+    for _ in range(60):
+        n = int(rng.integers(1, 9))
+        lq = rng.integers(0, 700, size=n)
+        lk = lq.copy() if rng.random() < 0.5 else rng.integers(0, 700, size=n)
+        for causal in (True, False):
+            _check_against_oracle(_cu(lq), _cu(lk), causal, 128 if rng.random() < 0.5 else 64)
+
+
+def test_tiny_schedule_values():
+    r = vl.varlen_schedule_export(_cu([17, 64, 128, 47]), _cu([17, 64, 128, 47]), True, 0, 64)
+    assert r["useful_pairs"] == 11617
+    assert r["bq"] == 128 and r["bk"] == 64
+
+
+# ------------------------------------------------------------------ error codes
+FAKE = 1 << 20  # a 256-aligned non-null address; never dereferenced on these paths
+
+
+def _fwd(**kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, cu_q=np.array([0, 4], np.int32), cu_k=np.array([0, 4], np.int32),
+             n_docs=1, tq=4, tk=4, hq=4, hkv=2, d=128, scale=0.0, causal=1, od=0, out=FAKE, lse=FAKE)
+    a.update(kw)
+    p = lambda x: None if x is None else ctypes.c_void_p(x)
+    ip = lambda x: None if x is None else x.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))
+    rc = vl.lib().varlen_attn_fwd(p(a["q"]), p(a["k"]), p(a["v"]), ip(a["cu_q"]), ip(a["cu_k"]),
+                                  a["n_docs"], a["tq"], a["tk"], a["hq"], a["hkv"], a["d"],
+                                  a["scale"], a["causal"], a["od"], p(a["out"]), p(a["lse"]), None)
+    return rc, vl.lib().varlen_last_error().decode()
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), -1),
+    (dict(out=None), -1),
+    (dict(od=7), -1),
+    (dict(hkv=3), -2),
+    (dict(hq=0), -2),
+    (dict(d=96), -4),
+    (dict(cu_q=np.array([1, 4], np.int32)), -3),
+    (dict(cu_q=np.array([0, 5], np.int32)), -3),
+    (dict(cu_k=np.array([0, 2, 1], np.int32), n_docs=2, tk=1,
+          cu_q=np.array([0, 2, 4], np.int32)), -3),
+    (dict(q=FAKE + 2), -1),
+])
+def test_fwd_rejects_bad_arguments(kw, code):
+    rc, msg = _fwd(**kw)
+    assert rc == code and msg
+
+
+def test_bwd_rejects_small_workspace():
+    L = vl.lib()
+    cu = np.array([0, 8], np.int32)
+    ip = cu.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))
+    f = ctypes.c_void_p(FAKE)
+    need = L.varlen_attn_bwd_workspace_size(8, 8, 4, 2, 64)
+    assert need > 0
+    rc = L.varlen_attn_bwd(f, f, f, f, f, f, ip, ip, 1, 8, 8, 4, 2, 64, 0.0, 1, f, f, f, f, need - 1, None)
+    assert rc == -6
+    rc = L.varlen_attn_bwd(f, f, f, f, f, f, ip, ip, 1, 8, 8, 4, 2, 64, 0.0, 1, f, f, f, None, need, None)
+    assert rc == -6
+
+
+def test_permute_and_merge_reject_bad_arguments():
+    L = vl.lib()
+    f = ctypes.c_void_p(FAKE)
+    g = ctypes.c_void_p(FAKE * 64)
+    assert L.sp_seq2head(f, g, 16, 6, 128, 4, 2, None) == -2      # 4 does not divide 6
+    assert L.sp_seq2head(f, g, 16, 8, 128, 4, 3, None) == -1      # element size
+    assert L.sp_seq2head(f, f, 16, 8, 128, 4, 2, None) == -1      # overlap
+    assert L.sp_head2seq(None, g, 16, 8, 128, 4, 2, None) == -1
+    arr = (ctypes.c_void_p * 2)(FAKE, FAKE * 2)
+    assert L.attn_lse_merge(0, arr, arr, 1, 4, 2, 128, g, g, 1, None) == -1
+    assert L.attn_lse_merge(65, arr, arr, 1, 4, 2, 128, g, g, 1, None) == -1
+    assert L.attn_lse_merge(2, arr, arr, 1, 4, 2, 96, g, g, 1, None) == -4
+    assert L.attn_lse_merge(2, arr, arr, 5, 4, 2, 128, g, g, 1, None) == -1
+    assert L.attn_lse_merge(2, arr, arr, 1, 4, 2, 128, ctypes.c_void_p(FAKE), g, 1, None) == -1
+
+
+def test_schedule_export_rejects():
+    L = vl.lib()
+    bad = np.array([0, 3, 2], np.int32)
+    ok = np.array([0, 3, 5], np.int32)
+    n = ctypes.c_int64()
+    ip = lambda a: a.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))
+    assert L.varlen_schedule_export(ip(bad), ip(ok), 2, 1, 0, 128, None, 0, ctypes.byref(n),
+                                    None, None, None, None) == -3
+    assert L.varlen_schedule_export(ip(ok), ip(ok), 2, 1, 2, 128, None, 0, ctypes.byref(n),
+                                    None, None, None, None) == -1
+    items = np.zeros(4, np.int32)
+    assert L.varlen_schedule_export(ip(ok), ip(ok), 2, 1, 0, 128, ip(items), 0, ctypes.byref(n),
+                                    None, None, None, None) == -6

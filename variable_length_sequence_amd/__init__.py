@@ -1,0 +1,236 @@
+"""Python binding of libvarlen: packed variable-length causal attention on MI355X.
+
+Argument marshalling only.  Every step of the computation runs in the HIP
+kernels of ``libvarlen.so`` (built in-tree by ``build.py``); PyTorch supplies
+device memory and the current stream.  There is no CPU fallback: if the
+library is missing every call raises.
+
+Entry points (same names as the C ABI in ``include/varlen.h``):
+  varlen_attn_fwd(q, k, v, cu_q, cu_k, causal=True, scale=None, out_dtype=bf16) -> (o, lse)
+  varlen_attn_bwd(q, k, v, o, do, lse, cu_q, cu_k, causal=True, scale=None) -> (dq, dk, dv)
+  attn_lse_merge(o_parts, lse_parts, out_dtype=bf16) -> (o, lse)
+  sp_seq2head(x, sp_degree) -> y ;  sp_head2seq(y) -> x
+  varlen_schedule_export(cu_q, cu_k, causal, pass_, head_dim) -> dict (host only)
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import List, Optional, Sequence
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libvarlen.so")
+
+VL_BF16, VL_F32 = 0, 1
+STATUS = {0: "VL_OK", -1: "VL_EINVAL", -2: "VL_ESHAPE", -3: "VL_ESEQLENS",
+          -4: "VL_EUNSUPPORTED", -5: "VL_EHIP", -6: "VL_EWORKSPACE"}
+
+EXPORTS = ["varlen_attn_fwd", "varlen_attn_bwd_workspace_size", "varlen_attn_bwd",
+           "attn_lse_merge", "sp_seq2head", "sp_head2seq", "varlen_schedule_export",
+           "varlen_last_error", "varlen_cache_clear", "varlen_version"]
+
+
+class VarlenError(RuntimeError):
+    """A libvarlen call returned a negative status."""
+
+    def __init__(self, code: int, msg: str):
+        super().__init__(f"{STATUS.get(code, code)}: {msg}")
+        self.code = code
+
+
+_lib = None
+
+
+def lib():
+    """The loaded libvarlen.so (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                           "`python -m variable_length_sequence_amd.build`")
+    L = ctypes.CDLL(LIB_PATH)
+    vp, i32, i64, f32 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_float
+    pi32, pi64 = ctypes.POINTER(ctypes.c_int32), ctypes.POINTER(ctypes.c_int64)
+    L.varlen_attn_fwd.argtypes = [vp, vp, vp, pi32, pi32, i32, i64, i64, i32, i32, i32, f32, i32,
+                                  i32, vp, vp, vp]
+    L.varlen_attn_fwd.restype = ctypes.c_int
+    L.varlen_attn_bwd_workspace_size.argtypes = [i64, i64, i32, i32, i32]
+    L.varlen_attn_bwd_workspace_size.restype = ctypes.c_size_t
+    L.varlen_attn_bwd.argtypes = [vp, vp, vp, vp, vp, vp, pi32, pi32, i32, i64, i64, i32, i32, i32,
+                                  f32, i32, vp, vp, vp, vp, ctypes.c_size_t, vp]
+    L.varlen_attn_bwd.restype = ctypes.c_int
+    L.attn_lse_merge.argtypes = [i32, ctypes.POINTER(vp), ctypes.POINTER(vp), i32, i64, i32, i32,
+                                 vp, vp, i32, vp]
+    L.attn_lse_merge.restype = ctypes.c_int
+    for n in ("sp_seq2head", "sp_head2seq"):
+        getattr(L, n).argtypes = [vp, vp, i64, i32, i32, i32, i32, vp]
+        getattr(L, n).restype = ctypes.c_int
+    L.varlen_schedule_export.argtypes = [pi32, pi32, i32, i32, i32, i32, pi32, i64, pi64, pi64,
+                                         pi64, pi32, pi32]
+    L.varlen_schedule_export.restype = ctypes.c_int
+    L.varlen_last_error.argtypes = []
+    L.varlen_last_error.restype = ctypes.c_char_p
+    L.varlen_cache_clear.argtypes = []
+    L.varlen_cache_clear.restype = None
+    L.varlen_version.argtypes = []
+    L.varlen_version.restype = ctypes.c_int
+    _lib = L
+    return L
+
+
+def _check(rc: int):
+    if rc != 0:
+        raise VarlenError(rc, lib().varlen_last_error().decode())
+
+
+def _cu_host(cu) -> np.ndarray:
+    """cu_seqlens as a contiguous host int32 array (a device tensor is copied, which syncs)."""
+    try:
+        import torch
+        if isinstance(cu, torch.Tensor):
+            cu = cu.detach().to("cpu")
+            return np.ascontiguousarray(cu.numpy().astype(np.int32))
+    except ImportError:  # pragma: no cover
+        pass
+    return np.ascontiguousarray(np.asarray(cu, dtype=np.int32))
+
+
+def _iptr(a: np.ndarray):
+    return a.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))
+
+
+def _stream():
+    import torch
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _dev_ptr(t) -> ctypes.c_void_p:
+    if not t.is_cuda:
+        raise ValueError("tensors must live on the GPU")
+    if not t.is_contiguous():
+        raise ValueError("tensors must be contiguous")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def varlen_attn_fwd(q, k, v, cu_q, cu_k, causal: bool = True, scale: Optional[float] = None,
+                    out_dtype=None, out=None, lse=None):
+    """Packed varlen attention forward.  q [Tq,Hq,d], k/v [Tk,Hkv,d] bf16 -> (o, lse[Hq,Tq])."""
+    import torch
+    out_dtype = torch.bfloat16 if out_dtype is None else out_dtype
+    cq, ck = _cu_host(cu_q), _cu_host(cu_k)
+    tq, hq, d = q.shape
+    tk, hkv, _ = k.shape
+    for t in (q, k, v):
+        if t.dtype != torch.bfloat16:
+            raise TypeError("q, k and v must be bfloat16")
+    if out is None:
+        out = torch.empty((tq, hq, d), dtype=out_dtype, device=q.device)
+    if lse is None:
+        lse = torch.empty((hq, tq), dtype=torch.float32, device=q.device)
+    od = VL_F32 if out.dtype == torch.float32 else VL_BF16
+    _check(lib().varlen_attn_fwd(_dev_ptr(q), _dev_ptr(k), _dev_ptr(v), _iptr(cq), _iptr(ck),
+                                 len(cq) - 1, tq, tk, hq, hkv, d, float(scale or 0.0), int(causal),
+                                 od, _dev_ptr(out), _dev_ptr(lse), _stream()))
+    return out, lse
+
+
+def varlen_attn_bwd(q, k, v, o, do, lse, cu_q, cu_k, causal: bool = True,
+                    scale: Optional[float] = None, workspace=None):
+    """Packed varlen attention backward -> (dq, dk, dv), bf16."""
+    import torch
+    cq, ck = _cu_host(cu_q), _cu_host(cu_k)
+    tq, hq, d = q.shape
+    tk, hkv, _ = k.shape
+    dq = torch.empty_like(q)
+    dk = torch.empty_like(k)
+    dv = torch.empty_like(v)
+    need = lib().varlen_attn_bwd_workspace_size(tq, tk, hq, hkv, d)
+    if workspace is None:
+        workspace = torch.empty(max(int(need), 256), dtype=torch.uint8, device=q.device)
+    _check(lib().varlen_attn_bwd(_dev_ptr(q), _dev_ptr(k), _dev_ptr(v), _dev_ptr(o), _dev_ptr(do),
+                                 _dev_ptr(lse), _iptr(cq), _iptr(ck), len(cq) - 1, tq, tk, hq, hkv,
+                                 d, float(scale or 0.0), int(causal), _dev_ptr(dq), _dev_ptr(dk),
+                                 _dev_ptr(dv), _dev_ptr(workspace), workspace.numel(), _stream()))
+    return dq, dk, dv
+
+
+def bwd_workspace_bytes(tq: int, tk: int, hq: int, hkv: int, d: int) -> int:
+    return int(lib().varlen_attn_bwd_workspace_size(tq, tk, hq, hkv, d))
+
+
+def attn_lse_merge(o_parts: Sequence, lse_parts: Sequence, out_dtype=None, out=None, lse_out=None):
+    """Merge partial (O [T,H,d], LSE [H,T]) results over disjoint key sets."""
+    import torch
+    out_dtype = torch.bfloat16 if out_dtype is None else out_dtype
+    n = len(o_parts)
+    if n == 0 or n != len(lse_parts):
+        raise ValueError("need the same positive number of O and LSE partials")
+    t, h, d = o_parts[0].shape
+    in_dt = o_parts[0].dtype
+    for o, l in zip(o_parts, lse_parts):
+        if o.shape != (t, h, d) or o.dtype != in_dt or l.shape != (h, t) or l.dtype != torch.float32:
+            raise ValueError("partials must share shape and dtype; LSE is fp32 [H, T]")
+    if out is None:
+        out = torch.empty((t, h, d), dtype=out_dtype, device=o_parts[0].device)
+    if lse_out is None:
+        lse_out = torch.empty((h, t), dtype=torch.float32, device=o_parts[0].device)
+    op = (ctypes.c_void_p * n)(*[_dev_ptr(o).value for o in o_parts])
+    lp = (ctypes.c_void_p * n)(*[_dev_ptr(l).value for l in lse_parts])
+    idt = VL_F32 if in_dt == torch.float32 else VL_BF16
+    odt = VL_F32 if out.dtype == torch.float32 else VL_BF16
+    _check(lib().attn_lse_merge(n, op, lp, idt, t, h, d, _dev_ptr(out), _dev_ptr(lse_out), odt,
+                                _stream()))
+    return out, lse_out
+
+
+def sp_seq2head(x, sp_degree: int, out=None):
+    """[n, H, d] -> [P, n, H/P, d] (chunk p = heads p*H/P .. (p+1)*H/P - 1)."""
+    import torch
+    n, H, d = x.shape
+    if H % sp_degree:
+        raise ValueError("sp_degree must divide the head count")
+    if out is None:
+        out = torch.empty((sp_degree, n, H // sp_degree, d), dtype=x.dtype, device=x.device)
+    _check(lib().sp_seq2head(_dev_ptr(x), _dev_ptr(out), n, H, d, sp_degree, x.element_size(),
+                             _stream()))
+    return out
+
+
+def sp_head2seq(y, out=None):
+    """[P, n, h, d] -> [n, P*h, d], the inverse of sp_seq2head."""
+    import torch
+    P, n, h, d = y.shape
+    if out is None:
+        out = torch.empty((n, P * h, d), dtype=y.dtype, device=y.device)
+    _check(lib().sp_head2seq(_dev_ptr(y), _dev_ptr(out), n, P * h, d, P, y.element_size(),
+                             _stream()))
+    return out
+
+
+def varlen_schedule_export(cu_q, cu_k, causal: bool, pass_: int, head_dim: int) -> dict:
+    """Host-only: the work list and pair counts the kernels use (no GPU needed)."""
+    cq, ck = _cu_host(cu_q), _cu_host(cu_k)
+    n = ctypes.c_int64(0)
+    useful, issued = ctypes.c_int64(0), ctypes.c_int64(0)
+    bq, bk = ctypes.c_int32(0), ctypes.c_int32(0)
+    L = lib()
+    _check(L.varlen_schedule_export(_iptr(cq), _iptr(ck), len(cq) - 1, int(causal), pass_,
+                                    head_dim, None, 0, ctypes.byref(n), None, None, None, None))
+    items = np.zeros((max(n.value, 1), 4), dtype=np.int32)
+    _check(L.varlen_schedule_export(_iptr(cq), _iptr(ck), len(cq) - 1, int(causal), pass_,
+                                    head_dim, _iptr(items), n.value, ctypes.byref(n),
+                                    ctypes.byref(useful), ctypes.byref(issued), ctypes.byref(bq),
+                                    ctypes.byref(bk)))
+    return {"items": items[:n.value], "useful_pairs": useful.value, "issued_pairs": issued.value,
+            "bq": bq.value, "bk": bk.value}
+
+
+def cache_clear():
+    lib().varlen_cache_clear()
+
+
+def version() -> int:
+    return int(lib().varlen_version())

@@ -1,0 +1,70 @@
+"""Compile libvarlen.so for gfx950 with hipcc, in-tree.
+
+``python -m variable_length_sequence_amd.build`` (or ``build()``) compiles every
+source under ``csrc/`` to an object in ``_build/`` and links
+``variable_length_sequence_amd/libvarlen.so``.  It always recompiles.
+"""
+from __future__ import annotations
+
+import os
+import shutil
+import subprocess
+import sys
+from concurrent.futures import ThreadPoolExecutor
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG)
+CSRC = os.path.join(PKG, "csrc")
+BUILD = os.path.join(ROOT, "_build")
+LIB = os.path.join(PKG, "libvarlen.so")
+
+SOURCES = ["scheduler.cpp", "api.cpp", "sp_permute.hip", "lse_merge.hip", "attn_fwd.hip",
+           "attn_bwd.hip"]
+
+ARCH = "gfx950"
+COMMON = ["-O3", "-fPIC", "-std=c++17", "-fvisibility=hidden", "-Wall", "-Wno-unused-function",
+          f"--offload-arch={ARCH}"]
+# gfx950 code is built without packed fp32 ALU ops (v_pk_*_f32)
+DEVICE = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
+
+
+def hipcc() -> str:
+    for cand in (os.environ.get("HIPCC"), "/opt/rocm/bin/hipcc", shutil.which("hipcc")):
+        if cand and os.path.exists(cand):
+            return cand
+    raise RuntimeError("hipcc not found (ROCm is required to build libvarlen)")
+
+
+def _compile(src: str, verbose: bool) -> str:
+    obj = os.path.join(BUILD, src + ".o")
+    cmd = [hipcc(), *COMMON, "-I", os.path.join(ROOT, "include")]
+    if src.endswith(".hip"):
+        cmd += ["-x", "hip", *DEVICE]
+    cmd += ["-c", os.path.join(CSRC, src), "-o", obj]
+    if verbose:
+        print(" ".join(cmd), file=sys.stderr)
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    err = "\n".join(ln for ln in res.stderr.splitlines()
+                    if "packed-fp32-ops" not in ln and ln.strip())
+    if res.returncode != 0:
+        raise RuntimeError(f"compiling {src} failed:\n{err}")
+    if err and verbose:
+        print(err, file=sys.stderr)
+    return obj
+
+
+def build(verbose: bool = False) -> str:
+    os.makedirs(BUILD, exist_ok=True)
+    with ThreadPoolExecutor(max_workers=min(8, len(SOURCES))) as ex:
+        objs = list(ex.map(lambda s: _compile(s, verbose), SOURCES))
+    tmp = LIB + ".tmp"
+    cmd = [hipcc(), "-shared", "-fPIC", f"--offload-arch={ARCH}", *objs, "-o", tmp]
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        raise RuntimeError("linking libvarlen.so failed:\n" + res.stderr)
+    os.replace(tmp, LIB)
+    return LIB
+
+
+if __name__ == "__main__":
+    print(build(verbose="-v" in sys.argv))

@@ -1,0 +1,348 @@
+// C ABI of libvarlen (declared in include/varlen.h): argument validation, the
+// cached device work lists, and dispatch to the HIP kernels.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstring>
+#include <map>
+#include <mutex>
+#include <string>
+#include <vector>
+
+#include "../../include/varlen.h"
+#include "launch.h"
+#include "scheduler.h"
+
+namespace {
+
+thread_local std::string g_err;
+
+int fail(int code, const std::string& msg) {
+  g_err = msg;
+  return code;
+}
+
+int hip_fail(hipError_t e, const char* what) {
+  g_err = std::string(what) + ": " + hipGetErrorString(e);
+  return VL_EHIP;
+}
+
+// ------------------------------------------------------------ work-list cache
+struct Plan {
+  vl::DevItem* dev = nullptr;
+  int32_t n = 0;
+  int32_t max_count = 0;
+  int64_t total_count = 0;
+};
+
+std::mutex g_mu;
+std::map<std::string, Plan> g_plans;
+constexpr size_t kMaxPlans = 4096;
+
+std::string plan_key(int dev, int pass, int causal, const int32_t* cu_q, const int32_t* cu_k,
+                     int32_t n_docs) {
+  std::string key;
+  const int32_t hdr[4] = {dev, pass, causal, n_docs};
+  key.append(reinterpret_cast<const char*>(hdr), sizeof(hdr));
+  key.append(reinterpret_cast<const char*>(cu_q), sizeof(int32_t) * size_t(n_docs + 1));
+  key.append(reinterpret_cast<const char*>(cu_k), sizeof(int32_t) * size_t(n_docs + 1));
+  return key;
+}
+
+void clear_plans_locked() {
+  for (auto& kv : g_plans)
+    if (kv.second.dev) (void)hipFree(kv.second.dev);
+  g_plans.clear();
+}
+
+// pass 0: forward / dQ list (query tiles); pass 1: dK/dV list (key tiles)
+int get_plan(int pass, int causal, const int32_t* cu_q, const int32_t* cu_k, int32_t n_docs,
+             Plan& out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  const std::string key = plan_key(dev, pass, causal, cu_q, cu_k, n_docs);
+  std::lock_guard<std::mutex> lock(g_mu);
+  auto itp = g_plans.find(key);
+  if (itp != g_plans.end()) {
+    out = itp->second;
+    return VL_OK;
+  }
+  const std::vector<vl::Doc> docs = vl::doc_table(cu_q, cu_k, n_docs);
+  const std::vector<vl::Item> items =
+      pass == 0 ? vl::fwd_items(docs, causal != 0, vl::kFwdBQ, vl::kFwdBK)
+                : vl::bwd_items(docs, causal != 0, vl::kBwdBQ, vl::kBwdBK);
+  const std::vector<vl::DevItem> di = vl::device_items(docs, items);
+  Plan p;
+  p.n = int32_t(di.size());
+  for (const auto& it : items) {
+    p.max_count = std::max(p.max_count, it.count);
+    p.total_count += it.count;
+  }
+  if (!di.empty()) {
+    // a new pattern: drain the device before touching the allocator when the cache is full
+    if (g_plans.size() >= kMaxPlans) {
+      (void)hipDeviceSynchronize();
+      clear_plans_locked();
+    }
+    e = hipMalloc(&p.dev, di.size() * sizeof(vl::DevItem));
+    if (e != hipSuccess) return hip_fail(e, "hipMalloc(work list)");
+    e = hipMemcpy(p.dev, di.data(), di.size() * sizeof(vl::DevItem), hipMemcpyHostToDevice);
+    if (e != hipSuccess) {
+      (void)hipFree(p.dev);
+      return hip_fail(e, "hipMemcpy(work list)");
+    }
+  }
+  g_plans.emplace(key, p);
+  out = p;
+  return VL_OK;
+}
+
+// ------------------------------------------------------------ validation
+int check_attn_common(const void* q, const void* k, const void* v, const int32_t* cu_q,
+                      const int32_t* cu_k, int32_t n_docs, int64_t total_q, int64_t total_k,
+                      int32_t hq, int32_t hkv, int32_t d) {
+  if (!q || !k || !v) return fail(VL_EINVAL, "q, k and v must be non-null device pointers");
+  if (!cu_q || !cu_k) return fail(VL_EINVAL, "cu_seqlens_q and cu_seqlens_k must be non-null");
+  if (n_docs < 0) return fail(VL_EINVAL, "n_docs must be >= 0");
+  if (total_q < 0 || total_k < 0) return fail(VL_EINVAL, "total token counts must be >= 0");
+  if (total_q > INT32_MAX || total_k > INT32_MAX)
+    return fail(VL_ESHAPE, "total token counts must fit int32");
+  if (hq <= 0 || hkv <= 0) return fail(VL_ESHAPE, "head counts must be positive");
+  if (hq % hkv != 0) return fail(VL_ESHAPE, "n_heads_q must be a multiple of n_heads_kv");
+  if (d != 64 && d != 128) return fail(VL_EUNSUPPORTED, "head_dim must be 64 or 128");
+  std::string err;
+  if (!vl::validate_cu(cu_q, n_docs, total_q, err)) return fail(VL_ESEQLENS, "cu_seqlens_q: " + err);
+  if (!vl::validate_cu(cu_k, n_docs, total_k, err)) return fail(VL_ESEQLENS, "cu_seqlens_k: " + err);
+  const uintptr_t al = reinterpret_cast<uintptr_t>(q) | reinterpret_cast<uintptr_t>(k) |
+                       reinterpret_cast<uintptr_t>(v);
+  if (al % 16) return fail(VL_EINVAL, "q, k and v must be 16-byte aligned");
+  return VL_OK;
+}
+
+float resolve_scale(float s, int d) { return s > 0.f ? s : 1.0f / std::sqrt(float(d)); }
+
+size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+}  // namespace
+
+extern "C" {
+
+const char* varlen_last_error(void) { return g_err.c_str(); }
+
+int varlen_version(void) { return 1; }
+
+void varlen_cache_clear(void) {
+  std::lock_guard<std::mutex> lock(g_mu);
+  clear_plans_locked();
+}
+
+int varlen_attn_fwd(const void* q, const void* k, const void* v, const int32_t* cu_seqlens_q,
+                    const int32_t* cu_seqlens_k, int32_t n_docs, int64_t total_q, int64_t total_k,
+                    int32_t n_heads_q, int32_t n_heads_kv, int32_t head_dim, float softmax_scale,
+                    int32_t causal, int32_t out_dtype, void* out, float* lse, void* stream) {
+  try {
+    g_err.clear();
+    int rc = check_attn_common(q, k, v, cu_seqlens_q, cu_seqlens_k, n_docs, total_q, total_k,
+                               n_heads_q, n_heads_kv, head_dim);
+    if (rc) return rc;
+    if (out_dtype != VL_BF16 && out_dtype != VL_F32) return fail(VL_EINVAL, "out_dtype must be VL_BF16 or VL_F32");
+    if (!out || !lse) return fail(VL_EINVAL, "out and lse must be non-null");
+    if (reinterpret_cast<uintptr_t>(out) % 16) return fail(VL_EINVAL, "out must be 16-byte aligned");
+    if (total_q == 0) return VL_OK;
+    Plan p;
+    rc = get_plan(0, causal != 0, cu_seqlens_q, cu_seqlens_k, n_docs, p);
+    if (rc) return rc;
+    vl::AttnShape s{total_q, total_k, n_heads_q, n_heads_kv, head_dim,
+                    resolve_scale(softmax_scale, head_dim), causal != 0};
+    hipError_t e = vl::launch_attn_fwd(s, q, k, v, p.dev, p.n, out_dtype, out, lse,
+                                       reinterpret_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(e, "attn_fwd launch");
+    return VL_OK;
+  } catch (const std::exception& ex) {
+    return fail(VL_EHIP, std::string("internal error: ") + ex.what());
+  } catch (...) {
+    return fail(VL_EHIP, "internal error");
+  }
+}
+
+size_t varlen_attn_bwd_workspace_size(int64_t total_q, int64_t total_k, int32_t n_heads_q,
+                                      int32_t n_heads_kv, int32_t head_dim) {
+  if (total_q < 0 || total_k < 0 || n_heads_q <= 0 || n_heads_kv <= 0 || head_dim <= 0) return 0;
+  return align256(size_t(total_q) * size_t(n_heads_q) * 4) +
+         align256(2 * size_t(total_k) * size_t(n_heads_kv) * size_t(head_dim) * 4);
+}
+
+int varlen_attn_bwd(const void* q, const void* k, const void* v, const void* out, const void* dout,
+                    const float* lse, const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
+                    int32_t n_docs, int64_t total_q, int64_t total_k, int32_t n_heads_q,
+                    int32_t n_heads_kv, int32_t head_dim, float softmax_scale, int32_t causal,
+                    void* dq, void* dk, void* dv, void* workspace, size_t workspace_bytes,
+                    void* stream) {
+  try {
+    g_err.clear();
+    int rc = check_attn_common(q, k, v, cu_seqlens_q, cu_seqlens_k, n_docs, total_q, total_k,
+                               n_heads_q, n_heads_kv, head_dim);
+    if (rc) return rc;
+    if (!out || !dout || !lse || !dq || !dk || !dv)
+      return fail(VL_EINVAL, "out, dout, lse, dq, dk and dv must be non-null");
+    const uintptr_t al = reinterpret_cast<uintptr_t>(out) | reinterpret_cast<uintptr_t>(dout) |
+                         reinterpret_cast<uintptr_t>(dq) | reinterpret_cast<uintptr_t>(dk) |
+                         reinterpret_cast<uintptr_t>(dv);
+    if (al % 16) return fail(VL_EINVAL, "out, dout, dq, dk and dv must be 16-byte aligned");
+    const size_t need = varlen_attn_bwd_workspace_size(total_q, total_k, n_heads_q, n_heads_kv, head_dim);
+    if (!workspace || workspace_bytes < need)
+      return fail(VL_EWORKSPACE, "workspace must hold at least " + std::to_string(need) + " bytes");
+    if (reinterpret_cast<uintptr_t>(workspace) % 256) return fail(VL_EWORKSPACE, "workspace must be 256-byte aligned");
+    if (total_q == 0 && total_k == 0) return VL_OK;
+    Plan pf, pb;
+    rc = get_plan(0, causal != 0, cu_seqlens_q, cu_seqlens_k, n_docs, pf);
+    if (rc) return rc;
+    rc = get_plan(1, causal != 0, cu_seqlens_q, cu_seqlens_k, n_docs, pb);
+    if (rc) return rc;
+    hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+    // dK/dV of kv tiles that no query tile reaches are zeros written by the kernel
+    int dev = 0, n_cu = 256;
+    (void)hipGetDevice(&dev);
+    (void)hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev);
+    // split the q heads of a group over workgroups when one item would
+    // otherwise outlast the average per-CU share of the whole pass
+    const int grp = n_heads_q / n_heads_kv;
+    int split = 1;
+    {
+      const double total = double(pb.total_count) * grp * n_heads_kv;
+      const double per_cu = total / double(n_cu);
+      while (split < grp && grp % (split * 2) == 0 &&
+             double(pb.max_count) * grp / split > per_cu)
+        split *= 2;
+    }
+    float* delta = reinterpret_cast<float*>(workspace);
+    float* dkv_acc = reinterpret_cast<float*>(reinterpret_cast<char*>(workspace) +
+                                              align256(size_t(total_q) * size_t(n_heads_q) * 4));
+    vl::AttnShape s{total_q, total_k, n_heads_q, n_heads_kv, head_dim,
+                    resolve_scale(softmax_scale, head_dim), causal != 0};
+    hipError_t e = vl::launch_attn_bwd(s, q, k, v, out, dout, lse, pf.dev, pf.n, pb.dev, pb.n,
+                                       split, dq, dk, dv, delta, dkv_acc, st);
+    if (e != hipSuccess) return hip_fail(e, "attn_bwd launch");
+    return VL_OK;
+  } catch (const std::exception& ex) {
+    return fail(VL_EHIP, std::string("internal error: ") + ex.what());
+  } catch (...) {
+    return fail(VL_EHIP, "internal error");
+  }
+}
+
+int attn_lse_merge(int32_t n_parts, const void* const* o_parts, const float* const* lse_parts,
+                   int32_t in_dtype, int64_t n_rows, int32_t n_heads, int32_t head_dim,
+                   void* o_out, float* lse_out, int32_t out_dtype, void* stream) {
+  try {
+    g_err.clear();
+    if (n_parts < 1 || n_parts > vl::kMaxMergeParts)
+      return fail(VL_EINVAL, "n_parts must be in [1, 64]");
+    if (!o_parts || !lse_parts || !o_out || !lse_out)
+      return fail(VL_EINVAL, "pointer arguments must be non-null");
+    if ((in_dtype != VL_BF16 && in_dtype != VL_F32) || (out_dtype != VL_BF16 && out_dtype != VL_F32))
+      return fail(VL_EINVAL, "dtypes must be VL_BF16 or VL_F32");
+    if (n_rows < 0 || n_heads <= 0) return fail(VL_ESHAPE, "n_rows must be >= 0 and n_heads > 0");
+    if (head_dim < 4 || head_dim > 256 || (head_dim & (head_dim - 1)))
+      return fail(VL_EUNSUPPORTED, "head_dim must be a power of two in [4, 256]");
+    const uintptr_t need_in = in_dtype == VL_F32 ? 16 : 8;
+    const uintptr_t need_out = out_dtype == VL_F32 ? 16 : 8;
+    for (int i = 0; i < n_parts; ++i) {
+      if (!o_parts[i] || !lse_parts[i]) return fail(VL_EINVAL, "partial pointers must be non-null");
+      if (reinterpret_cast<uintptr_t>(o_parts[i]) % need_in)
+        return fail(VL_EINVAL, "partial O buffers must be aligned to 4 elements");
+      if (o_parts[i] == o_out) return fail(VL_EINVAL, "o_out must not alias a partial");
+    }
+    if (reinterpret_cast<uintptr_t>(o_out) % need_out) return fail(VL_EINVAL, "o_out must be aligned to 4 elements");
+    hipError_t e = vl::launch_lse_merge(n_parts, o_parts, lse_parts, in_dtype, n_rows, n_heads,
+                                        head_dim, o_out, lse_out, out_dtype,
+                                        reinterpret_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(e, "lse_merge launch");
+    return VL_OK;
+  } catch (...) {
+    return fail(VL_EHIP, "internal error");
+  }
+}
+
+static int permute_common(const void* src, void* dst, int64_t n_tokens, int32_t n_heads,
+                          int32_t head_dim, int32_t sp_degree, int32_t elem_bytes, int dir,
+                          void* stream) {
+  g_err.clear();
+  if (n_tokens < 0 || n_heads <= 0 || head_dim <= 0) return fail(VL_ESHAPE, "sizes must be positive");
+  if (n_tokens > 0 && (!src || !dst)) return fail(VL_EINVAL, "x and y must be non-null");
+  if (elem_bytes != 2 && elem_bytes != 4) return fail(VL_EINVAL, "elem_bytes must be 2 or 4");
+  if (sp_degree <= 0 || n_heads % sp_degree) return fail(VL_ESHAPE, "sp_degree must divide n_heads");
+  if (n_tokens == 0) return VL_OK;
+  const int64_t bytes = n_tokens * n_heads * int64_t(head_dim) * elem_bytes;
+  const char* s = reinterpret_cast<const char*>(src);
+  const char* d = reinterpret_cast<const char*>(dst);
+  if (n_tokens > 0 && s < d + bytes && d < s + bytes) return fail(VL_EINVAL, "x and y must not overlap");
+  if (int64_t(n_heads) * head_dim * elem_bytes >= (int64_t(1) << 30))
+    return fail(VL_ESHAPE, "a token row must be below 1 GiB");
+  if (n_tokens >= (int64_t(1) << 31)) return fail(VL_ESHAPE, "n_tokens must fit int32");
+  hipError_t e = vl::launch_sp_permute(src, dst, n_tokens, n_heads, head_dim, sp_degree, elem_bytes,
+                                       dir, reinterpret_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "sp_permute launch");
+  return VL_OK;
+}
+
+int sp_seq2head(const void* x, void* y, int64_t n_tokens, int32_t n_heads, int32_t head_dim,
+                int32_t sp_degree, int32_t elem_bytes, void* stream) {
+  try {
+    return permute_common(x, y, n_tokens, n_heads, head_dim, sp_degree, elem_bytes, 0, stream);
+  } catch (...) {
+    return fail(VL_EHIP, "internal error");
+  }
+}
+
+int sp_head2seq(const void* y, void* x, int64_t n_tokens, int32_t n_heads, int32_t head_dim,
+                int32_t sp_degree, int32_t elem_bytes, void* stream) {
+  try {
+    return permute_common(y, x, n_tokens, n_heads, head_dim, sp_degree, elem_bytes, 1, stream);
+  } catch (...) {
+    return fail(VL_EHIP, "internal error");
+  }
+}
+
+int varlen_schedule_export(const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
+                           int32_t n_docs, int32_t causal, int32_t pass, int32_t head_dim,
+                           int32_t* items, int64_t cap, int64_t* n_items, int64_t* useful_pairs,
+                           int64_t* issued_pairs, int32_t* bq, int32_t* bk) {
+  try {
+    g_err.clear();
+    if (!cu_seqlens_q || !cu_seqlens_k || !n_items) return fail(VL_EINVAL, "null argument");
+    if (n_docs < 0) return fail(VL_EINVAL, "n_docs must be >= 0");
+    if (pass != 0 && pass != 1) return fail(VL_EINVAL, "pass must be 0 or 1");
+    if (head_dim != 64 && head_dim != 128) return fail(VL_EUNSUPPORTED, "head_dim must be 64 or 128");
+    std::string err;
+    if (!vl::validate_cu(cu_seqlens_q, n_docs, cu_seqlens_q[n_docs], err))
+      return fail(VL_ESEQLENS, "cu_seqlens_q: " + err);
+    if (!vl::validate_cu(cu_seqlens_k, n_docs, cu_seqlens_k[n_docs], err))
+      return fail(VL_ESEQLENS, "cu_seqlens_k: " + err);
+    const int tq = pass == 0 ? vl::kFwdBQ : vl::kBwdBQ;
+    const int tk = pass == 0 ? vl::kFwdBK : vl::kBwdBK;
+    const auto docs = vl::doc_table(cu_seqlens_q, cu_seqlens_k, n_docs);
+    const auto list = pass == 0 ? vl::fwd_items(docs, causal != 0, tq, tk)
+                                : vl::bwd_items(docs, causal != 0, tq, tk);
+    *n_items = int64_t(list.size());
+    if (useful_pairs) *useful_pairs = vl::visible_pairs(docs, causal != 0);
+    if (issued_pairs) *issued_pairs = vl::issued_pairs(list, tq, tk);
+    if (bq) *bq = tq;
+    if (bk) *bk = tk;
+    if (items) {
+      if (cap < int64_t(list.size())) return fail(VL_EWORKSPACE, "items capacity too small");
+      for (size_t i = 0; i < list.size(); ++i) {
+        items[4 * i + 0] = list[i].doc;
+        items[4 * i + 1] = list[i].tile;
+        items[4 * i + 2] = list[i].first;
+        items[4 * i + 3] = list[i].count;
+      }
+    }
+    return VL_OK;
+  } catch (const std::exception& ex) {
+    return fail(VL_EINVAL, std::string("internal error: ") + ex.what());
+  }
+}
+
+}  // extern "C"

@@ -1,0 +1,604 @@
+// Backward attention over packed variable-length documents on gfx950.
+//
+// The exact gradient of the forward (the pages do not write it out; P is
+// recomputed from the saved LSE, the attention recompute the NSP page
+// discusses in Sections 2.3 and 4.2.2):
+//   D_i = dO_i . O_i,  P_ij = exp(S_ij - LSE_i),  dP_ij = dO_i . V_j,
+//   dS_ij = P_ij (dP_ij - D_i),
+//   dV_j = sum_i P_ij dO_i,  dK_j = scale sum_i dS_ij Q_i,  dQ_i = scale sum_j dS_ij K_j.
+//
+// Three kernels, no atomics on dQ:
+//   1. bwd_pre: D = rowsum(dO * O) in fp32, [Hq, T].
+//   2. dkdv: one workgroup per (128-key tile of a document, kv head[, slice of
+//      its q heads]); each wave owns 32 keys and keeps their K, V operands and
+//      fp32 dK, dV accumulators in registers while 32-row query tiles of every
+//      q head of the group stream through LDS (row-major and transposed).
+//      Scores are computed as S = Q K^T so a lane owns one key; the query rows
+//      of the A operand are permuted so P and dS come out of the MFMA already
+//      in the A-operand layout of dV += P^T dO and dK += dS^T Q.
+//   3. dq: the forward's mapping (a lane owns one query): S^T = K Q^T and
+//      dP^T = V dO^T per 64-key tile, then dQ^T += K^T dS^T.
+// The extra two contractions of (3) replace a zeroed fp32 dQ accumulator, its
+// atomics and a conversion pass, and keep dQ deterministic.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+
+#include "common.h"
+#include "launch.h"
+
+namespace vl {
+
+namespace {
+
+constexpr int kThreads = 256;
+
+// ---------------------------------------------------------------- D = rowsum(dO O)
+template <int D>
+__global__ void __launch_bounds__(kThreads)
+bwd_pre_kernel(const uint16_t* __restrict__ o, const uint16_t* __restrict__ dout,
+               float* __restrict__ delta, int64_t total_q, int hq) {
+  constexpr int LPR = D / 8;                 // lanes per (row, head)
+  constexpr int RPB = kThreads / LPR;        // rows per block
+  const int sub = threadIdx.x / LPR;
+  const int c8 = threadIdx.x % LPR;
+  const int64_t n_pairs = total_q * hq;
+  for (int64_t pr = int64_t(blockIdx.x) * RPB + sub; pr < n_pairs;
+       pr += int64_t(gridDim.x) * RPB) {
+    const u32x4 a = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(o + pr * D + c8 * 8));
+    const u32x4 b = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(dout + pr * D + c8 * 8));
+    float acc = 0.f;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      acc = fmaf(bf16_lo(a[j]), bf16_lo(b[j]), acc);
+      acc = fmaf(bf16_hi(a[j]), bf16_hi(b[j]), acc);
+    }
+#pragma unroll
+    for (int m = LPR / 2; m >= 1; m >>= 1) acc += __shfl_xor(acc, m, 64);
+    if (c8 == 0) {
+      const int64_t t = pr / hq;
+      const int h = int(pr - t * hq);
+      delta[int64_t(h) * total_q + t] = acc;
+    }
+  }
+}
+
+__global__ void __launch_bounds__(kThreads)
+fill_zero_kernel(f32x4* __restrict__ p, int64_t n4) {
+  for (int64_t i = int64_t(blockIdx.x) * kThreads + threadIdx.x; i < n4;
+       i += int64_t(gridDim.x) * kThreads)
+    p[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+}
+
+// fp32 [T, H, D] accumulator -> bf16
+__global__ void __launch_bounds__(kThreads)
+f32_to_bf16_kernel(const f32x4* __restrict__ src, u32x2* __restrict__ dst, int64_t n4) {
+  for (int64_t i = int64_t(blockIdx.x) * kThreads + threadIdx.x; i < n4;
+       i += int64_t(gridDim.x) * kThreads) {
+    const f32x4 x = src[i];
+    dst[i] = u32x2{pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3])};
+  }
+}
+
+// Loads a 4-row x 8-column bf16 block (rows past `n_valid` are zero).
+__device__ __forceinline__ void load_block4x8(u32x4 (&r)[4], const uint16_t* __restrict__ base,
+                                              int64_t tok_stride, int row0, int n_valid) {
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    if (row0 + j < n_valid)
+      r[j] = *reinterpret_cast<const u32x4*>(base + int64_t(row0 + j) * tok_stride);
+    else
+      r[j] = u32x4{0, 0, 0, 0};
+  }
+}
+
+// Writes the block row-major (stride rs) and transposed (stride ts) into LDS.
+__device__ __forceinline__ void store_block4x8(const u32x4 (&r)[4], uint16_t* nat, int rs,
+                                               uint16_t* tr, int ts, int row0, int col0) {
+  if (nat) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) *reinterpret_cast<u32x4*>(nat + (row0 + j) * rs + col0) = r[j];
+  }
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    u32x2 even, odd;
+    even[0] = (r[0][u] & 0xffffu) | (r[1][u] << 16);
+    even[1] = (r[2][u] & 0xffffu) | (r[3][u] << 16);
+    odd[0] = (r[0][u] >> 16) | (r[1][u] & 0xffff0000u);
+    odd[1] = (r[2][u] >> 16) | (r[3][u] & 0xffff0000u);
+    const int c = col0 + 2 * u;
+    *reinterpret_cast<u32x2*>(tr + c * ts + row0) = even;
+    *reinterpret_cast<u32x2*>(tr + (c + 1) * ts + row0) = odd;
+  }
+}
+
+// ---------------------------------------------------------------- dK, dV
+constexpr int KB_Q = kBwdBQ;   // 32 query rows per step
+constexpr int KB_K = kBwdBK;   // 128 keys per workgroup
+
+template <int D>
+struct KvSmem {
+  static constexpr int NS = D + 8;       // row-major tile stride
+  static constexpr int TS = KB_Q + 8;    // transposed tile stride
+  uint16_t q[KB_Q * NS];
+  uint16_t qt[D * TS];
+  uint16_t dout[KB_Q * NS];
+  uint16_t dot[D * TS];
+  float lse2[KB_Q];
+  float delta[KB_Q];
+};
+
+template <int D>
+__global__ void __launch_bounds__(kThreads, 1)
+attn_bwd_dkdv_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
+                     const uint16_t* __restrict__ v, const uint16_t* __restrict__ dout,
+                     const float* __restrict__ lse, const float* __restrict__ delta,
+                     const DevItem* __restrict__ items, int n_items, int hq, int hkv,
+                     int head_split, float scale, int causal, int64_t total_q,
+                     uint16_t* __restrict__ dk, uint16_t* __restrict__ dv,
+                     float* __restrict__ dkv_acc, int64_t total_k) {
+  constexpr int NKS = D / 16;
+  constexpr int NCB = D / 32;
+  constexpr int CPR = D / 8;                        // 8-column groups per row
+  constexpr int NBLK = (KB_Q / 4) * CPR;            // 4x8 blocks per tile
+  __shared__ KvSmem<D> sm;
+
+  const int b = blockIdx.x;
+  const int xcd = b & 7;
+  const int r = b >> 3;
+  const int per_item = hkv * head_split;
+  const int item_idx = (r / per_item) * 8 + xcd;
+  const int g = (r % per_item) / head_split;
+  const int split = r % head_split;
+  if (item_idx >= n_items) return;
+  const DevItem it = items[item_idx];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int w = tid >> 6;
+  const int half = lane >> 5;
+  const int l32 = lane & 31;
+
+  const int lq = it.lq, lk = it.lk;
+  const int off = lk - lq;
+  const int j0 = it.tile * KB_K;               // first key of the tile (doc-relative)
+  const int key = j0 + w * 32 + l32;           // this lane's key
+  const int64_t q_tok = int64_t(hq) * D;
+  const int64_t kv_tok = int64_t(hkv) * D;
+  const float c = scale * kLog2e;
+  const int grp = hq / hkv;
+  const int hpg = grp / head_split;            // q heads handled here
+  const int h_begin = g * grp + split * hpg;
+
+  // K and V operands (B of S = Q K^T and of dP = dO V^T): key l32, dims 16s + 8 half ..
+  bf16x8 kf[NKS], vf[NKS];
+  {
+    const int64_t row = int64_t(it.k_start) + key;
+    const uint16_t* kp = k + row * kv_tok + int64_t(g) * D + 8 * half;
+    const uint16_t* vp = v + row * kv_tok + int64_t(g) * D + 8 * half;
+#pragma unroll
+    for (int s = 0; s < NKS; ++s) {
+      u32x4 a = u32x4{0, 0, 0, 0}, bb = u32x4{0, 0, 0, 0};
+      if (key < lk) {
+        a = *reinterpret_cast<const u32x4*>(kp + 16 * s);
+        bb = *reinterpret_cast<const u32x4*>(vp + 16 * s);
+      }
+      kf[s] = as_bf16x8(a);
+      vf[s] = as_bf16x8(bb);
+    }
+  }
+
+  f32x16 dk_acc[NCB], dv_acc[NCB];
+#pragma unroll
+  for (int cb = 0; cb < NCB; ++cb)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      dk_acc[cb][i] = 0.f;
+      dv_acc[cb][i] = 0.f;
+    }
+
+  // this wave's keys [wk_first, wk_last]; queries that may see them start at wk_first - off
+  const int wk_first = j0 + w * 32;
+  const int wk_last = min(j0 + w * 32 + 31, lk - 1);
+  const int n_steps = hpg * it.count;
+
+  // staging: threads [0, NBLK) stage Q, [128, 128 + NBLK) stage dO
+  const bool stage_q = tid < NBLK;
+  const bool stage_do = tid >= 128 && tid < 128 + NBLK;
+  const int sb = stage_q ? tid : tid - 128;
+  const int s_row = (sb / CPR) * 4, s_col = (sb % CPR) * 8;
+
+  u32x4 pre[4];
+  float pre_lse = 0.f;
+  auto fetch = [&](int step) {
+    const int h = h_begin + step / it.count;
+    const int i0 = (it.first + step % it.count) * KB_Q;
+    const int64_t rowbase = int64_t(it.q_start) + i0;
+    if (stage_q || stage_do) {
+      const uint16_t* src = (stage_q ? q : dout) + rowbase * q_tok + int64_t(h) * D + s_col;
+      load_block4x8(pre, src + int64_t(s_row) * q_tok, q_tok, 0, lq - i0 - s_row);
+    }
+    if (tid < KB_Q) {
+      const int i = i0 + tid;
+      pre_lse = (i < lq) ? lse[int64_t(h) * total_q + it.q_start + i] : INFINITY;
+    } else if (tid >= 64 && tid < 64 + KB_Q) {
+      const int i = i0 + tid - 64;
+      pre_lse = (i < lq) ? delta[int64_t(h) * total_q + it.q_start + i] : 0.f;
+    }
+  };
+
+  if (n_steps > 0) fetch(0);
+  for (int step = 0; step < n_steps; ++step) {
+    const int i0 = (it.first + step % it.count) * KB_Q;
+    __syncthreads();
+    if (stage_q) store_block4x8(pre, sm.q, KvSmem<D>::NS, sm.qt, KvSmem<D>::TS, s_row, s_col);
+    if (stage_do) store_block4x8(pre, sm.dout, KvSmem<D>::NS, sm.dot, KvSmem<D>::TS, s_row, s_col);
+    if (tid < KB_Q) sm.lse2[tid] = (pre_lse == -INFINITY) ? INFINITY : pre_lse * kLog2e;
+    else if (tid >= 64 && tid < 64 + KB_Q) sm.delta[tid - 64] = pre_lse;
+    __syncthreads();
+    if (step + 1 < n_steps) fetch(step + 1);
+
+    // wave-uniform: does any query of this tile see any key of this wave?
+    const int iq_last = min(i0 + KB_Q - 1, lq - 1);
+    const bool live = (wk_first < lk) && (!causal || wk_first <= iq_last + off);
+    if (!live) continue;
+    const bool need_mask = (i0 + KB_Q > lq) || (wk_first + 31 >= lk) ||
+                           (causal && wk_last > i0 + off);
+
+    // S = Q K^T and dP = dO V^T (rows: queries 16s + 8 half + t; cols: this wave's keys)
+    f32x16 sacc, pacc;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      sacc[i] = 0.f;
+      pacc[i] = 0.f;
+    }
+    {
+      const int prow = swap_bits23(l32);
+      const uint16_t* qp = &sm.q[prow * KvSmem<D>::NS + 8 * half];
+      const uint16_t* dp = &sm.dout[prow * KvSmem<D>::NS + 8 * half];
+#pragma unroll
+      for (int s = 0; s < NKS; ++s) {
+        sacc = mfma32(as_bf16x8(*reinterpret_cast<const u32x4*>(qp + 16 * s)), kf[s], sacc);
+        pacc = mfma32(as_bf16x8(*reinterpret_cast<const u32x4*>(dp + 16 * s)), vf[s], pacc);
+      }
+    }
+
+    // P and dS; the 16 queries of this lane are 16s + 8 half + t
+    float lse_r[16], dl_r[16];
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      const f32x4 l0 = *reinterpret_cast<const f32x4*>(&sm.lse2[16 * s + 8 * half]);
+      const f32x4 l1 = *reinterpret_cast<const f32x4*>(&sm.lse2[16 * s + 8 * half + 4]);
+      const f32x4 d0 = *reinterpret_cast<const f32x4*>(&sm.delta[16 * s + 8 * half]);
+      const f32x4 d1 = *reinterpret_cast<const f32x4*>(&sm.delta[16 * s + 8 * half + 4]);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        lse_r[8 * s + j] = l0[j];
+        lse_r[8 * s + 4 + j] = l1[j];
+        dl_r[8 * s + j] = d0[j];
+        dl_r[8 * s + 4 + j] = d1[j];
+      }
+    }
+    float p[16], ds[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) p[i] = exp2f(fmaf(sacc[i], c, -lse_r[i]));
+    if (need_mask) {
+      // element i holds query qb + e, e = 16 (i / 8) + i % 8; it is visible iff
+      // e < lq - qb (a real row), key < lk, and (causal) e >= key - off - qb
+      const int qb = i0 + 8 * half;
+      const int e_end = lq - qb;
+      const int e_min = causal ? key - off - qb : INT32_MIN;
+      const int e_cap = (key < lk) ? e_end : INT32_MIN;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int e = 16 * (i >> 3) + (i & 7);
+        p[i] = (e < e_cap && e >= e_min) ? p[i] : 0.f;
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < 16; ++i) ds[i] = p[i] * (pacc[i] - dl_r[i]) * scale;
+    bf16x8 pf[2], dsf[2];
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      u32x4 up, ud;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        up[j] = pack_bf16x2(p[8 * s + 2 * j], p[8 * s + 2 * j + 1]);
+        ud[j] = pack_bf16x2(ds[8 * s + 2 * j], ds[8 * s + 2 * j + 1]);
+      }
+      pf[s] = as_bf16x8(up);
+      dsf[s] = as_bf16x8(ud);
+    }
+
+    // dV += P^T dO, dK += dS^T Q   (B operands from the transposed tiles)
+#pragma unroll
+    for (int cb = 0; cb < NCB; ++cb) {
+      const uint16_t* dtp = &sm.dot[(cb * 32 + l32) * KvSmem<D>::TS + 8 * half];
+      const uint16_t* qtp = &sm.qt[(cb * 32 + l32) * KvSmem<D>::TS + 8 * half];
+#pragma unroll
+      for (int s = 0; s < 2; ++s) {
+        dv_acc[cb] = mfma32(pf[s], as_bf16x8(*reinterpret_cast<const u32x4*>(dtp + 16 * s)), dv_acc[cb]);
+        dk_acc[cb] = mfma32(dsf[s], as_bf16x8(*reinterpret_cast<const u32x4*>(qtp + 16 * s)), dk_acc[cb]);
+      }
+    }
+  }
+
+  // epilogue: lane holds column c = 32 cb + l32 of keys 32 w + 8 (v/4) + 4 half + v%4
+#pragma unroll
+  for (int cb = 0; cb < NCB; ++cb) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int kk = j0 + w * 32 + 8 * (i >> 2) + 4 * half + (i & 3);
+      if (kk < lk) {
+        const int64_t idx = (int64_t(it.k_start) + kk) * kv_tok + int64_t(g) * D + cb * 32 + l32;
+        if (head_split == 1) {
+          dk[idx] = __builtin_bit_cast(uint16_t, (__bf16)dk_acc[cb][i]);
+          dv[idx] = __builtin_bit_cast(uint16_t, (__bf16)dv_acc[cb][i]);
+        } else {
+          atomicAdd(dkv_acc + idx, dk_acc[cb][i]);
+          atomicAdd(dkv_acc + total_k * kv_tok + idx, dv_acc[cb][i]);
+        }
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------- dQ
+constexpr int QB_Q = kFwdBQ;  // 128 queries per workgroup (4 waves x 32)
+constexpr int QB_K = kFwdBK;  // 64 keys per step
+
+template <int D>
+struct QSmem {
+  static constexpr int NS = D + 8;
+  static constexpr int TS = QB_K + 8;
+  uint16_t k[QB_K * NS];
+  uint16_t v[QB_K * NS];
+  uint16_t kt[D * TS];
+};
+
+template <int D>
+__global__ void __launch_bounds__(kThreads, 2)
+attn_bwd_dq_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
+                   const uint16_t* __restrict__ v, const uint16_t* __restrict__ dout,
+                   const float* __restrict__ lse, const float* __restrict__ delta,
+                   const DevItem* __restrict__ items, int n_items, int hq, int hkv, float scale,
+                   int causal, int64_t total_q, uint16_t* __restrict__ dq) {
+  constexpr int NKS = D / 16;
+  constexpr int NCB = D / 32;
+  constexpr int CPR = D / 8;
+  constexpr int NBLK = (QB_K / 4) * CPR;   // 4x8 blocks per K (or V) tile
+  __shared__ QSmem<D> sm;
+
+  const int b = blockIdx.x;
+  const int xcd = b & 7;
+  const int r = b >> 3;
+  const int item_idx = (r / hq) * 8 + xcd;
+  const int h = r % hq;
+  if (item_idx >= n_items) return;
+  const DevItem it = items[item_idx];
+  const int g = h / (hq / hkv);
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int w = tid >> 6;
+  const int half = lane >> 5;
+  const int l32 = lane & 31;
+
+  const int lq = it.lq, lk = it.lk;
+  const int off = lk - lq;
+  const int q0 = it.tile * QB_Q;
+  const int qrow = q0 + w * 32 + l32;
+  const int64_t q_tok = int64_t(hq) * D;
+  const int64_t kv_tok = int64_t(hkv) * D;
+  const float c = scale * kLog2e;
+
+  bf16x8 qf[NKS], df[NKS];
+  {
+    const int64_t row = int64_t(it.q_start) + qrow;
+    const uint16_t* qp = q + row * q_tok + int64_t(h) * D + 8 * half;
+    const uint16_t* dp = dout + row * q_tok + int64_t(h) * D + 8 * half;
+#pragma unroll
+    for (int s = 0; s < NKS; ++s) {
+      u32x4 a = u32x4{0, 0, 0, 0}, bb = u32x4{0, 0, 0, 0};
+      if (qrow < lq) {
+        a = *reinterpret_cast<const u32x4*>(qp + 16 * s);
+        bb = *reinterpret_cast<const u32x4*>(dp + 16 * s);
+      }
+      qf[s] = as_bf16x8(a);
+      df[s] = as_bf16x8(bb);
+    }
+  }
+  float lse2 = INFINITY, dl = 0.f;
+  if (qrow < lq) {
+    const float l = lse[int64_t(h) * total_q + it.q_start + qrow];
+    lse2 = (l == -INFINITY) ? INFINITY : l * kLog2e;
+    dl = delta[int64_t(h) * total_q + it.q_start + qrow];
+  }
+
+  f32x16 acc[NCB];
+#pragma unroll
+  for (int cb = 0; cb < NCB; ++cb)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) acc[cb][i] = 0.f;
+
+  const uint16_t* kbase = k + int64_t(it.k_start) * kv_tok + int64_t(g) * D;
+  const uint16_t* vbase = v + int64_t(it.k_start) * kv_tok + int64_t(g) * D;
+  const int wq_first = q0 + w * 32;
+  const int wq_last = min(q0 + w * 32 + 31, lq - 1);
+
+  const bool stage = tid < NBLK;
+  const int s_row = (tid / CPR) * 4, s_col = (tid % CPR) * 8;
+  u32x4 pk[4], pv[4];
+  auto fetch = [&](int kv0) {
+    if (stage) {
+      load_block4x8(pk, kbase + int64_t(kv0 + s_row) * kv_tok + s_col, kv_tok, 0, lk - kv0 - s_row);
+      load_block4x8(pv, vbase + int64_t(kv0 + s_row) * kv_tok + s_col, kv_tok, 0, lk - kv0 - s_row);
+    }
+  };
+
+  const int n_kv = it.count;
+  if (n_kv > 0) fetch(0);
+  for (int kt = 0; kt < n_kv; ++kt) {
+    const int kv0 = kt * QB_K;
+    __syncthreads();
+    if (stage) {
+      store_block4x8(pk, sm.k, QSmem<D>::NS, sm.kt, QSmem<D>::TS, s_row, s_col);
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        *reinterpret_cast<u32x4*>(&sm.v[(s_row + j) * QSmem<D>::NS + s_col]) = pv[j];
+    }
+    __syncthreads();
+    if (kt + 1 < n_kv) fetch(kv0 + QB_K);
+
+    const bool live = (wq_first < lq) && (!causal || kv0 <= wq_last + off);
+    if (!live) continue;
+    const bool need_mask = (kv0 + QB_K > lk) || (causal && kv0 + QB_K - 1 > wq_first + off);
+
+    f32x16 s[2], dp[2];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        s[kb][i] = 0.f;
+        dp[kb][i] = 0.f;
+      }
+      const int prow = kb * 32 + swap_bits23(l32);
+      const uint16_t* kp = &sm.k[prow * QSmem<D>::NS + 8 * half];
+      const uint16_t* vp = &sm.v[prow * QSmem<D>::NS + 8 * half];
+#pragma unroll
+      for (int st = 0; st < NKS; ++st) {
+        s[kb] = mfma32(as_bf16x8(*reinterpret_cast<const u32x4*>(kp + 16 * st)), qf[st], s[kb]);
+        dp[kb] = mfma32(as_bf16x8(*reinterpret_cast<const u32x4*>(vp + 16 * st)), df[st], dp[kb]);
+      }
+    }
+
+    const int lim = causal ? min(lk - 1, qrow + off) : lk - 1;
+    bf16x8 dsf[2][2];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int hs = 0; hs < 2; ++hs) {
+        u32x4 u;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          float dsv[2];
+#pragma unroll
+          for (int e = 0; e < 2; ++e) {
+            const int i = 8 * hs + 2 * j + e;
+            float pv_ = exp2f(fmaf(s[kb][i], c, -lse2));
+            if (need_mask) {
+              const int kk = kv0 + kb * 32 + 16 * hs + 8 * half + 2 * j + e;
+              if (kk > lim) pv_ = 0.f;
+            }
+            dsv[e] = pv_ * (dp[kb][i] - dl) * scale;
+          }
+          u[j] = pack_bf16x2(dsv[0], dsv[1]);
+        }
+        dsf[kb][hs] = as_bf16x8(u);
+      }
+
+    // dQ^T += K^T dS^T
+#pragma unroll
+    for (int cb = 0; cb < NCB; ++cb) {
+      const uint16_t* tp = &sm.kt[(cb * 32 + l32) * QSmem<D>::TS + 8 * half];
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int hs = 0; hs < 2; ++hs)
+          acc[cb] = mfma32(as_bf16x8(*reinterpret_cast<const u32x4*>(tp + kb * 32 + hs * 16)),
+                           dsf[kb][hs], acc[cb]);
+    }
+  }
+
+  if (qrow < lq) {
+    const int64_t orow = (int64_t(it.q_start) + qrow) * q_tok + int64_t(h) * D;
+#pragma unroll
+    for (int cb = 0; cb < NCB; ++cb)
+#pragma unroll
+      for (int gq = 0; gq < 4; ++gq) {
+        const int cc = cb * 32 + 8 * gq + 4 * half;
+        u32x2 o2;
+        o2[0] = pack_bf16x2(acc[cb][4 * gq], acc[cb][4 * gq + 1]);
+        o2[1] = pack_bf16x2(acc[cb][4 * gq + 2], acc[cb][4 * gq + 3]);
+        *reinterpret_cast<u32x2*>(dq + orow + cc) = o2;
+      }
+  }
+}
+
+int device_cus() {
+  int dev = 0, n = 256;
+  (void)hipGetDevice(&dev);
+  (void)hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev);
+  return n;
+}
+
+template <int D>
+hipError_t run_bwd(const AttnShape& s, const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                   const uint16_t* o, const uint16_t* dout, const float* lse,
+                   const DevItem* fwd_list, int32_t n_fwd, const DevItem* bwd_list, int32_t n_bwd,
+                   int32_t head_split, uint16_t* dq, uint16_t* dk, uint16_t* dv, float* delta,
+                   float* dkv_acc, hipStream_t stream) {
+  const int n_cu = device_cus();
+  {
+    constexpr int RPB = kThreads / (D / 8);
+    const int64_t want = (s.total_q * s.hq + RPB - 1) / RPB;
+    const int blocks = int(std::max<int64_t>(1, std::min<int64_t>(want, int64_t(n_cu) * 16)));
+    if (s.total_q > 0)
+      hipLaunchKernelGGL((bwd_pre_kernel<D>), dim3(blocks), dim3(kThreads), 0, stream, o, dout,
+                         delta, s.total_q, s.hq);
+  }
+  const int64_t kv_elems = s.total_k * s.hkv * D;
+  if (head_split > 1 && kv_elems > 0) {
+    const int64_t n4 = 2 * kv_elems / 4;
+    const int blocks = int(std::min<int64_t>((n4 + kThreads - 1) / kThreads, int64_t(n_cu) * 16));
+    hipLaunchKernelGGL(fill_zero_kernel, dim3(blocks), dim3(kThreads), 0, stream,
+                       reinterpret_cast<f32x4*>(dkv_acc), n4);
+  }
+  if (n_bwd > 0) {
+    const int groups = (n_bwd + 7) / 8;
+    const dim3 grid(unsigned(groups) * 8u * unsigned(s.hkv * head_split));
+    hipLaunchKernelGGL((attn_bwd_dkdv_kernel<D>), grid, dim3(kThreads), 0, stream, q, k, v, dout,
+                       lse, delta, bwd_list, n_bwd, s.hq, s.hkv, head_split, s.scale, s.causal,
+                       s.total_q, dk, dv, dkv_acc, s.total_k);
+  }
+  if (head_split > 1 && kv_elems > 0) {
+    const int64_t n4 = kv_elems / 4;
+    const int blocks = int(std::min<int64_t>((n4 + kThreads - 1) / kThreads, int64_t(n_cu) * 16));
+    hipLaunchKernelGGL(f32_to_bf16_kernel, dim3(blocks), dim3(kThreads), 0, stream,
+                       reinterpret_cast<const f32x4*>(dkv_acc), reinterpret_cast<u32x2*>(dk), n4);
+    hipLaunchKernelGGL(f32_to_bf16_kernel, dim3(blocks), dim3(kThreads), 0, stream,
+                       reinterpret_cast<const f32x4*>(dkv_acc + kv_elems),
+                       reinterpret_cast<u32x2*>(dv), n4);
+  }
+  if (n_fwd > 0) {
+    const int groups = (n_fwd + 7) / 8;
+    const dim3 grid(unsigned(groups) * 8u * unsigned(s.hq));
+    hipLaunchKernelGGL((attn_bwd_dq_kernel<D>), grid, dim3(kThreads), 0, stream, q, k, v, dout, lse,
+                       delta, fwd_list, n_fwd, s.hq, s.hkv, s.scale, s.causal, s.total_q, dq);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_attn_bwd(const AttnShape& s, const void* q, const void* k, const void* v,
+                           const void* o, const void* dout, const float* lse,
+                           const DevItem* fwd_list, int32_t n_fwd, const DevItem* bwd_list,
+                           int32_t n_bwd, int32_t head_split, void* dq, void* dk, void* dv,
+                           float* delta, float* dkv_acc, hipStream_t stream) {
+  auto* Q = reinterpret_cast<const uint16_t*>(q);
+  auto* K = reinterpret_cast<const uint16_t*>(k);
+  auto* V = reinterpret_cast<const uint16_t*>(v);
+  auto* O = reinterpret_cast<const uint16_t*>(o);
+  auto* DO = reinterpret_cast<const uint16_t*>(dout);
+  auto* DQ = reinterpret_cast<uint16_t*>(dq);
+  auto* DK = reinterpret_cast<uint16_t*>(dk);
+  auto* DV = reinterpret_cast<uint16_t*>(dv);
+  if (s.d == 128)
+    return run_bwd<128>(s, Q, K, V, O, DO, lse, fwd_list, n_fwd, bwd_list, n_bwd, head_split, DQ,
+                        DK, DV, delta, dkv_acc, stream);
+  return run_bwd<64>(s, Q, K, V, O, DO, lse, fwd_list, n_fwd, bwd_list, n_bwd, head_split, DQ, DK,
+                     DV, delta, dkv_acc, stream);
+}
+
+}  // namespace vl

@@ -1,0 +1,315 @@
+// Forward attention over packed variable-length documents on gfx950.
+//
+// Computes O = softmax(scale Q K^T) V and LSE per query, each query seeing
+// only the keys of its own document (HSAP page, Section 2.1, cu_len; NSP page,
+// Section 2.2) and, if causal, only keys at or before its position.  The
+// softmax is evaluated online over key tiles, so the score matrix is never
+// stored (BASP page, Section II-A on tiling and online softmax; HSAP page,
+// Section 2.2.1).
+//
+// Mapping (one workgroup = one work item x one q head; 4 waves):
+//   * a work item is a 128-row query tile of one document plus the number of
+//     64-row key tiles it needs (tiles past the causal diagonal are never
+//     listed);  wave w owns query rows 32w .. 32w+31 of the tile;
+//   * scores are computed transposed, S^T = K Q^T, on 32x32x16 bf16 MFMAs, so
+//     each lane owns one query (its column) and row statistics need only one
+//     exchange with the other half-wave;
+//   * the key rows of the MFMA A operand are permuted (bits 2 and 3 of the row
+//     swapped) so that the fp32 S^T values a lane holds are, after rounding
+//     P to bf16, exactly the B operand of O^T += V^T P^T with no shuffles;
+//   * K tiles are staged in LDS row-major, V tiles transposed (d-major), both
+//     padded by 16 B per row; the next tile's global loads are issued before
+//     the current tile's MFMAs;
+//   * work items are ordered longest first and the workgroup id is remapped
+//     so all q heads of one item run on the same XCD (shared K/V in its L2).
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+
+#include "common.h"
+#include "launch.h"
+
+namespace vl {
+
+namespace {
+
+constexpr int BQ = kFwdBQ;  // 128
+constexpr int BK = kFwdBK;  // 64
+constexpr int kThreads = 256;
+
+template <int D>
+struct FwdSmem {
+  static constexpr int KS = D + 8;   // K tile row stride (elements)
+  static constexpr int VS = BK + 8;  // V^T tile row stride (elements)
+  uint16_t k[BK * KS];
+  uint16_t vt[D * VS];
+};
+
+// Global loads of one K/V tile into registers (zero rows past the document).
+template <int D>
+struct TileRegs {
+  static constexpr int KCH = BK * D / 8 / kThreads;   // 16-byte K chunks per thread
+  static constexpr int VBLK = (BK / 4) * (D / 8);     // 4-key x 8-dim V blocks
+  u32x4 k[KCH];
+  u32x4 v[4];
+};
+
+template <int D>
+__device__ __forceinline__ void load_tile(TileRegs<D>& r, const uint16_t* __restrict__ kbase,
+                                          const uint16_t* __restrict__ vbase, int64_t tok_stride,
+                                          int kv0, int lk, int tid) {
+  constexpr int CPR = D / 8;  // chunks per row
+#pragma unroll
+  for (int i = 0; i < TileRegs<D>::KCH; ++i) {
+    const int id = tid + i * kThreads;
+    const int row = id / CPR, c8 = id % CPR;
+    const int key = kv0 + row;
+    if (key < lk)
+      r.k[i] = *reinterpret_cast<const u32x4*>(kbase + int64_t(key) * tok_stride + c8 * 8);
+    else
+      r.k[i] = u32x4{0, 0, 0, 0};
+  }
+  if (tid < TileRegs<D>::VBLK) {
+    const int kg = tid / CPR, c8 = tid % CPR;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int key = kv0 + kg * 4 + j;
+      if (key < lk)
+        r.v[j] = *reinterpret_cast<const u32x4*>(vbase + int64_t(key) * tok_stride + c8 * 8);
+      else
+        r.v[j] = u32x4{0, 0, 0, 0};
+    }
+  }
+}
+
+template <int D>
+__device__ __forceinline__ void store_tile(const TileRegs<D>& r, FwdSmem<D>& sm, int tid) {
+  constexpr int CPR = D / 8;
+#pragma unroll
+  for (int i = 0; i < TileRegs<D>::KCH; ++i) {
+    const int id = tid + i * kThreads;
+    const int row = id / CPR, c8 = id % CPR;
+    *reinterpret_cast<u32x4*>(&sm.k[row * FwdSmem<D>::KS + c8 * 8]) = r.k[i];
+  }
+  if (tid < TileRegs<D>::VBLK) {
+    const int kg = tid / CPR, c8 = tid % CPR;
+    // transpose 4 keys x 8 dims into 8 dims x 4 keys
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      u32x2 even, odd;
+      even[0] = (r.v[0][u] & 0xffffu) | (r.v[1][u] << 16);
+      even[1] = (r.v[2][u] & 0xffffu) | (r.v[3][u] << 16);
+      odd[0] = (r.v[0][u] >> 16) | (r.v[1][u] & 0xffff0000u);
+      odd[1] = (r.v[2][u] >> 16) | (r.v[3][u] & 0xffff0000u);
+      const int c = c8 * 8 + 2 * u;
+      *reinterpret_cast<u32x2*>(&sm.vt[c * FwdSmem<D>::VS + kg * 4]) = even;
+      *reinterpret_cast<u32x2*>(&sm.vt[(c + 1) * FwdSmem<D>::VS + kg * 4]) = odd;
+    }
+  }
+}
+
+template <int D, bool F32OUT>
+__global__ void __launch_bounds__(kThreads, 2)
+attn_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
+                const uint16_t* __restrict__ v, const DevItem* __restrict__ items, int n_items,
+                int hq, int hkv, float scale, int causal, void* __restrict__ out,
+                float* __restrict__ lse, int64_t total_q) {
+  constexpr int NKS = D / 16;  // k-steps over the head dim
+  constexpr int NCB = D / 32;  // 32-wide blocks of the head dim
+  __shared__ FwdSmem<D> sm;
+
+  // workgroup -> (item, head): the 8 XCDs take items round-robin, and all
+  // heads of one item stay on one XCD
+  const int b = blockIdx.x;
+  const int xcd = b & 7;
+  const int r = b >> 3;
+  const int item_idx = (r / hq) * 8 + xcd;
+  const int h = r % hq;
+  if (item_idx >= n_items) return;
+  const DevItem it = items[item_idx];
+  const int g = h / (hq / hkv);
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int w = tid >> 6;
+  const int half = lane >> 5;
+  const int l32 = lane & 31;
+
+  const int lq = it.lq, lk = it.lk;
+  const int q0 = it.tile * BQ;
+  const int qrow = q0 + w * 32 + l32;        // doc-relative query row of this lane
+  const int off = lk - lq;                   // causal diagonal offset
+  const int64_t q_tok = int64_t(hq) * D;
+  const int64_t kv_tok = int64_t(hkv) * D;
+  const float c = scale * kLog2e;
+
+  // Q fragment (B operand of S^T = K Q^T): query l32, dims 16s + 8 half .. +8
+  bf16x8 qf[NKS];
+  {
+    const uint16_t* qp = q + (int64_t(it.q_start) + qrow) * q_tok + int64_t(h) * D + 8 * half;
+#pragma unroll
+    for (int s = 0; s < NKS; ++s) {
+      u32x4 u = u32x4{0, 0, 0, 0};
+      if (qrow < lq) u = *reinterpret_cast<const u32x4*>(qp + 16 * s);
+      qf[s] = as_bf16x8(u);
+    }
+  }
+
+  f32x16 acc[NCB];
+#pragma unroll
+  for (int cb = 0; cb < NCB; ++cb)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) acc[cb][i] = 0.f;
+  float m_run = -INFINITY;  // running max of raw scores of this lane's query
+  float l_run = 0.f;        // running sum (this half-wave's keys)
+
+  const uint16_t* kbase = k + int64_t(it.k_start) * kv_tok + int64_t(g) * D;
+  const uint16_t* vbase = v + int64_t(it.k_start) * kv_tok + int64_t(g) * D;
+
+  // first and last query rows of this wave (for skipping / masking)
+  const int wq_first = q0 + w * 32;
+  const int wq_last = min(q0 + w * 32 + 31, lq - 1);
+
+  TileRegs<D> regs;
+  const int n_kv = it.count;
+  if (n_kv > 0) load_tile<D>(regs, kbase, vbase, kv_tok, 0, lk, tid);
+
+  for (int kt = 0; kt < n_kv; ++kt) {
+    const int kv0 = kt * BK;
+    __syncthreads();               // previous tile fully consumed
+    store_tile<D>(regs, sm, tid);
+    __syncthreads();
+    if (kt + 1 < n_kv) load_tile<D>(regs, kbase, vbase, kv_tok, kv0 + BK, lk, tid);
+
+    // wave-uniform: skip tiles no query of this wave can see
+    const bool wave_live = (wq_first < lq) && (!causal || kv0 <= wq_last + off);
+    if (!wave_live) continue;
+    const bool need_mask = (kv0 + BK > lk) || (causal && kv0 + BK - 1 > wq_first + off);
+
+    // S^T for the two 32-key halves of the tile
+    f32x16 s[2];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) s[kb][i] = 0.f;
+      const uint16_t* kp = &sm.k[(kb * 32 + swap_bits23(l32)) * FwdSmem<D>::KS + 8 * half];
+#pragma unroll
+      for (int st = 0; st < NKS; ++st) {
+        const bf16x8 a = as_bf16x8(*reinterpret_cast<const u32x4*>(kp + 16 * st));
+        s[kb] = mfma32(a, qf[st], s[kb]);
+      }
+    }
+
+    if (need_mask) {
+      const int lim = causal ? min(lk - 1, qrow + off) : lk - 1;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int key = kv0 + kb * 32 + 16 * (i >> 3) + 8 * half + (i & 7);
+          if (key > lim) s[kb][i] = -INFINITY;
+        }
+    }
+
+    float mx = -INFINITY;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[kb][i]);
+    mx = fmaxf(mx, xor32(mx));
+    const float m_new = fmaxf(m_run, mx);
+    const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
+    const float alpha = exp2f((m_run - m_use) * c);
+    const float mc = m_use * c;
+    m_run = m_new;
+
+    float psum = 0.f;
+    bf16x8 pf[2][2];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+      for (int hs = 0; hs < 2; ++hs) {
+        u32x4 u;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const float p0 = exp2f(fmaf(s[kb][8 * hs + 2 * j], c, -mc));
+          const float p1 = exp2f(fmaf(s[kb][8 * hs + 2 * j + 1], c, -mc));
+          psum += p0 + p1;
+          u[j] = pack_bf16x2(p0, p1);
+        }
+        pf[kb][hs] = as_bf16x8(u);
+      }
+    }
+    l_run = l_run * alpha + psum;
+#pragma unroll
+    for (int cb = 0; cb < NCB; ++cb)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) acc[cb][i] *= alpha;
+
+    // O^T += V^T P^T
+#pragma unroll
+    for (int cb = 0; cb < NCB; ++cb) {
+      const uint16_t* vp = &sm.vt[(cb * 32 + l32) * FwdSmem<D>::VS + 8 * half];
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int hs = 0; hs < 2; ++hs) {
+          const bf16x8 a = as_bf16x8(*reinterpret_cast<const u32x4*>(vp + kb * 32 + hs * 16));
+          acc[cb] = mfma32(a, pf[kb][hs], acc[cb]);
+        }
+    }
+  }
+
+  // epilogue: O = acc / l, LSE = m scale + ln l
+  const float l_tot = l_run + xor32(l_run);
+  const float inv = (l_tot > 0.f) ? 1.f / l_tot : 0.f;
+  if (qrow < lq) {
+    const int64_t orow = (int64_t(it.q_start) + qrow) * q_tok + int64_t(h) * D;
+#pragma unroll
+    for (int cb = 0; cb < NCB; ++cb)
+#pragma unroll
+      for (int gq = 0; gq < 4; ++gq) {
+        const int cc = cb * 32 + 8 * gq + 4 * half;
+        if constexpr (F32OUT) {
+          f32x4 o4;
+#pragma unroll
+          for (int j = 0; j < 4; ++j) o4[j] = acc[cb][4 * gq + j] * inv;
+          *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(out) + orow + cc) = o4;
+        } else {
+          u32x2 o2;
+          o2[0] = pack_bf16x2(acc[cb][4 * gq] * inv, acc[cb][4 * gq + 1] * inv);
+          o2[1] = pack_bf16x2(acc[cb][4 * gq + 2] * inv, acc[cb][4 * gq + 3] * inv);
+          *reinterpret_cast<u32x2*>(reinterpret_cast<uint16_t*>(out) + orow + cc) = o2;
+        }
+      }
+    if (half == 0) {
+      const float lv = (l_tot > 0.f) ? (m_run * scale + __logf(l_tot)) : -INFINITY;
+      lse[int64_t(h) * total_q + it.q_start + qrow] = lv;
+    }
+  }
+}
+
+}  // namespace
+
+hipError_t launch_attn_fwd(const AttnShape& s, const void* q, const void* k, const void* v,
+                           const DevItem* items, int32_t n_items, int32_t out_dtype, void* out,
+                           float* lse, hipStream_t stream) {
+  if (n_items == 0) return hipSuccess;
+  const int groups = (n_items + 7) / 8;
+  const dim3 grid(unsigned(groups) * 8u * unsigned(s.hq));
+  const auto* qq = reinterpret_cast<const uint16_t*>(q);
+  const auto* kk = reinterpret_cast<const uint16_t*>(k);
+  const auto* vv = reinterpret_cast<const uint16_t*>(v);
+#define VL_FWD(DD, F32)                                                                        \
+  hipLaunchKernelGGL((attn_fwd_kernel<DD, F32>), grid, dim3(kThreads), 0, stream, qq, kk, vv,   \
+                     items, n_items, s.hq, s.hkv, s.scale, s.causal, out, lse, s.total_q)
+  if (s.d == 128) {
+    if (out_dtype == 1) VL_FWD(128, true); else VL_FWD(128, false);
+  } else {
+    if (out_dtype == 1) VL_FWD(64, true); else VL_FWD(64, false);
+  }
+#undef VL_FWD
+  return hipGetLastError();
+}
+
+}  // namespace vl

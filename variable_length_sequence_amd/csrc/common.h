@@ -1,0 +1,66 @@
+// Device-side helpers shared by the attention kernels (gfx950 / CDNA4).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace vl {
+
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
+typedef __attribute__((ext_vector_type(4))) __bf16 bf16x4;
+typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
+typedef __attribute__((ext_vector_type(16))) float f32x16;
+typedef __attribute__((ext_vector_type(4))) float f32x4;
+typedef __attribute__((ext_vector_type(4))) uint32_t u32x4;
+typedef __attribute__((ext_vector_type(2))) uint32_t u32x2;
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+// D(32x32, fp32) += A(32x16, bf16) * B(16x32, bf16) on the matrix cores.
+// Lane l holds A[row l%32][k 8*(l/32) .. +8], B[k 8*(l/32) .. +8][col l%32];
+// C value v of lane l is C[row 8*(v/4) + 4*(l/32) + v%4][col l%32].
+__device__ __forceinline__ f32x16 mfma32(const bf16x8& a, const bf16x8& b, const f32x16& c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ bf16x8 as_bf16x8(const u32x4& u) {
+  return __builtin_bit_cast(bf16x8, u);
+}
+__device__ __forceinline__ u32x4 as_u32x4(const bf16x8& b) {
+  return __builtin_bit_cast(u32x4, b);
+}
+
+// fp32 -> bf16, round to nearest even (v_cvt_pk_bf16_f32 on gfx950).
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  bf16x2 r;
+  r[0] = (__bf16)lo;
+  r[1] = (__bf16)hi;
+  return __builtin_bit_cast(uint32_t, r);
+}
+
+__device__ __forceinline__ float bf16_lo(uint32_t u) { return __uint_as_float(u << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t u) { return __uint_as_float(u & 0xffff0000u); }
+
+// Row index permutation of the 32-row A operand that makes the C rows held by
+// lane half h for k-step s (C values 8s .. 8s+7) the consecutive keys
+// 16s + 8h + 0..7: swap bits 2 and 3.
+__device__ __forceinline__ int swap_bits23(int m) {
+  return (m & ~12) | ((m & 4) << 1) | ((m & 8) >> 1);
+}
+
+// Exchange a value with the lane 32 positions away (the other half-wave).
+__device__ __forceinline__ float xor32(float x) {
+  return __shfl_xor(x, 32, 64);
+}
+
+// Workgroup id remapped so that consecutive logical ids land on the same XCD
+// (workgroups are dispatched round-robin over the 8 XCDs of an MI355X).
+__device__ __forceinline__ uint32_t xcd_remap(uint32_t bid, uint32_t nblocks) {
+  const uint32_t nx = 8;
+  const uint32_t per = nblocks / nx;           // full rounds
+  const uint32_t full = per * nx;
+  if (bid >= full) return bid;                 // ragged tail: identity
+  return (bid % nx) * per + bid / nx;
+}
+
+}  // namespace vl

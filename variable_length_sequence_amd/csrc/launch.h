@@ -1,0 +1,50 @@
+// Internal host launchers of the HIP kernels (not part of the C ABI).
+// Arguments are assumed validated by the caller (api.cpp); each returns the
+// hipError_t of its launch.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "scheduler.h"
+
+namespace vl {
+
+// Ulysses pack/unpack: dir 0 = seq2head (x -> y), dir 1 = head2seq (y -> x).
+hipError_t launch_sp_permute(const void* src, void* dst, int64_t n_tokens, int32_t n_heads,
+                             int32_t head_dim, int32_t sp_degree, int32_t elem_bytes, int dir,
+                             hipStream_t stream);
+
+constexpr int kMaxMergeParts = 64;
+
+hipError_t launch_lse_merge(int32_t n_parts, const void* const* o_parts,
+                            const float* const* lse_parts, int32_t in_dtype, int64_t n_rows,
+                            int32_t n_heads, int32_t head_dim, void* o_out, float* lse_out,
+                            int32_t out_dtype, hipStream_t stream);
+
+// Tile sizes of the attention kernels (rows of a query tile / key tile).
+constexpr int kFwdBQ = 128;   // forward and dQ kernels: 4 waves x 32 queries
+constexpr int kFwdBK = 64;
+constexpr int kBwdBQ = 32;    // dK/dV kernel: query rows per step
+constexpr int kBwdBK = 128;   // dK/dV kernel: 4 waves x 32 keys
+
+struct AttnShape {
+  int64_t total_q, total_k;
+  int32_t hq, hkv, d;
+  float scale;
+  int32_t causal;
+};
+
+hipError_t launch_attn_fwd(const AttnShape& s, const void* q, const void* k, const void* v,
+                           const DevItem* items, int32_t n_items, int32_t out_dtype, void* out,
+                           float* lse, hipStream_t stream);
+
+// Backward: D_i = dO_i . O_i, then dK/dV over the kv-tile list, then dQ over
+// the query-tile list.  dkv_acc is fp32 [2, total_k, hkv, d] scratch used when
+// q heads of one group are split over several workgroups (head_split > 1).
+hipError_t launch_attn_bwd(const AttnShape& s, const void* q, const void* k, const void* v,
+                           const void* o, const void* dout, const float* lse,
+                           const DevItem* fwd_list, int32_t n_fwd, const DevItem* bwd_list,
+                           int32_t n_bwd, int32_t head_split, void* dq, void* dk, void* dv,
+                           float* delta, float* dkv_acc, hipStream_t stream);
+
+}  // namespace vl

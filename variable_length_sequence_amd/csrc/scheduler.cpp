@@ -1,0 +1,125 @@
+// Host-side work-list scheduler; see scheduler.h.
+#include "scheduler.h"
+
+#include <algorithm>
+
+namespace vl {
+
+static inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+static inline int64_t floor_div(int64_t a, int64_t b) {
+  int64_t q = a / b;
+  return (a % b != 0 && ((a < 0) != (b < 0))) ? q - 1 : q;
+}
+
+bool validate_cu(const int32_t* cu, int32_t n_docs, int64_t total, std::string& err) {
+  if (!cu) { err = "cu_seqlens is null"; return false; }
+  if (n_docs < 0) { err = "n_docs is negative"; return false; }
+  if (cu[0] != 0) { err = "cu_seqlens[0] must be 0"; return false; }
+  for (int32_t i = 0; i < n_docs; ++i) {
+    if (cu[i + 1] < cu[i]) {
+      err = "cu_seqlens must be non-decreasing (entry " + std::to_string(i + 1) + ")";
+      return false;
+    }
+  }
+  if (int64_t(cu[n_docs]) != total) {
+    err = "cu_seqlens[n_docs] = " + std::to_string(cu[n_docs]) +
+          " does not equal the total token count " + std::to_string(total);
+    return false;
+  }
+  return true;
+}
+
+std::vector<Doc> doc_table(const int32_t* cu_q, const int32_t* cu_k, int32_t n_docs) {
+  std::vector<Doc> d(static_cast<size_t>(n_docs));
+  for (int32_t i = 0; i < n_docs; ++i)
+    d[size_t(i)] = Doc{cu_q[i], int64_t(cu_q[i + 1]) - cu_q[i], cu_k[i], int64_t(cu_k[i + 1]) - cu_k[i]};
+  return d;
+}
+
+static void lpt_sort(std::vector<Item>& items) {
+  std::stable_sort(items.begin(), items.end(), [](const Item& a, const Item& b) {
+    if (a.count != b.count) return a.count > b.count;
+    if (a.doc != b.doc) return a.doc < b.doc;
+    return a.tile < b.tile;
+  });
+}
+
+std::vector<Item> fwd_items(const std::vector<Doc>& docs, bool causal, int bq, int bk) {
+  std::vector<Item> out;
+  for (size_t b = 0; b < docs.size(); ++b) {
+    const Doc& d = docs[b];
+    const int64_t n_k = ceil_div(d.lk, bk);
+    const int64_t n_t = ceil_div(d.lq, bq);
+    for (int64_t t = 0; t < n_t; ++t) {
+      int64_t n_kv = n_k;
+      if (causal) {
+        // the tile's last row sees keys up to last_row + (Lk - Lq)
+        const int64_t last_row = std::min(d.lq, (t + 1) * bq) - 1;
+        const int64_t last_key = last_row + (d.lk - d.lq);
+        n_kv = std::min(std::max(floor_div(last_key, bk) + 1, int64_t(0)), n_k);
+      }
+      out.push_back(Item{int32_t(b), int32_t(t), 0, int32_t(n_kv)});
+    }
+  }
+  lpt_sort(out);
+  return out;
+}
+
+std::vector<Item> bwd_items(const std::vector<Doc>& docs, bool causal, int bq, int bk) {
+  std::vector<Item> out;
+  for (size_t b = 0; b < docs.size(); ++b) {
+    const Doc& d = docs[b];
+    const int64_t n_q = ceil_div(d.lq, bq);
+    const int64_t n_j = ceil_div(d.lk, bk);
+    for (int64_t j = 0; j < n_j; ++j) {
+      int64_t t0 = 0;
+      if (causal) {
+        // key j*bk is first seen by query row j*bk - (Lk - Lq)
+        const int64_t first_row = std::max(int64_t(0), j * bk - (d.lk - d.lq));
+        t0 = std::min(first_row / bq, n_q);
+      }
+      out.push_back(Item{int32_t(b), int32_t(j), int32_t(t0), int32_t(n_q - t0)});
+    }
+  }
+  lpt_sort(out);
+  return out;
+}
+
+int64_t visible_pairs(const std::vector<Doc>& docs, bool causal) {
+  int64_t tot = 0;
+  for (const Doc& d : docs) {
+    if (!causal) { tot += d.lq * d.lk; continue; }
+    // row i sees min(max(i + off + 1, 0), Lk) keys, off = Lk - Lq
+    const int64_t off = d.lk - d.lq;
+    // rows with i + off + 1 <= 0 see nothing; rows with i + off + 1 >= Lk see Lk
+    const int64_t i_lo = std::max(int64_t(0), -off);           // first row seeing >= 1 key
+    const int64_t i_hi = std::min(d.lq, d.lk - off - 1);        // rows [i_lo, i_hi) see < Lk
+    if (i_hi > i_lo) {
+      // sum_{i=i_lo}^{i_hi-1} (i + off + 1)
+      const int64_t a = i_lo + off + 1, z = i_hi - 1 + off + 1, n = i_hi - i_lo;
+      tot += (a + z) * n / 2;
+    }
+    const int64_t full_from = std::max(i_lo, std::max(i_hi, int64_t(0)));
+    if (d.lq > full_from) tot += (d.lq - full_from) * d.lk;
+  }
+  return tot;
+}
+
+int64_t issued_pairs(const std::vector<Item>& items, int bq, int bk) {
+  int64_t n = 0;
+  for (const Item& it : items) n += it.count;
+  return n * int64_t(bq) * bk;
+}
+
+std::vector<DevItem> device_items(const std::vector<Doc>& docs, const std::vector<Item>& items) {
+  std::vector<DevItem> out(items.size());
+  for (size_t i = 0; i < items.size(); ++i) {
+    const Item& it = items[i];
+    const Doc& d = docs[size_t(it.doc)];
+    out[i] = DevItem{int32_t(d.q_start), int32_t(d.lq), int32_t(d.k_start), int32_t(d.lk),
+                     it.tile, it.first, it.count, it.doc};
+  }
+  return out;
+}
+
+}  // namespace vl

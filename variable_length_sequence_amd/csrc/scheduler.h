@@ -1,0 +1,54 @@
+// Host-side work-list scheduler for packed variable-length attention.
+//
+// Documents sit back to back in the packed token axis, delimited by the
+// cumulative lengths (HSAP page, Section 2.1, cu_len).  Each document is cut
+// into query tiles and key tiles that never cross a document boundary, so no
+// tile can mix two documents.  For causal attention a (query tile, key tile)
+// pair entirely above the diagonal holds no visible pair -- the "N" block of
+// the HSAP page's Figure 3 -- and is never issued.  Items are ordered longest
+// first, the same rule the NSP planner applies to samples (NSP page,
+// Section 4.1.3, Algorithm 1), so the longest tiles start first on the GPU.
+//
+// Pure C++17: no HIP, so it builds and runs on any host.
+#pragma once
+#include <stdint.h>
+
+#include <string>
+#include <vector>
+
+namespace vl {
+
+struct Doc {
+  int64_t q_start, lq, k_start, lk;
+};
+
+// One unit of kernel work, as exported: for the forward pass
+// (doc, q_tile, first kv tile, kv tile count); for the backward pass
+// (doc, kv_tile, first q tile, q tile count).
+struct Item {
+  int32_t doc, tile, first, count;
+};
+
+// What a kernel reads per work item (self-contained, 32 bytes).
+struct DevItem {
+  int32_t q_start, lq, k_start, lk;
+  int32_t tile, first, count, doc;
+};
+
+// Validates one cumulative-length array: n_docs + 1 entries, cu[0] == 0,
+// non-decreasing, cu[n_docs] == total.  Returns false and sets err otherwise.
+bool validate_cu(const int32_t* cu, int32_t n_docs, int64_t total, std::string& err);
+
+std::vector<Doc> doc_table(const int32_t* cu_q, const int32_t* cu_k, int32_t n_docs);
+
+std::vector<Item> fwd_items(const std::vector<Doc>& docs, bool causal, int bq, int bk);
+std::vector<Item> bwd_items(const std::vector<Doc>& docs, bool causal, int bq, int bk);
+
+// Visible (query, key) pairs per head.
+int64_t visible_pairs(const std::vector<Doc>& docs, bool causal);
+// Pairs covered by issued tiles per head (full tile area).
+int64_t issued_pairs(const std::vector<Item>& items, int bq, int bk);
+
+std::vector<DevItem> device_items(const std::vector<Doc>& docs, const std::vector<Item>& items);
+
+}  // namespace vl
