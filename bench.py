@@ -1,0 +1,307 @@
+#!/usr/bin/env python3
+"""Benchmark of packed variable-length causal attention on one MI355X.
+
+One step = the whole hot path over one synthetic packed batch: the cached
+work lists (cu_seqlens validation and scheduling; built once, then looked up),
+varlen_attn_fwd and varlen_attn_bwd (D = rowsum(dO*O), dK/dV, dQ).  The
+headline workload is the 16384-token long-tail batch (lognormal lengths,
+median 512, sigma 1.2, clipped to [64, 8192]; 32 q heads, 4 kv heads,
+head_dim 128).  The metric is useful TFLOP/s: 4 d FLOPs per visible
+(query, key) pair forward and 10 d backward, times the q heads; masked tiles
+and masked elements are not counted.
+
+Prints ONE JSON line.  Besides the headline it carries:
+  roofline      the dominant kernel's algorithmic FLOPs per launch over its
+                average HIP-event duration, against the bf16 dense MFMA peak;
+  kernels       every kernel's launches, average time and roofline fraction;
+  cpu_baseline  the fp64 oracle on the host cores for the same batch;
+  extra         the other workloads: the Ulysses permute on one GPU's
+                [49152, 32, 128] shard, the ring share (8 partial forwards +
+                attn_lse_merge), the 384K Ulysses attention share and the
+                131072-token Pareto batch per length bucket.
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2516.6   # MI355X dense bf16 MFMA: 256 CU x 2.4 GHz x 4096 FLOP/clk
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+
+
+def _args():
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-extra", action="store_true", help="skip the other workloads")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    return ap.parse_args()
+
+
+def useful(vl, cu_q, cu_k, causal, hq, d):
+    pairs = vl.varlen_schedule_export(cu_q, cu_k, causal, 0, d)["useful_pairs"]
+    return pairs, 4 * d * pairs * hq, 10 * d * pairs * hq
+
+
+class Timer:
+    """Wall clock plus HIP events on the current stream, bracketed by synchronize."""
+
+    def __init__(self, torch):
+        self.torch = torch
+
+    def __enter__(self):
+        t = self.torch
+        t.cuda.synchronize()
+        self.e0 = t.cuda.Event(enable_timing=True)
+        self.e1 = t.cuda.Event(enable_timing=True)
+        self.w0 = time.perf_counter()
+        self.e0.record()
+        return self
+
+    def __exit__(self, *exc):
+        self.e1.record()
+        self.torch.cuda.synchronize()
+        self.wall_ms = (time.perf_counter() - self.w0) * 1e3
+        self.event_ms = self.e0.elapsed_time(self.e1)
+
+
+def kernel_table(prof, flops, bytes_):
+    out = {}
+    for name, (n, ms) in prof.items():
+        avg = ms / max(n, 1)
+        rec = {"launches": n, "avg_ms": round(avg, 5)}
+        if name in flops:
+            tf = flops[name] / (avg * 1e-3) / 1e12
+            rec.update(bound="mfma", achieved_tflops=round(tf, 2),
+                       frac=round(tf / PEAK_BF16_TFLOPS, 4))
+        elif name in bytes_:
+            gbs = bytes_[name] / (avg * 1e-3) / 1e9
+            rec.update(bound="hbm", achieved_gbs=round(gbs, 1), frac=round(gbs / PEAK_HBM_GBS, 4))
+        out[name] = rec
+    return out
+
+
+def attn_step_fn(vl, torch, w, q, k, v, do, cu):
+    ws = torch.empty(vl.bwd_workspace_bytes(q.shape[0], k.shape[0], w.hq, w.hkv, w.d),
+                     dtype=torch.uint8, device=q.device)
+
+    def step():
+        o, lse = vl.varlen_attn_fwd(q, k, v, cu, cu, causal=True)
+        vl.varlen_attn_bwd(q, k, v, o, do, lse, cu, cu, causal=True, workspace=ws)
+    return step
+
+
+def bench_attention(vl, torch, w, steps, warmup, dev, tensors=None, profile=True):
+    import workloads
+    q, k, v, do = tensors if tensors is not None else workloads.make_tensors(w)
+    q, k, v, do = (t.to(dev) for t in (q, k, v, do))
+    cu = w.cu
+    step = attn_step_fn(vl, torch, w, q, k, v, do, cu)
+    for _ in range(warmup):
+        step()
+    if profile:
+        vl.profile_enable(True)
+    with Timer(torch) as tm:
+        for _ in range(steps):
+            step()
+    prof = vl.profile_read() if profile else {}
+    if profile:
+        vl.profile_enable(False)
+    pairs, ffwd, fbwd = useful(vl, cu, cu, True, w.hq, w.d)
+    ms = tm.wall_ms / steps
+    del q, k, v, do
+    return dict(ms=ms, event_ms=tm.event_ms / steps, pairs=pairs, flops_fwd=ffwd, flops_bwd=fbwd,
+                tflops=(ffwd + fbwd) / (ms * 1e-3) / 1e12, prof=prof)
+
+
+def attn_kernel_flops(pairs, hq, d):
+    # algorithmic FLOPs each kernel must do per launch (per visible pair):
+    # forward QK^T and PV; dK/dV kernel S, dP, dV, dK; dQ kernel only dQ
+    # (its S and dP recompute is overhead of the split design)
+    return {"attn_fwd": 4 * d * pairs * hq, "bwd_dkdv": 8 * d * pairs * hq,
+            "bwd_dq": 2 * d * pairs * hq}
+
+
+def cpu_baseline(w):
+    import numpy as np
+    import oracle
+    import workloads
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+    q, k, v, do = workloads.make_tensors(w)
+    f = lambda t: t.float().numpy()
+    qn, kn, vn, don = f(q), f(k), f(v), f(do)
+    cu = w.cu
+    t0 = time.perf_counter()
+    oracle.attn_bwd(qn, kn, vn, don, cu, cu, causal=True, return_fwd=True)
+    sec = time.perf_counter() - t0
+    vis = oracle.schedule.visible_pairs(cu, cu, True)
+    flops = 14 * w.d * vis * w.hq
+    return {"value": round(flops / sec / 1e12, 5), "unit": "TFLOP/s", "cores": int(threads),
+            "kind": "oracle", "seconds": round(sec, 2),
+            "host_cpus": os.cpu_count(), "affinity": len(os.sched_getaffinity(0)),
+            "sample": f"full {w.name} batch, fp64 numpy forward + backward "
+                      f"(O, LSE, dQ, dK, dV) of all {len(w.lengths)} documents x {w.hq} heads"}
+
+
+def bench_permute(vl, torch, dev, steps):
+    n, H, d, P = 49152, 32, 128, 8
+    g = torch.Generator(device=dev).manual_seed(0)
+    xs = [torch.randn(n, H, d, generator=g, device=dev).to(torch.bfloat16) for _ in range(2)]
+    ys = [torch.empty(P, n, H // P, d, dtype=torch.bfloat16, device=dev) for _ in range(2)]
+    for i in range(2):
+        vl.sp_seq2head(xs[i], P, out=ys[i])
+        vl.sp_head2seq(ys[i], out=xs[i])
+    vl.profile_enable(True)
+    for i in range(steps):
+        vl.sp_seq2head(xs[i % 2], P, out=ys[i % 2])     # alternate buffers: 768 MiB > MALL
+        vl.sp_head2seq(ys[(i + 1) % 2], out=xs[(i + 1) % 2])
+    prof = vl.profile_read()
+    vl.profile_enable(False)
+    nbytes = 2 * n * H * d * 2
+    return prof, {"sp_seq2head": nbytes, "sp_head2seq": nbytes}
+
+
+def bench_ring(vl, torch, dev, steps):
+    import numpy as np
+    import workloads
+    w = workloads.ring_256k()
+    n, c, qc = w.extra["n_chunks"], w.extra["chunk"], w.extra["q_chunk"]
+    q, k, v, _ = workloads.make_tensors(w, with_do=False)
+    qd = q[qc * c:(qc + 1) * c].contiguous().to(dev)
+    kd, vd = k.to(dev), v.to(dev)
+    del q, k, v
+    one = np.array([0, c], np.int32)
+    parts_o = [torch.empty(c, w.hq, w.d, dtype=torch.float32, device=dev) for _ in range(n)]
+    parts_l = [torch.empty(w.hq, c, dtype=torch.float32, device=dev) for _ in range(n)]
+
+    def step():
+        for j in range(n):
+            vl.varlen_attn_fwd(qd, kd[j * c:(j + 1) * c], vd[j * c:(j + 1) * c], one, one,
+                               causal=(j == qc), out=parts_o[j], lse=parts_l[j])
+        return vl.attn_lse_merge(parts_o, parts_l, out_dtype=torch.bfloat16)
+    step()
+    vl.profile_enable(True)
+    with Timer(torch) as tm:
+        for _ in range(steps):
+            step()
+    prof = vl.profile_read()
+    vl.profile_enable(False)
+    pairs = 7 * c * c + c * (c + 1) // 2
+    flops = 4 * w.d * pairs * w.hq
+    merge_bytes = n * (c * w.hq * w.d * 4 + c * w.hq * 4) + c * w.hq * w.d * 2 + c * w.hq * 4
+    ms = tm.wall_ms / steps
+    return {"workload": w.name, "ms_per_step": round(ms, 3),
+            "tflops": round(flops / (ms * 1e-3) / 1e12, 2), "useful_tflop": round(flops / 1e12, 3),
+            "kernels": kernel_table(prof, {}, {"lse_merge": merge_bytes}),
+            "attn_fwd_avg_ms": round(prof["attn_fwd"][1] / prof["attn_fwd"][0], 4)}
+
+
+def main():
+    a = _args()
+    if a.gpus != 1:
+        print(f"bench.py measures one GPU only: --gpus {a.gpus} is not supported "
+              "(no collectives in this build; see the sharding design notes)", file=sys.stderr)
+        sys.exit(2)
+    import numpy as np
+    import torch
+
+    import variable_length_sequence_amd as vl
+    import workloads
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    vl.lib()
+    dev = torch.device("cuda:0")
+    w = workloads.longtail_16k()
+    print(f"[bench] {w.name}: {len(w.lengths)} docs, {w.total} tokens, "
+          f"{a.warmup} warmup + {a.steps} timed steps", file=sys.stderr, flush=True)
+    r = bench_attention(vl, torch, w, a.steps, a.warmup, dev)
+    kflops = attn_kernel_flops(r["pairs"], w.hq, w.d)
+    bpre = 2 * w.total * w.hq * w.d * 2 + w.total * w.hq * 4
+    ktab = kernel_table(r["prof"], kflops, {"bwd_pre": bpre})
+    dom = max((n for n in kflops if n in r["prof"]), key=lambda n: r["prof"][n][1])
+    dom_avg = r["prof"][dom][1] / r["prof"][dom][0]
+    achieved = kflops[dom] / (dom_avg * 1e-3) / 1e12
+    out = {
+        "metric": "packed varlen causal attn fwd+bwd TFLOP/s (useful FLOPs) on 1 MI355X; % MFMA peak",
+        "value": round(r["tflops"], 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": a.steps,
+        "warmup": a.warmup,
+        "ms_per_step": round(r["ms"], 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": w.name, "tokens": w.total, "docs": len(w.lengths),
+                   "max_doc": max(w.lengths), "n_heads_q": w.hq, "n_heads_kv": w.hkv,
+                   "head_dim": w.d, "causal": True, "length_seed": 0,
+                   "lengths": "lognormal(median 512, sigma 1.2) clipped [64, 8192]"},
+        "pct_mfma_peak": round(100 * r["tflops"] / PEAK_BF16_TFLOPS, 2),
+        "useful_tflop_per_step": round((r["flops_fwd"] + r["flops_bwd"]) / 1e12, 4),
+        "roofline": {"bound": "mfma", "kernel": dom, "achieved": round(achieved, 2),
+                     "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                     "flops_per_launch": kflops[dom], "avg_launch_ms": round(dom_avg, 5)},
+        "kernels": ktab,
+    }
+    print(f"[bench] headline {out['value']} TFLOP/s, {out['ms_per_step']} ms/step", file=sys.stderr,
+          flush=True)
+    if not a.no_extra:
+        extra = {}
+        print("[bench] permute", file=sys.stderr, flush=True)
+        prof, by = bench_permute(vl, torch, dev, 10)
+        extra["ulysses_permute_49152x32x128_P8"] = kernel_table(prof, {}, by)
+        print("[bench] ring share", file=sys.stderr, flush=True)
+        extra["ring_256k_chunk7"] = bench_ring(vl, torch, dev, 2)
+        torch.cuda.empty_cache()
+        for wf, steps in ((workloads.ulysses_384k, 2), (workloads.mixed_128k, 3)):
+            ww = wf()
+            print(f"[bench] {ww.name}", file=sys.stderr, flush=True)
+            rr = bench_attention(vl, torch, ww, steps, 1, dev)
+            kf = attn_kernel_flops(rr["pairs"], ww.hq, ww.d)
+            extra[ww.name] = {"ms_per_step": round(rr["ms"], 3), "tflops": round(rr["tflops"], 2),
+                              "pct_mfma_peak": round(100 * rr["tflops"] / PEAK_BF16_TFLOPS, 2),
+                              "useful_tflop": round((rr["flops_fwd"] + rr["flops_bwd"]) / 1e12, 3),
+                              "kernels": kernel_table(rr["prof"], kf, {})}
+            torch.cuda.empty_cache()
+        # per length bucket of the Pareto batch: bucket-only packed sub-batches
+        mw = workloads.mixed_128k()
+        q, k, v, do = workloads.make_tensors(mw)
+        cu = mw.cu
+        buckets = {}
+        for name, idx in workloads.length_buckets(mw.lengths).items():
+            if not idx:
+                continue
+            rows = np.concatenate([np.arange(cu[i], cu[i + 1]) for i in idx])
+            sub = workloads.Workload(f"{mw.name}_{name}", [mw.lengths[i] for i in idx], hq=mw.hq,
+                                     hkv=mw.hkv, d=mw.d)
+            t = [x[rows].contiguous() for x in (q, k, v, do)]
+            rr = bench_attention(vl, torch, sub, 3, 1, dev, tensors=t, profile=False)
+            buckets[name] = {"docs": len(idx), "tokens": sub.total, "ms_per_step": round(rr["ms"], 3),
+                             "tflops": round(rr["tflops"], 2),
+                             "useful_tflop": round((rr["flops_fwd"] + rr["flops_bwd"]) / 1e12, 3)}
+            torch.cuda.empty_cache()
+        extra["mixed_128k_buckets"] = buckets
+        out["extra"] = extra
+    if not a.no_cpu_baseline:
+        print("[bench] cpu baseline (fp64 oracle)", file=sys.stderr, flush=True)
+        out["cpu_baseline"] = cpu_baseline(w)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -185,6 +185,19 @@ VL_API int varlen_schedule_export(const int32_t* cu_seqlens_q, const int32_t* cu
                            int64_t* useful_pairs, int64_t* issued_pairs,
                            int32_t* bq, int32_t* bk);
 
+/*
+ * varlen_profile_enable / varlen_profile_read - optional per-kernel timing.
+ * While enabled, every kernel the library launches is bracketed by two HIP
+ * events recorded on its launch stream.  Enabling clears earlier records.
+ * varlen_profile_read(idx, ...) reports the idx-th distinct kernel name seen
+ * (first-launch order): its launch count and summed elapsed milliseconds; it
+ * waits for those events and returns VL_EINVAL past the last name.
+ *   name      buffer of name_cap bytes for the NUL-terminated kernel name
+ */
+VL_API int varlen_profile_enable(int32_t on);
+VL_API int varlen_profile_read(int32_t idx, char* name, int32_t name_cap,
+                               int64_t* launches, double* total_ms);
+
 /* Message of the last failed call on this thread ("" if none). */
 VL_API const char* varlen_last_error(void);
 

@@ -29,7 +29,8 @@ STATUS = {0: "VL_OK", -1: "VL_EINVAL", -2: "VL_ESHAPE", -3: "VL_ESEQLENS",
 
 EXPORTS = ["varlen_attn_fwd", "varlen_attn_bwd_workspace_size", "varlen_attn_bwd",
            "attn_lse_merge", "sp_seq2head", "sp_head2seq", "varlen_schedule_export",
-           "varlen_last_error", "varlen_cache_clear", "varlen_version"]
+           "varlen_last_error", "varlen_cache_clear", "varlen_version", "varlen_profile_enable",
+           "varlen_profile_read"]
 
 
 class VarlenError(RuntimeError):
@@ -77,6 +78,10 @@ def lib():
     L.varlen_cache_clear.restype = None
     L.varlen_version.argtypes = []
     L.varlen_version.restype = ctypes.c_int
+    L.varlen_profile_enable.argtypes = [i32]
+    L.varlen_profile_enable.restype = ctypes.c_int
+    L.varlen_profile_read.argtypes = [i32, ctypes.c_char_p, i32, pi64, ctypes.POINTER(ctypes.c_double)]
+    L.varlen_profile_read.restype = ctypes.c_int
     _lib = L
     return L
 
@@ -226,6 +231,22 @@ def varlen_schedule_export(cu_q, cu_k, causal: bool, pass_: int, head_dim: int) 
                                     ctypes.byref(bk)))
     return {"items": items[:n.value], "useful_pairs": useful.value, "issued_pairs": issued.value,
             "bq": bq.value, "bk": bk.value}
+
+
+def profile_enable(on: bool = True):
+    """Start (clearing earlier records) or stop per-kernel HIP-event timing."""
+    _check(lib().varlen_profile_enable(int(on)))
+
+
+def profile_read() -> dict:
+    """{kernel name: (launches, total ms)} of the records since profile_enable(True)."""
+    out, i = {}, 0
+    buf = ctypes.create_string_buffer(128)
+    n, ms = ctypes.c_int64(0), ctypes.c_double(0.0)
+    while lib().varlen_profile_read(i, buf, 128, ctypes.byref(n), ctypes.byref(ms)) == 0:
+        out[buf.value.decode()] = (int(n.value), float(ms.value))
+        i += 1
+    return out
 
 
 def cache_clear():

@@ -18,7 +18,7 @@ CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libvarlen.so")
 
-SOURCES = ["scheduler.cpp", "api.cpp", "sp_permute.hip", "lse_merge.hip", "attn_fwd.hip",
+SOURCES = ["scheduler.cpp", "api.cpp", "profiler.cpp", "sp_permute.hip", "lse_merge.hip", "attn_fwd.hip",
            "attn_bwd.hip"]
 
 ARCH = "gfx950"

@@ -26,6 +26,7 @@
 
 #include "common.h"
 #include "launch.h"
+#include "profiler.h"
 
 namespace vl {
 
@@ -543,6 +544,7 @@ hipError_t run_bwd(const AttnShape& s, const uint16_t* q, const uint16_t* k, con
     constexpr int RPB = kThreads / (D / 8);
     const int64_t want = (s.total_q * s.hq + RPB - 1) / RPB;
     const int blocks = int(std::max<int64_t>(1, std::min<int64_t>(want, int64_t(n_cu) * 16)));
+    ProfScope prof("bwd_pre", stream);
     if (s.total_q > 0)
       hipLaunchKernelGGL((bwd_pre_kernel<D>), dim3(blocks), dim3(kThreads), 0, stream, o, dout,
                          delta, s.total_q, s.hq);
@@ -551,12 +553,14 @@ hipError_t run_bwd(const AttnShape& s, const uint16_t* q, const uint16_t* k, con
   if (head_split > 1 && kv_elems > 0) {
     const int64_t n4 = 2 * kv_elems / 4;
     const int blocks = int(std::min<int64_t>((n4 + kThreads - 1) / kThreads, int64_t(n_cu) * 16));
+    ProfScope prof("bwd_dkv_zero", stream);
     hipLaunchKernelGGL(fill_zero_kernel, dim3(blocks), dim3(kThreads), 0, stream,
                        reinterpret_cast<f32x4*>(dkv_acc), n4);
   }
   if (n_bwd > 0) {
     const int groups = (n_bwd + 7) / 8;
     const dim3 grid(unsigned(groups) * 8u * unsigned(s.hkv * head_split));
+    ProfScope prof("bwd_dkdv", stream);
     hipLaunchKernelGGL((attn_bwd_dkdv_kernel<D>), grid, dim3(kThreads), 0, stream, q, k, v, dout,
                        lse, delta, bwd_list, n_bwd, s.hq, s.hkv, head_split, s.scale, s.causal,
                        s.total_q, dk, dv, dkv_acc, s.total_k);
@@ -564,6 +568,7 @@ hipError_t run_bwd(const AttnShape& s, const uint16_t* q, const uint16_t* k, con
   if (head_split > 1 && kv_elems > 0) {
     const int64_t n4 = kv_elems / 4;
     const int blocks = int(std::min<int64_t>((n4 + kThreads - 1) / kThreads, int64_t(n_cu) * 16));
+    ProfScope prof("bwd_dkv_convert", stream);
     hipLaunchKernelGGL(f32_to_bf16_kernel, dim3(blocks), dim3(kThreads), 0, stream,
                        reinterpret_cast<const f32x4*>(dkv_acc), reinterpret_cast<u32x2*>(dk), n4);
     hipLaunchKernelGGL(f32_to_bf16_kernel, dim3(blocks), dim3(kThreads), 0, stream,
@@ -573,6 +578,7 @@ hipError_t run_bwd(const AttnShape& s, const uint16_t* q, const uint16_t* k, con
   if (n_fwd > 0) {
     const int groups = (n_fwd + 7) / 8;
     const dim3 grid(unsigned(groups) * 8u * unsigned(s.hq));
+    ProfScope prof("bwd_dq", stream);
     hipLaunchKernelGGL((attn_bwd_dq_kernel<D>), grid, dim3(kThreads), 0, stream, q, k, v, dout, lse,
                        delta, fwd_list, n_fwd, s.hq, s.hkv, s.scale, s.causal, s.total_q, dq);
   }

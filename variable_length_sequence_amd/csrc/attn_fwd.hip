@@ -28,6 +28,7 @@
 
 #include "common.h"
 #include "launch.h"
+#include "profiler.h"
 
 namespace vl {
 
@@ -300,6 +301,7 @@ hipError_t launch_attn_fwd(const AttnShape& s, const void* q, const void* k, con
   const auto* qq = reinterpret_cast<const uint16_t*>(q);
   const auto* kk = reinterpret_cast<const uint16_t*>(k);
   const auto* vv = reinterpret_cast<const uint16_t*>(v);
+  ProfScope prof("attn_fwd", stream);
 #define VL_FWD(DD, F32)                                                                        \
   hipLaunchKernelGGL((attn_fwd_kernel<DD, F32>), grid, dim3(kThreads), 0, stream, qq, kk, vv,   \
                      items, n_items, s.hq, s.hkv, s.scale, s.causal, out, lse, s.total_q)

@@ -15,6 +15,7 @@
 
 #include "common.h"
 #include "launch.h"
+#include "profiler.h"
 
 namespace vl {
 
@@ -119,6 +120,7 @@ hipError_t dispatch(const PartPtrs& p, int n_parts, int64_t n_rows, int n_heads,
   (void)hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev);
   const int64_t want = (n_pairs + rows_per_block - 1) / rows_per_block;
   const int blocks = int(std::max<int64_t>(1, std::min<int64_t>(want, int64_t(n_cu) * 16)));
+  ProfScope prof("lse_merge", stream);
 #define VL_MERGE_CASE(N)                                                                     \
   case N:                                                                                    \
     hipLaunchKernelGGL((lse_merge_kernel<TI, TO, N>), dim3(blocks), dim3(kThreads), 0, stream, p, \

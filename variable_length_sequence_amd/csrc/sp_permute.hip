@@ -14,6 +14,7 @@
 
 #include "fastdiv.h"
 #include "launch.h"
+#include "profiler.h"
 
 namespace vl {
 
@@ -82,6 +83,7 @@ hipError_t run(const void* src, void* dst, int64_t n_tok, int32_t deg, int64_t r
     const int64_t want = (int64_t(n_units) + kThreads * kIlp - 1) / (kThreads * kIlp);
     const int blocks = int(std::max<int64_t>(1, std::min<int64_t>(want, int64_t(n_cu) * 16)));
     // the [n, H, d] side is offset to this token range; the other side is indexed globally
+    ProfScope prof(dir == 0 ? "sp_seq2head" : "sp_head2seq", stream);
     if (dir == 0) {
       const U* s = reinterpret_cast<const U*>(src) + t0 * units_per_tok;
       hipLaunchKernelGGL((sp_permute_kernel<U, 0>), dim3(blocks), dim3(kThreads), 0, stream, s,
