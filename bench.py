@@ -210,7 +210,7 @@ def main():
     a = _args()
     if a.gpus != 1:
         print(f"bench.py measures one GPU only: --gpus {a.gpus} is not supported "
-              "(no collectives in this build; see the sharding design notes)", file=sys.stderr)
+              "(this build runs on one GPU and has no collectives)", file=sys.stderr)
         sys.exit(2)
     import numpy as np
     import torch

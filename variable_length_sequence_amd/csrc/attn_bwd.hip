@@ -94,11 +94,14 @@ __device__ __forceinline__ void load_block4x8(u32x4 (&r)[4], const uint16_t* __r
 }
 
 // Writes the block row-major (stride rs) and transposed (stride ts) into LDS.
+// Row r of the row-major copy is kept at LDS row swap_bits23(r), so the
+// permuted A-operand rows a lane reads are consecutive LDS rows.
 __device__ __forceinline__ void store_block4x8(const u32x4 (&r)[4], uint16_t* nat, int rs,
                                                uint16_t* tr, int ts, int row0, int col0) {
   if (nat) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) *reinterpret_cast<u32x4*>(nat + (row0 + j) * rs + col0) = r[j];
+    for (int j = 0; j < 4; ++j)
+      *reinterpret_cast<u32x4*>(nat + swap_bits23(row0 + j) * rs + col0) = r[j];
   }
 #pragma unroll
   for (int u = 0; u < 4; ++u) {
@@ -207,7 +210,9 @@ attn_bwd_dkdv_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
   const bool stage_q = tid < NBLK;
   const bool stage_do = tid >= 128 && tid < 128 + NBLK;
   const int sb = stage_q ? tid : tid - 128;
-  const int s_row = (sb / CPR) * 4, s_col = (sb % CPR) * 8;
+  // row group fastest across lanes: the transposed 8-byte LDS writes of one
+  // instruction then fall on consecutive banks
+  const int s_row = (sb % (KB_Q / 4)) * 4, s_col = (sb / (KB_Q / 4)) * 8;
 
   u32x4 pre[4];
   float pre_lse = 0.f;
@@ -254,9 +259,8 @@ attn_bwd_dkdv_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
       pacc[i] = 0.f;
     }
     {
-      const int prow = swap_bits23(l32);
-      const uint16_t* qp = &sm.q[prow * KvSmem<D>::NS + 8 * half];
-      const uint16_t* dp = &sm.dout[prow * KvSmem<D>::NS + 8 * half];
+      const uint16_t* qp = &sm.q[l32 * KvSmem<D>::NS + 8 * half];
+      const uint16_t* dp = &sm.dout[l32 * KvSmem<D>::NS + 8 * half];
 #pragma unroll
       for (int s = 0; s < NKS; ++s) {
         sacc = mfma32(as_bf16x8(*reinterpret_cast<const u32x4*>(qp + 16 * s)), kf[s], sacc);
@@ -282,7 +286,7 @@ attn_bwd_dkdv_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
     }
     float p[16], ds[16];
 #pragma unroll
-    for (int i = 0; i < 16; ++i) p[i] = exp2f(fmaf(sacc[i], c, -lse_r[i]));
+    for (int i = 0; i < 16; ++i) p[i] = __builtin_amdgcn_exp2f(fmaf(sacc[i], c, -lse_r[i]));
     if (need_mask) {
       // element i holds query qb + e, e = 16 (i / 8) + i % 8; it is visible iff
       // e < lq - qb (a real row), key < lk, and (causal) e >= key - off - qb
@@ -428,7 +432,7 @@ attn_bwd_dq_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ 
   const int wq_last = min(q0 + w * 32 + 31, lq - 1);
 
   const bool stage = tid < NBLK;
-  const int s_row = (tid / CPR) * 4, s_col = (tid % CPR) * 8;
+  const int s_row = (tid % (QB_K / 4)) * 4, s_col = (tid / (QB_K / 4)) * 8;
   u32x4 pk[4], pv[4];
   auto fetch = [&](int kv0) {
     if (stage) {
@@ -446,7 +450,7 @@ attn_bwd_dq_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ 
       store_block4x8(pk, sm.k, QSmem<D>::NS, sm.kt, QSmem<D>::TS, s_row, s_col);
 #pragma unroll
       for (int j = 0; j < 4; ++j)
-        *reinterpret_cast<u32x4*>(&sm.v[(s_row + j) * QSmem<D>::NS + s_col]) = pv[j];
+        *reinterpret_cast<u32x4*>(&sm.v[swap_bits23(s_row + j) * QSmem<D>::NS + s_col]) = pv[j];
     }
     __syncthreads();
     if (kt + 1 < n_kv) fetch(kv0 + QB_K);
@@ -463,7 +467,7 @@ attn_bwd_dq_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ 
         s[kb][i] = 0.f;
         dp[kb][i] = 0.f;
       }
-      const int prow = kb * 32 + swap_bits23(l32);
+      const int prow = kb * 32 + l32;
       const uint16_t* kp = &sm.k[prow * QSmem<D>::NS + 8 * half];
       const uint16_t* vp = &sm.v[prow * QSmem<D>::NS + 8 * half];
 #pragma unroll
@@ -486,7 +490,7 @@ attn_bwd_dq_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ 
 #pragma unroll
           for (int e = 0; e < 2; ++e) {
             const int i = 8 * hs + 2 * j + e;
-            float pv_ = exp2f(fmaf(s[kb][i], c, -lse2));
+            float pv_ = __builtin_amdgcn_exp2f(fmaf(s[kb][i], c, -lse2));
             if (need_mask) {
               const int kk = kv0 + kb * 32 + 16 * hs + 8 * half + 2 * j + e;
               if (kk > lim) pv_ = 0.f;

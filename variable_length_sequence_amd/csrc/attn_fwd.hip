@@ -71,7 +71,7 @@ __device__ __forceinline__ void load_tile(TileRegs<D>& r, const uint16_t* __rest
       r.k[i] = u32x4{0, 0, 0, 0};
   }
   if (tid < TileRegs<D>::VBLK) {
-    const int kg = tid / CPR, c8 = tid % CPR;
+    const int kg = tid % (BK / 4), c8 = tid / (BK / 4);
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int key = kv0 + kg * 4 + j;
@@ -90,10 +90,12 @@ __device__ __forceinline__ void store_tile(const TileRegs<D>& r, FwdSmem<D>& sm,
   for (int i = 0; i < TileRegs<D>::KCH; ++i) {
     const int id = tid + i * kThreads;
     const int row = id / CPR, c8 = id % CPR;
-    *reinterpret_cast<u32x4*>(&sm.k[row * FwdSmem<D>::KS + c8 * 8]) = r.k[i];
+    // key row r is kept at LDS row swap_bits23(r): the A-operand rows a lane
+    // needs are then consecutive LDS rows
+    *reinterpret_cast<u32x4*>(&sm.k[swap_bits23(row) * FwdSmem<D>::KS + c8 * 8]) = r.k[i];
   }
   if (tid < TileRegs<D>::VBLK) {
-    const int kg = tid / CPR, c8 = tid % CPR;
+    const int kg = tid % (BK / 4), c8 = tid / (BK / 4);
     // transpose 4 keys x 8 dims into 8 dims x 4 keys
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
@@ -161,7 +163,7 @@ attn_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
   for (int cb = 0; cb < NCB; ++cb)
 #pragma unroll
     for (int i = 0; i < 16; ++i) acc[cb][i] = 0.f;
-  float m_run = -INFINITY;  // running max of raw scores of this lane's query
+  float m_run = -INFINITY;  // reference max of raw scores of this lane's query
   float l_run = 0.f;        // running sum (this half-wave's keys)
 
   const uint16_t* kbase = k + int64_t(it.k_start) * kv_tok + int64_t(g) * D;
@@ -193,7 +195,7 @@ attn_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
       for (int i = 0; i < 16; ++i) s[kb][i] = 0.f;
-      const uint16_t* kp = &sm.k[(kb * 32 + swap_bits23(l32)) * FwdSmem<D>::KS + 8 * half];
+      const uint16_t* kp = &sm.k[(kb * 32 + l32) * FwdSmem<D>::KS + 8 * half];
 #pragma unroll
       for (int st = 0; st < NKS; ++st) {
         const bf16x8 a = as_bf16x8(*reinterpret_cast<const u32x4*>(kp + 16 * st));
@@ -218,11 +220,21 @@ attn_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
 #pragma unroll
       for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[kb][i]);
     mx = fmaxf(mx, xor32(mx));
+    // m_run is the reference max of the exponent.  It is moved (and O and l
+    // rescaled) only when the running max exceeds it by more than 2^8 in
+    // probability, so p <= 256 and most tiles skip the rescale entirely.
     const float m_new = fmaxf(m_run, mx);
-    const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-    const float alpha = exp2f((m_run - m_use) * c);
-    const float mc = m_use * c;
-    m_run = m_new;
+    const bool grow = (m_new - m_run) * c > 8.f;   // false while both are -inf
+    if (__ballot(grow)) {
+      const float alpha = grow ? __builtin_amdgcn_exp2f((m_run - m_new) * c) : 1.f;
+      m_run = grow ? m_new : m_run;
+      l_run *= alpha;
+#pragma unroll
+      for (int cb = 0; cb < NCB; ++cb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) acc[cb][i] *= alpha;
+    }
+    const float mc = (m_run == -INFINITY) ? 0.f : m_run * c;
 
     float psum = 0.f;
     bf16x8 pf[2][2];
@@ -233,19 +245,15 @@ attn_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
         u32x4 u;
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          const float p0 = exp2f(fmaf(s[kb][8 * hs + 2 * j], c, -mc));
-          const float p1 = exp2f(fmaf(s[kb][8 * hs + 2 * j + 1], c, -mc));
+          const float p0 = __builtin_amdgcn_exp2f(fmaf(s[kb][8 * hs + 2 * j], c, -mc));
+          const float p1 = __builtin_amdgcn_exp2f(fmaf(s[kb][8 * hs + 2 * j + 1], c, -mc));
           psum += p0 + p1;
           u[j] = pack_bf16x2(p0, p1);
         }
         pf[kb][hs] = as_bf16x8(u);
       }
     }
-    l_run = l_run * alpha + psum;
-#pragma unroll
-    for (int cb = 0; cb < NCB; ++cb)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) acc[cb][i] *= alpha;
+    l_run += psum;
 
     // O^T += V^T P^T
 #pragma unroll
