@@ -244,10 +244,10 @@ attn_bwd_dkdv_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
     __syncthreads();
     if (step + 1 < n_steps) fetch(step + 1);
 
-    // wave-uniform: does any query of this tile see any key of this wave?
-    const int iq_last = min(i0 + KB_Q - 1, lq - 1);
-    const bool live = (wk_first < lk) && (!causal || wk_first <= iq_last + off);
-    if (!live) continue;
+    // Waves whose keys no query of this tile sees still run the step (fully
+    // masked): all waves meet at the next barrier anyway, and a skip branch
+    // here makes the compiler shuttle the dK/dV accumulators between VGPRs
+    // and AGPRs on every step.
     const bool need_mask = (i0 + KB_Q > lq) || (wk_first + 31 >= lk) ||
                            (causal && wk_last > i0 + off);
 
