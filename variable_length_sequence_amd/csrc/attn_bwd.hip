@@ -119,6 +119,7 @@ __device__ __forceinline__ void store_block4x8(const u32x4 (&r)[4], uint16_t* na
 // ---------------------------------------------------------------- dK, dV
 constexpr int KB_Q = kBwdBQ;   // 32 query rows per step
 constexpr int KB_K = kBwdBK;   // 128 keys per workgroup
+constexpr int kKvThreads = 512;
 
 template <int D>
 struct KvSmem {
@@ -132,8 +133,14 @@ struct KvSmem {
   float delta[KB_Q];
 };
 
+// 8 waves: waves 0-3 accumulate dV, waves 4-7 dK, for the same four 32-key
+// blocks (wave w and w + 4 share block w & 3 and, being w apart by 4, the same
+// SIMD).  Both roles recompute S = Q K^T; the dV role then needs only
+// P^T dO, the dK role dP = dO V^T and dS^T Q.  Splitting the roles halves the
+// accumulators a wave holds, so two waves fit per SIMD and one wave's
+// exponentials overlap the other's MFMAs.
 template <int D>
-__global__ void __launch_bounds__(kThreads, 1)
+__global__ void __launch_bounds__(kKvThreads)
 attn_bwd_dkdv_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
                      const uint16_t* __restrict__ v, const uint16_t* __restrict__ dout,
                      const float* __restrict__ lse, const float* __restrict__ delta,
@@ -159,7 +166,9 @@ attn_bwd_dkdv_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int w = tid >> 6;
+  const int wave = tid >> 6;
+  const int role = wave >> 2;                  // 0: dV, 1: dK
+  const int w = wave & 3;                      // key block
   const int half = lane >> 5;
   const int l32 = lane & 31;
 
@@ -174,7 +183,7 @@ attn_bwd_dkdv_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
   const int hpg = grp / head_split;            // q heads handled here
   const int h_begin = g * grp + split * hpg;
 
-  // K and V operands (B of S = Q K^T and of dP = dO V^T): key l32, dims 16s + 8 half ..
+  // K (both roles) and V (dK role) as B operands: key l32, dims 16s + 8 half ..
   bf16x8 kf[NKS], vf[NKS];
   {
     const int64_t row = int64_t(it.k_start) + key;
@@ -185,33 +194,28 @@ attn_bwd_dkdv_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
       u32x4 a = u32x4{0, 0, 0, 0}, bb = u32x4{0, 0, 0, 0};
       if (key < lk) {
         a = *reinterpret_cast<const u32x4*>(kp + 16 * s);
-        bb = *reinterpret_cast<const u32x4*>(vp + 16 * s);
+        if (role) bb = *reinterpret_cast<const u32x4*>(vp + 16 * s);
       }
       kf[s] = as_bf16x8(a);
       vf[s] = as_bf16x8(bb);
     }
   }
 
-  f32x16 dk_acc[NCB], dv_acc[NCB];
+  f32x16 acc[NCB];                             // dV (role 0) or dK (role 1)
 #pragma unroll
   for (int cb = 0; cb < NCB; ++cb)
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      dk_acc[cb][i] = 0.f;
-      dv_acc[cb][i] = 0.f;
-    }
+    for (int i = 0; i < 16; ++i) acc[cb][i] = 0.f;
 
-  // this wave's keys [wk_first, wk_last]; queries that may see them start at wk_first - off
   const int wk_first = j0 + w * 32;
-  const int wk_last = min(j0 + w * 32 + 31, lk - 1);
   const int n_steps = hpg * it.count;
 
-  // staging: threads [0, NBLK) stage Q, [128, 128 + NBLK) stage dO
+  // staging by the dV waves: threads [0, NBLK) stage Q, [128, 128 + NBLK) dO;
+  // row group fastest across lanes so the transposed LDS writes hit
+  // consecutive banks
   const bool stage_q = tid < NBLK;
   const bool stage_do = tid >= 128 && tid < 128 + NBLK;
   const int sb = stage_q ? tid : tid - 128;
-  // row group fastest across lanes: the transposed 8-byte LDS writes of one
-  // instruction then fall on consecutive banks
   const int s_row = (sb % (KB_Q / 4)) * 4, s_col = (sb / (KB_Q / 4)) * 8;
 
   u32x4 pre[4];
@@ -240,95 +244,94 @@ attn_bwd_dkdv_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
     if (stage_q) store_block4x8(pre, sm.q, KvSmem<D>::NS, sm.qt, KvSmem<D>::TS, s_row, s_col);
     if (stage_do) store_block4x8(pre, sm.dout, KvSmem<D>::NS, sm.dot, KvSmem<D>::TS, s_row, s_col);
     if (tid < KB_Q) sm.lse2[tid] = (pre_lse == -INFINITY) ? INFINITY : pre_lse * kLog2e;
-    else if (tid >= 64 && tid < 64 + KB_Q) sm.delta[tid - 64] = pre_lse;
+    else if (tid >= 64 && tid < 64 + KB_Q) sm.delta[tid - 64] = pre_lse * scale;
     __syncthreads();
     if (step + 1 < n_steps) fetch(step + 1);
 
-    // Waves whose keys no query of this tile sees still run the step (fully
-    // masked): all waves meet at the next barrier anyway, and a skip branch
-    // here makes the compiler shuttle the dK/dV accumulators between VGPRs
-    // and AGPRs on every step.
-    const bool need_mask = (i0 + KB_Q > lq) || (wk_first + 31 >= lk) ||
-                           (causal && wk_last > i0 + off);
-
-    // S = Q K^T and dP = dO V^T (rows: queries 16s + 8 half + t; cols: this wave's keys)
-    f32x16 sacc, pacc;
+    // S = Q K^T (rows: queries 16s + 8 half + t; cols: this wave's keys).
+    // Waves whose keys this query tile cannot see still run the step, fully
+    // masked: every wave meets at the next barrier anyway.
+    f32x16 sacc;
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      sacc[i] = 0.f;
-      pacc[i] = 0.f;
-    }
+    for (int i = 0; i < 16; ++i) sacc[i] = 0.f;
     {
       const uint16_t* qp = &sm.q[l32 * KvSmem<D>::NS + 8 * half];
-      const uint16_t* dp = &sm.dout[l32 * KvSmem<D>::NS + 8 * half];
 #pragma unroll
-      for (int s = 0; s < NKS; ++s) {
+      for (int s = 0; s < NKS; ++s)
         sacc = mfma32(as_bf16x8(*reinterpret_cast<const u32x4*>(qp + 16 * s)), kf[s], sacc);
-        pacc = mfma32(as_bf16x8(*reinterpret_cast<const u32x4*>(dp + 16 * s)), vf[s], pacc);
-      }
     }
 
-    // P and dS; the 16 queries of this lane are 16s + 8 half + t
-    float lse_r[16], dl_r[16];
-#pragma unroll
-    for (int s = 0; s < 2; ++s) {
-      const f32x4 l0 = *reinterpret_cast<const f32x4*>(&sm.lse2[16 * s + 8 * half]);
-      const f32x4 l1 = *reinterpret_cast<const f32x4*>(&sm.lse2[16 * s + 8 * half + 4]);
-      const f32x4 d0 = *reinterpret_cast<const f32x4*>(&sm.delta[16 * s + 8 * half]);
-      const f32x4 d1 = *reinterpret_cast<const f32x4*>(&sm.delta[16 * s + 8 * half + 4]);
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        lse_r[8 * s + j] = l0[j];
-        lse_r[8 * s + 4 + j] = l1[j];
-        dl_r[8 * s + j] = d0[j];
-        dl_r[8 * s + 4 + j] = d1[j];
-      }
-    }
-    float p[16], ds[16];
-#pragma unroll
-    for (int i = 0; i < 16; ++i) p[i] = __builtin_amdgcn_exp2f(fmaf(sacc[i], c, -lse_r[i]));
-    if (need_mask) {
-      // element i holds query qb + e, e = 16 (i / 8) + i % 8; it is visible iff
-      // e < lq - qb (a real row), key < lk, and (causal) e >= key - off - qb
+    // P; element i holds query qb + e, e = 16 (i / 8) + i % 8.  It is visible
+    // iff e < lq - qb (a real row), key < lk, and (causal) e >= key - off - qb.
+    float p[16];
+    {
       const int qb = i0 + 8 * half;
-      const int e_end = lq - qb;
       const int e_min = causal ? key - off - qb : INT32_MIN;
-      const int e_cap = (key < lk) ? e_end : INT32_MIN;
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int e = 16 * (i >> 3) + (i & 7);
-        p[i] = (e < e_cap && e >= e_min) ? p[i] : 0.f;
-      }
-    }
-#pragma unroll
-    for (int i = 0; i < 16; ++i) ds[i] = p[i] * (pacc[i] - dl_r[i]) * scale;
-    bf16x8 pf[2], dsf[2];
-#pragma unroll
-    for (int s = 0; s < 2; ++s) {
-      u32x4 up, ud;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        up[j] = pack_bf16x2(p[8 * s + 2 * j], p[8 * s + 2 * j + 1]);
-        ud[j] = pack_bf16x2(ds[8 * s + 2 * j], ds[8 * s + 2 * j + 1]);
-      }
-      pf[s] = as_bf16x8(up);
-      dsf[s] = as_bf16x8(ud);
-    }
-
-    // dV += P^T dO, dK += dS^T Q   (B operands from the transposed tiles)
-#pragma unroll
-    for (int cb = 0; cb < NCB; ++cb) {
-      const uint16_t* dtp = &sm.dot[(cb * 32 + l32) * KvSmem<D>::TS + 8 * half];
-      const uint16_t* qtp = &sm.qt[(cb * 32 + l32) * KvSmem<D>::TS + 8 * half];
+      const int e_cap = (key < lk) ? lq - qb : INT32_MIN;
 #pragma unroll
       for (int s = 0; s < 2; ++s) {
-        dv_acc[cb] = mfma32(pf[s], as_bf16x8(*reinterpret_cast<const u32x4*>(dtp + 16 * s)), dv_acc[cb]);
-        dk_acc[cb] = mfma32(dsf[s], as_bf16x8(*reinterpret_cast<const u32x4*>(qtp + 16 * s)), dk_acc[cb]);
+        const f32x4 l0 = *reinterpret_cast<const f32x4*>(&sm.lse2[16 * s + 8 * half]);
+        const f32x4 l1 = *reinterpret_cast<const f32x4*>(&sm.lse2[16 * s + 8 * half + 4]);
+#pragma unroll
+        for (int t = 0; t < 8; ++t) {
+          const int i = 8 * s + t;
+          const int e = 16 * s + t;
+          const float pv = __builtin_amdgcn_exp2f(fmaf(sacc[i], c, -(t < 4 ? l0[t] : l1[t - 4])));
+          p[i] = (e < e_cap && e >= e_min) ? pv : 0.f;
+        }
       }
+    }
+
+    // A operand of the accumulation: P (dV role) or dS = P (dP - D) scale (dK role)
+    bf16x8 af[2];
+    if (role == 0) {
+#pragma unroll
+      for (int s = 0; s < 2; ++s) {
+        u32x4 u;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) u[j] = pack_bf16x2(p[8 * s + 2 * j], p[8 * s + 2 * j + 1]);
+        af[s] = as_bf16x8(u);
+      }
+    } else {
+      f32x16 pacc;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) pacc[i] = 0.f;
+      const uint16_t* dp = &sm.dout[l32 * KvSmem<D>::NS + 8 * half];
+#pragma unroll
+      for (int s = 0; s < NKS; ++s)
+        pacc = mfma32(as_bf16x8(*reinterpret_cast<const u32x4*>(dp + 16 * s)), vf[s], pacc);
+#pragma unroll
+      for (int s = 0; s < 2; ++s) {
+        const f32x4 d0 = *reinterpret_cast<const f32x4*>(&sm.delta[16 * s + 8 * half]);
+        const f32x4 d1 = *reinterpret_cast<const f32x4*>(&sm.delta[16 * s + 8 * half + 4]);
+        u32x4 u;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int i = 8 * s + 2 * j;
+          const float da = (2 * j < 4) ? d0[2 * j] : d1[2 * j - 4];
+          const float db = (2 * j + 1 < 4) ? d0[2 * j + 1] : d1[2 * j + 1 - 4];
+          u[j] = pack_bf16x2(p[i] * fmaf(pacc[i], scale, -da), p[i + 1] * fmaf(pacc[i + 1], scale, -db));
+        }
+        af[s] = as_bf16x8(u);
+      }
+    }
+
+    // dV += P^T dO or dK += dS^T Q  (B operands from the transposed tiles)
+    {
+      const uint16_t* bt = (role == 0 ? sm.dot : sm.qt) + l32 * KvSmem<D>::TS + 8 * half;
+#pragma unroll
+      for (int cb = 0; cb < NCB; ++cb)
+#pragma unroll
+        for (int s = 0; s < 2; ++s)
+          acc[cb] = mfma32(af[s],
+                           as_bf16x8(*reinterpret_cast<const u32x4*>(bt + cb * 32 * KvSmem<D>::TS + 16 * s)),
+                           acc[cb]);
     }
   }
 
   // epilogue: lane holds column c = 32 cb + l32 of keys 32 w + 8 (v/4) + 4 half + v%4
+  uint16_t* outp = role == 0 ? dv : dk;
+  float* accp = dkv_acc + (role == 0 ? total_k * kv_tok : 0);
 #pragma unroll
   for (int cb = 0; cb < NCB; ++cb) {
 #pragma unroll
@@ -336,16 +339,14 @@ attn_bwd_dkdv_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
       const int kk = j0 + w * 32 + 8 * (i >> 2) + 4 * half + (i & 3);
       if (kk < lk) {
         const int64_t idx = (int64_t(it.k_start) + kk) * kv_tok + int64_t(g) * D + cb * 32 + l32;
-        if (head_split == 1) {
-          dk[idx] = __builtin_bit_cast(uint16_t, (__bf16)dk_acc[cb][i]);
-          dv[idx] = __builtin_bit_cast(uint16_t, (__bf16)dv_acc[cb][i]);
-        } else {
-          atomicAdd(dkv_acc + idx, dk_acc[cb][i]);
-          atomicAdd(dkv_acc + total_k * kv_tok + idx, dv_acc[cb][i]);
-        }
+        if (head_split == 1)
+          outp[idx] = __builtin_bit_cast(uint16_t, (__bf16)acc[cb][i]);
+        else
+          atomicAdd(accp + idx, acc[cb][i]);
       }
     }
   }
+  (void)wk_first;
 }
 
 // ---------------------------------------------------------------- dQ
@@ -565,7 +566,7 @@ hipError_t run_bwd(const AttnShape& s, const uint16_t* q, const uint16_t* k, con
     const int groups = (n_bwd + 7) / 8;
     const dim3 grid(unsigned(groups) * 8u * unsigned(s.hkv * head_split));
     ProfScope prof("bwd_dkdv", stream);
-    hipLaunchKernelGGL((attn_bwd_dkdv_kernel<D>), grid, dim3(kThreads), 0, stream, q, k, v, dout,
+    hipLaunchKernelGGL((attn_bwd_dkdv_kernel<D>), grid, dim3(kKvThreads), 0, stream, q, k, v, dout,
                        lse, delta, bwd_list, n_bwd, s.hq, s.hkv, head_split, s.scale, s.causal,
                        s.total_q, dk, dv, dkv_acc, s.total_k);
   }

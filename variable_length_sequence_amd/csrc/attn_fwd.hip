@@ -189,18 +189,39 @@ attn_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     if (!wave_live) continue;
     const bool need_mask = (kv0 + BK > lk) || (causal && kv0 + BK - 1 > wq_first + off);
 
-    // S^T for the two 32-key halves of the tile
+    // S^T for the two 32-key halves of the tile.  K fragments are read from
+    // LDS kPf steps ahead of the MFMA that consumes them, and the schedule is
+    // pinned to (1 MFMA, 1 LDS read) pairs so the read latency hides behind
+    // the matrix pipe.
     f32x16 s[2];
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
+    for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int i = 0; i < 16; ++i) s[kb][i] = 0.f;
-      const uint16_t* kp = &sm.k[(kb * 32 + l32) * FwdSmem<D>::KS + 8 * half];
+    {
+      constexpr int NF = 2 * NKS;
+      constexpr int kPf = 4;
+      const uint16_t* kp = &sm.k[l32 * FwdSmem<D>::KS + 8 * half];
+      auto kfrag = [&](int f) {
+        return as_bf16x8(*reinterpret_cast<const u32x4*>(
+            kp + (f / NKS) * 32 * FwdSmem<D>::KS + 16 * (f % NKS)));
+      };
+      bf16x8 kr[kPf];
 #pragma unroll
-      for (int st = 0; st < NKS; ++st) {
-        const bf16x8 a = as_bf16x8(*reinterpret_cast<const u32x4*>(kp + 16 * st));
-        s[kb] = mfma32(a, qf[st], s[kb]);
+      for (int f = 0; f < kPf; ++f) kr[f] = kfrag(f);
+#pragma unroll
+      for (int f = 0; f < NF; ++f) {
+        const bf16x8 a = kr[f % kPf];
+        if (f + kPf < NF) kr[f % kPf] = kfrag(f + kPf);
+        s[f / NKS] = mfma32(a, qf[f % NKS], s[f / NKS]);
       }
+      __builtin_amdgcn_sched_group_barrier(0x100, kPf, 0);
+#pragma unroll
+      for (int f = 0; f < NF - kPf; ++f) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x008, kPf, 0);
     }
 
     if (need_mask) {
@@ -236,37 +257,57 @@ attn_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     }
     const float mc = (m_run == -INFINITY) ? 0.f : m_run * c;
 
+    // P (bf16) for the four 16-key steps j = (kb, hs), and O^T += V^T P^T.
+    // The exponentials of step j+1 are computed while step j's MFMAs run.
     float psum = 0.f;
-    bf16x8 pf[2][2];
+    auto pstep = [&](int j) {
+      const int kb = j >> 1, hs = j & 1;
+      u32x4 u;
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
+      for (int e = 0; e < 4; ++e) {
+        const float p0 = __builtin_amdgcn_exp2f(fmaf(s[kb][8 * hs + 2 * e], c, -mc));
+        const float p1 = __builtin_amdgcn_exp2f(fmaf(s[kb][8 * hs + 2 * e + 1], c, -mc));
+        psum += p0 + p1;
+        u[e] = pack_bf16x2(p0, p1);
+      }
+      return as_bf16x8(u);
+    };
+    const uint16_t* vp = &sm.vt[l32 * FwdSmem<D>::VS + 8 * half];
+    auto vfrag = [&](int cb, int j) {
+      return as_bf16x8(*reinterpret_cast<const u32x4*>(
+          vp + cb * 32 * FwdSmem<D>::VS + (j >> 1) * 32 + (j & 1) * 16));
+    };
+    bf16x8 pcur = pstep(0);
+    bf16x8 vr[NCB];
 #pragma unroll
-      for (int hs = 0; hs < 2; ++hs) {
-        u32x4 u;
+    for (int cb = 0; cb < NCB; ++cb) vr[cb] = vfrag(cb, 0);
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const float p0 = __builtin_amdgcn_exp2f(fmaf(s[kb][8 * hs + 2 * j], c, -mc));
-          const float p1 = __builtin_amdgcn_exp2f(fmaf(s[kb][8 * hs + 2 * j + 1], c, -mc));
-          psum += p0 + p1;
-          u[j] = pack_bf16x2(p0, p1);
-        }
-        pf[kb][hs] = as_bf16x8(u);
+    for (int j = 0; j < 4; ++j) {
+      bf16x8 vn[NCB];
+      if (j + 1 < 4) {
+#pragma unroll
+        for (int cb = 0; cb < NCB; ++cb) vn[cb] = vfrag(cb, j + 1);
+      }
+      const bf16x8 pnext = (j + 1 < 4) ? pstep(j + 1) : pcur;
+#pragma unroll
+      for (int cb = 0; cb < NCB; ++cb) acc[cb] = mfma32(vr[cb], pcur, acc[cb]);
+      pcur = pnext;
+      if (j + 1 < 4) {
+#pragma unroll
+        for (int cb = 0; cb < NCB; ++cb) vr[cb] = vn[cb];
+      }
+    }
+    // per step: NCB (MFMA, LDS read, ~7 VALU) triples
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+#pragma unroll
+      for (int cb = 0; cb < NCB; ++cb) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 1);
+        __builtin_amdgcn_sched_group_barrier(0x002, 7, 1);
       }
     }
     l_run += psum;
-
-    // O^T += V^T P^T
-#pragma unroll
-    for (int cb = 0; cb < NCB; ++cb) {
-      const uint16_t* vp = &sm.vt[(cb * 32 + l32) * FwdSmem<D>::VS + 8 * half];
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int hs = 0; hs < 2; ++hs) {
-          const bf16x8 a = as_bf16x8(*reinterpret_cast<const u32x4*>(vp + kb * 32 + hs * 16));
-          acc[cb] = mfma32(a, pf[kb][hs], acc[cb]);
-        }
-    }
   }
 
   // epilogue: O = acc / l, LSE = m scale + ln l
