@@ -116,6 +116,29 @@ __device__ __forceinline__ void store_block4x8(const u32x4 (&r)[4], uint16_t* na
   }
 }
 
+// A chain of N dependent-accumulator MFMAs whose LDS operand fragment f is
+// read PF fragments ahead of its use; the schedule is pinned to (MFMA, LDS
+// read) pairs so the read latency hides behind the matrix pipe.
+template <int N, int PF, int SYNC, typename Load, typename Mac>
+__device__ __forceinline__ void mfma_chain(Load load, Mac mac) {
+  bf16x8 r[PF];
+#pragma unroll
+  for (int f = 0; f < PF; ++f) r[f] = load(f);
+#pragma unroll
+  for (int f = 0; f < N; ++f) {
+    const bf16x8 a = r[f % PF];
+    if (f + PF < N) r[f % PF] = load(f + PF);
+    mac(f, a);
+  }
+  __builtin_amdgcn_sched_group_barrier(0x100, PF, SYNC);
+#pragma unroll
+  for (int f = 0; f < N - PF; ++f) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, SYNC);
+    __builtin_amdgcn_sched_group_barrier(0x100, 1, SYNC);
+  }
+  __builtin_amdgcn_sched_group_barrier(0x008, PF, SYNC);
+}
+
 // ---------------------------------------------------------------- dK, dV
 constexpr int KB_Q = kBwdBQ;   // 32 query rows per step
 constexpr int KB_K = kBwdBK;   // 128 keys per workgroup
@@ -129,8 +152,8 @@ struct KvSmem {
   uint16_t qt[D * TS];
   uint16_t dout[KB_Q * NS];
   uint16_t dot[D * TS];
-  float lse2[KB_Q];
-  float delta[KB_Q];
+  alignas(16) float lse2[KB_Q];
+  alignas(16) float delta[KB_Q];
 };
 
 // 8 waves: waves 0-3 accumulate dV, waves 4-7 dK, for the same four 32-key
@@ -248,6 +271,16 @@ attn_bwd_dkdv_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
     __syncthreads();
     if (step + 1 < n_steps) fetch(step + 1);
 
+    // per-query LSE (and scaled D for the dK role) of this lane's 16 queries
+    // 16s + 8 half + t, read before the MFMAs so their latency is hidden
+    f32x4 lr[4], dr[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      lr[j] = *reinterpret_cast<const f32x4*>(&sm.lse2[16 * (j >> 1) + 8 * half + 4 * (j & 1)]);
+      dr[j] = role ? *reinterpret_cast<const f32x4*>(&sm.delta[16 * (j >> 1) + 8 * half + 4 * (j & 1)])
+                   : f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+
     // S = Q K^T (rows: queries 16s + 8 half + t; cols: this wave's keys).
     // Waves whose keys this query tile cannot see still run the step, fully
     // masked: every wave meets at the next barrier anyway.
@@ -256,9 +289,9 @@ attn_bwd_dkdv_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
     for (int i = 0; i < 16; ++i) sacc[i] = 0.f;
     {
       const uint16_t* qp = &sm.q[l32 * KvSmem<D>::NS + 8 * half];
-#pragma unroll
-      for (int s = 0; s < NKS; ++s)
-        sacc = mfma32(as_bf16x8(*reinterpret_cast<const u32x4*>(qp + 16 * s)), kf[s], sacc);
+      mfma_chain<NKS, 4, 0>(
+          [&](int f) { return as_bf16x8(*reinterpret_cast<const u32x4*>(qp + 16 * f)); },
+          [&](int f, const bf16x8& a) { sacc = mfma32(a, kf[f], sacc); });
     }
 
     // P; element i holds query qb + e, e = 16 (i / 8) + i % 8.  It is visible
@@ -269,16 +302,10 @@ attn_bwd_dkdv_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
       const int e_min = causal ? key - off - qb : INT32_MIN;
       const int e_cap = (key < lk) ? lq - qb : INT32_MIN;
 #pragma unroll
-      for (int s = 0; s < 2; ++s) {
-        const f32x4 l0 = *reinterpret_cast<const f32x4*>(&sm.lse2[16 * s + 8 * half]);
-        const f32x4 l1 = *reinterpret_cast<const f32x4*>(&sm.lse2[16 * s + 8 * half + 4]);
-#pragma unroll
-        for (int t = 0; t < 8; ++t) {
-          const int i = 8 * s + t;
-          const int e = 16 * s + t;
-          const float pv = __builtin_amdgcn_exp2f(fmaf(sacc[i], c, -(t < 4 ? l0[t] : l1[t - 4])));
-          p[i] = (e < e_cap && e >= e_min) ? pv : 0.f;
-        }
+      for (int i = 0; i < 16; ++i) {
+        const int e = 16 * (i >> 3) + (i & 7);
+        const float pv = __builtin_amdgcn_exp2f(fmaf(sacc[i], c, -lr[i >> 2][i & 3]));
+        p[i] = (e < e_cap && e >= e_min) ? pv : 0.f;
       }
     }
 
@@ -297,20 +324,17 @@ attn_bwd_dkdv_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
 #pragma unroll
       for (int i = 0; i < 16; ++i) pacc[i] = 0.f;
       const uint16_t* dp = &sm.dout[l32 * KvSmem<D>::NS + 8 * half];
-#pragma unroll
-      for (int s = 0; s < NKS; ++s)
-        pacc = mfma32(as_bf16x8(*reinterpret_cast<const u32x4*>(dp + 16 * s)), vf[s], pacc);
+      mfma_chain<NKS, 4, 1>(
+          [&](int f) { return as_bf16x8(*reinterpret_cast<const u32x4*>(dp + 16 * f)); },
+          [&](int f, const bf16x8& a) { pacc = mfma32(a, vf[f], pacc); });
 #pragma unroll
       for (int s = 0; s < 2; ++s) {
-        const f32x4 d0 = *reinterpret_cast<const f32x4*>(&sm.delta[16 * s + 8 * half]);
-        const f32x4 d1 = *reinterpret_cast<const f32x4*>(&sm.delta[16 * s + 8 * half + 4]);
         u32x4 u;
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           const int i = 8 * s + 2 * j;
-          const float da = (2 * j < 4) ? d0[2 * j] : d1[2 * j - 4];
-          const float db = (2 * j + 1 < 4) ? d0[2 * j + 1] : d1[2 * j + 1 - 4];
-          u[j] = pack_bf16x2(p[i] * fmaf(pacc[i], scale, -da), p[i + 1] * fmaf(pacc[i + 1], scale, -db));
+          u[j] = pack_bf16x2(p[i] * fmaf(pacc[i], scale, -dr[i >> 2][i & 3]),
+                             p[i + 1] * fmaf(pacc[i + 1], scale, -dr[(i + 1) >> 2][(i + 1) & 3]));
         }
         af[s] = as_bf16x8(u);
       }
@@ -319,13 +343,12 @@ attn_bwd_dkdv_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
     // dV += P^T dO or dK += dS^T Q  (B operands from the transposed tiles)
     {
       const uint16_t* bt = (role == 0 ? sm.dot : sm.qt) + l32 * KvSmem<D>::TS + 8 * half;
-#pragma unroll
-      for (int cb = 0; cb < NCB; ++cb)
-#pragma unroll
-        for (int s = 0; s < 2; ++s)
-          acc[cb] = mfma32(af[s],
-                           as_bf16x8(*reinterpret_cast<const u32x4*>(bt + cb * 32 * KvSmem<D>::TS + 16 * s)),
-                           acc[cb]);
+      mfma_chain<2 * NCB, 4, 2>(
+          [&](int f) {
+            return as_bf16x8(*reinterpret_cast<const u32x4*>(
+                bt + (f >> 1) * 32 * KvSmem<D>::TS + 16 * (f & 1)));
+          },
+          [&](int f, const bf16x8& bfr) { acc[f >> 1] = mfma32(af[f & 1], bfr, acc[f >> 1]); });
     }
   }
 
