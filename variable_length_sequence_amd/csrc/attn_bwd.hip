@@ -81,41 +81,6 @@ f32_to_bf16_kernel(const f32x4* __restrict__ src, u32x2* __restrict__ dst, int64
   }
 }
 
-// Loads a 4-row x 8-column bf16 block (rows past `n_valid` are zero).
-__device__ __forceinline__ void load_block4x8(u32x4 (&r)[4], const uint16_t* __restrict__ base,
-                                              int64_t tok_stride, int row0, int n_valid) {
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    if (row0 + j < n_valid)
-      r[j] = *reinterpret_cast<const u32x4*>(base + int64_t(row0 + j) * tok_stride);
-    else
-      r[j] = u32x4{0, 0, 0, 0};
-  }
-}
-
-// Writes the block row-major (stride rs) and transposed (stride ts) into LDS.
-// Row r of the row-major copy is kept at LDS row swap_bits23(r), so the
-// permuted A-operand rows a lane reads are consecutive LDS rows.
-__device__ __forceinline__ void store_block4x8(const u32x4 (&r)[4], uint16_t* nat, int rs,
-                                               uint16_t* tr, int ts, int row0, int col0) {
-  if (nat) {
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-      *reinterpret_cast<u32x4*>(nat + swap_bits23(row0 + j) * rs + col0) = r[j];
-  }
-#pragma unroll
-  for (int u = 0; u < 4; ++u) {
-    u32x2 even, odd;
-    even[0] = (r[0][u] & 0xffffu) | (r[1][u] << 16);
-    even[1] = (r[2][u] & 0xffffu) | (r[3][u] << 16);
-    odd[0] = (r[0][u] >> 16) | (r[1][u] & 0xffff0000u);
-    odd[1] = (r[2][u] >> 16) | (r[3][u] & 0xffff0000u);
-    const int c = col0 + 2 * u;
-    *reinterpret_cast<u32x2*>(tr + c * ts + row0) = even;
-    *reinterpret_cast<u32x2*>(tr + (c + 1) * ts + row0) = odd;
-  }
-}
-
 // A chain of N dependent-accumulator MFMAs whose LDS operand fragment f is
 // read PF fragments ahead of its use; the schedule is pinned to (MFMA, LDS
 // read) pairs so the read latency hides behind the matrix pipe.
@@ -146,12 +111,11 @@ constexpr int kKvThreads = 512;
 
 template <int D>
 struct KvSmem {
-  static constexpr int NS = D + 8;       // row-major tile stride
-  static constexpr int TS = KB_Q + 8;    // transposed tile stride
-  uint16_t q[KB_Q * NS];
-  uint16_t qt[D * TS];
-  uint16_t dout[KB_Q * NS];
-  uint16_t dot[D * TS];
+  // Q and dO tiles, row-major with swizzled chunks; query row r is kept at LDS
+  // row swap_bits23(r).  The transposed operands (dO for dV += P^T dO, Q for
+  // dK += dS^T Q) are read from the same tiles with the transpose read.
+  uint16_t q[KB_Q * D];
+  uint16_t dout[KB_Q * D];
   alignas(16) float lse2[KB_Q];
   alignas(16) float delta[KB_Q];
 };
@@ -173,8 +137,8 @@ attn_bwd_dkdv_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
                      float* __restrict__ dkv_acc, int64_t total_k) {
   constexpr int NKS = D / 16;
   constexpr int NCB = D / 32;
-  constexpr int CPR = D / 8;                        // 8-column groups per row
-  constexpr int NBLK = (KB_Q / 4) * CPR;            // 4x8 blocks per tile
+  constexpr int NCH = D / 8;                        // 16-byte chunks per row
+  constexpr int TCH = KB_Q * NCH;                   // chunks per tile
   __shared__ KvSmem<D> sm;
 
   const int b = blockIdx.x;
@@ -233,23 +197,23 @@ attn_bwd_dkdv_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
   const int wk_first = j0 + w * 32;
   const int n_steps = hpg * it.count;
 
-  // staging by the dV waves: threads [0, NBLK) stage Q, [128, 128 + NBLK) dO;
-  // row group fastest across lanes so the transposed LDS writes hit
-  // consecutive banks
-  const bool stage_q = tid < NBLK;
-  const bool stage_do = tid >= 128 && tid < 128 + NBLK;
-  const int sb = stage_q ? tid : tid - 128;
-  const int s_row = (sb % (KB_Q / 4)) * 4, s_col = (sb / (KB_Q / 4)) * 8;
-
-  u32x4 pre[4];
+  // staging: the 2 * TCH chunks of the Q and dO tiles over all threads, chunk
+  // index fastest (coalesced global reads, conflict-free LDS writes)
+  constexpr int SPT = 2 * TCH / kKvThreads;         // chunks per thread
+  u32x4 pre[SPT];
   float pre_lse = 0.f;
   auto fetch = [&](int step) {
     const int h = h_begin + step / it.count;
     const int i0 = (it.first + step % it.count) * KB_Q;
     const int64_t rowbase = int64_t(it.q_start) + i0;
-    if (stage_q || stage_do) {
-      const uint16_t* src = (stage_q ? q : dout) + rowbase * q_tok + int64_t(h) * D + s_col;
-      load_block4x8(pre, src + int64_t(s_row) * q_tok, q_tok, 0, lq - i0 - s_row);
+#pragma unroll
+    for (int u = 0; u < SPT; ++u) {
+      const int id = tid + u * kKvThreads;
+      const int t = id % TCH, row = t / NCH, ch = t % NCH;
+      const uint16_t* src = id < TCH ? q : dout;
+      pre[u] = (i0 + row < lq)
+                   ? *reinterpret_cast<const u32x4*>(src + (rowbase + row) * q_tok + int64_t(h) * D + ch * 8)
+                   : u32x4{0, 0, 0, 0};
     }
     if (tid < KB_Q) {
       const int i = i0 + tid;
@@ -264,8 +228,13 @@ attn_bwd_dkdv_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
   for (int step = 0; step < n_steps; ++step) {
     const int i0 = (it.first + step % it.count) * KB_Q;
     __syncthreads();
-    if (stage_q) store_block4x8(pre, sm.q, KvSmem<D>::NS, sm.qt, KvSmem<D>::TS, s_row, s_col);
-    if (stage_do) store_block4x8(pre, sm.dout, KvSmem<D>::NS, sm.dot, KvSmem<D>::TS, s_row, s_col);
+#pragma unroll
+    for (int u = 0; u < SPT; ++u) {
+      const int id = tid + u * kKvThreads;
+      const int t = id % TCH;
+      uint16_t* dst = id < TCH ? sm.q : sm.dout;
+      *reinterpret_cast<u32x4*>(dst + SwzTile<D>::chunk(swap_bits23(t / NCH), t % NCH)) = pre[u];
+    }
     if (tid < KB_Q) sm.lse2[tid] = (pre_lse == -INFINITY) ? INFINITY : pre_lse * kLog2e;
     else if (tid >= 64 && tid < 64 + KB_Q) sm.delta[tid - 64] = pre_lse * scale;
     __syncthreads();
@@ -288,9 +257,10 @@ attn_bwd_dkdv_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
 #pragma unroll
     for (int i = 0; i < 16; ++i) sacc[i] = 0.f;
     {
-      const uint16_t* qp = &sm.q[l32 * KvSmem<D>::NS + 8 * half];
       mfma_chain<NKS, 4, 0>(
-          [&](int f) { return as_bf16x8(*reinterpret_cast<const u32x4*>(qp + 16 * f)); },
+          [&](int f) {
+            return as_bf16x8(*reinterpret_cast<const u32x4*>(&sm.q[SwzTile<D>::chunk(l32, 2 * f + half)]));
+          },
           [&](int f, const bf16x8& a) { sacc = mfma32(a, kf[f], sacc); });
     }
 
@@ -323,9 +293,10 @@ attn_bwd_dkdv_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
       f32x16 pacc;
 #pragma unroll
       for (int i = 0; i < 16; ++i) pacc[i] = 0.f;
-      const uint16_t* dp = &sm.dout[l32 * KvSmem<D>::NS + 8 * half];
       mfma_chain<NKS, 4, 1>(
-          [&](int f) { return as_bf16x8(*reinterpret_cast<const u32x4*>(dp + 16 * f)); },
+          [&](int f) {
+            return as_bf16x8(*reinterpret_cast<const u32x4*>(&sm.dout[SwzTile<D>::chunk(l32, 2 * f + half)]));
+          },
           [&](int f, const bf16x8& a) { pacc = mfma32(a, vf[f], pacc); });
 #pragma unroll
       for (int s = 0; s < 2; ++s) {
@@ -340,14 +311,11 @@ attn_bwd_dkdv_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
       }
     }
 
-    // dV += P^T dO or dK += dS^T Q  (B operands from the transposed tiles)
+    // dV += P^T dO or dK += dS^T Q  (B operands read transposed)
     {
-      const uint16_t* bt = (role == 0 ? sm.dot : sm.qt) + l32 * KvSmem<D>::TS + 8 * half;
+      const uint16_t* bt = role == 0 ? sm.dout : sm.q;
       mfma_chain<2 * NCB, 4, 2>(
-          [&](int f) {
-            return as_bf16x8(*reinterpret_cast<const u32x4*>(
-                bt + (f >> 1) * 32 * KvSmem<D>::TS + 16 * (f & 1)));
-          },
+          [&](int f) { return tr_frag<D>(bt, lane, 16 * (f & 1), 32 * (f >> 1)); },
           [&](int f, const bf16x8& bfr) { acc[f >> 1] = mfma32(af[f & 1], bfr, acc[f >> 1]); });
     }
   }
@@ -378,11 +346,10 @@ constexpr int QB_K = kFwdBK;  // 64 keys per step
 
 template <int D>
 struct QSmem {
-  static constexpr int NS = D + 8;
-  static constexpr int TS = QB_K + 8;
-  uint16_t k[QB_K * NS];
-  uint16_t v[QB_K * NS];
-  uint16_t kt[D * TS];
+  // K and V tiles, row-major with swizzled chunks; key row r at LDS row
+  // swap_bits23(r).  K^T for dQ^T += K^T dS^T is read with the transpose read.
+  uint16_t k[QB_K * D];
+  uint16_t v[QB_K * D];
 };
 
 template <int D>
@@ -394,8 +361,8 @@ attn_bwd_dq_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ 
                    int causal, int64_t total_q, uint16_t* __restrict__ dq) {
   constexpr int NKS = D / 16;
   constexpr int NCB = D / 32;
-  constexpr int CPR = D / 8;
-  constexpr int NBLK = (QB_K / 4) * CPR;   // 4x8 blocks per K (or V) tile
+  constexpr int NCH = D / 8;                      // 16-byte chunks per row
+  constexpr int SPT = QB_K * NCH / kThreads;      // chunks per thread per tensor
   __shared__ QSmem<D> sm;
 
   const int b = blockIdx.x;
@@ -455,13 +422,20 @@ attn_bwd_dq_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ 
   const int wq_first = q0 + w * 32;
   const int wq_last = min(q0 + w * 32 + 31, lq - 1);
 
-  const bool stage = tid < NBLK;
-  const int s_row = (tid % (QB_K / 4)) * 4, s_col = (tid / (QB_K / 4)) * 8;
-  u32x4 pk[4], pv[4];
+  u32x4 pk[SPT], pv[SPT];
   auto fetch = [&](int kv0) {
-    if (stage) {
-      load_block4x8(pk, kbase + int64_t(kv0 + s_row) * kv_tok + s_col, kv_tok, 0, lk - kv0 - s_row);
-      load_block4x8(pv, vbase + int64_t(kv0 + s_row) * kv_tok + s_col, kv_tok, 0, lk - kv0 - s_row);
+#pragma unroll
+    for (int u = 0; u < SPT; ++u) {
+      const int id = tid + u * kThreads;
+      const int row = id / NCH, ch = id % NCH;
+      if (kv0 + row < lk) {
+        const int64_t o = int64_t(kv0 + row) * kv_tok + ch * 8;
+        pk[u] = *reinterpret_cast<const u32x4*>(kbase + o);
+        pv[u] = *reinterpret_cast<const u32x4*>(vbase + o);
+      } else {
+        pk[u] = u32x4{0, 0, 0, 0};
+        pv[u] = u32x4{0, 0, 0, 0};
+      }
     }
   };
 
@@ -470,11 +444,12 @@ attn_bwd_dq_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ 
   for (int kt = 0; kt < n_kv; ++kt) {
     const int kv0 = kt * QB_K;
     __syncthreads();
-    if (stage) {
-      store_block4x8(pk, sm.k, QSmem<D>::NS, sm.kt, QSmem<D>::TS, s_row, s_col);
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
-        *reinterpret_cast<u32x4*>(&sm.v[swap_bits23(s_row + j) * QSmem<D>::NS + s_col]) = pv[j];
+    for (int u = 0; u < SPT; ++u) {
+      const int id = tid + u * kThreads;
+      const int o = SwzTile<D>::chunk(swap_bits23(id / NCH), id % NCH);
+      *reinterpret_cast<u32x4*>(&sm.k[o]) = pk[u];
+      *reinterpret_cast<u32x4*>(&sm.v[o]) = pv[u];
     }
     __syncthreads();
     if (kt + 1 < n_kv) fetch(kv0 + QB_K);
@@ -483,28 +458,25 @@ attn_bwd_dq_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ 
     if (!live) continue;
     const bool need_mask = (kv0 + QB_K > lk) || (causal && kv0 + QB_K - 1 > wq_first + off);
 
-    f32x16 s[2], dp[2];
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        s[kb][i] = 0.f;
-        dp[kb][i] = 0.f;
-      }
-      const int prow = kb * 32 + l32;
-      const uint16_t* kp = &sm.k[prow * QSmem<D>::NS + 8 * half];
-      const uint16_t* vp = &sm.v[prow * QSmem<D>::NS + 8 * half];
-#pragma unroll
-      for (int st = 0; st < NKS; ++st) {
-        s[kb] = mfma32(as_bf16x8(*reinterpret_cast<const u32x4*>(kp + 16 * st)), qf[st], s[kb]);
-        dp[kb] = mfma32(as_bf16x8(*reinterpret_cast<const u32x4*>(vp + 16 * st)), df[st], dp[kb]);
-      }
-    }
-
+    // per 32-key half kb: S^T and dP^T (16 MFMAs), then dS^T packed to bf16;
+    // one half at a time keeps only one pair of accumulators live
     const int lim = causal ? min(lk - 1, qrow + off) : lk - 1;
     bf16x8 dsf[2][2];
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+    for (int kb = 0; kb < 2; ++kb) {
+      f32x16 sa, da;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        sa[i] = 0.f;
+        da[i] = 0.f;
+      }
+      const int prow = kb * 32 + l32;
+#pragma unroll
+      for (int st = 0; st < NKS; ++st) {
+        const int o = SwzTile<D>::chunk(prow, 2 * st + half);
+        sa = mfma32(as_bf16x8(*reinterpret_cast<const u32x4*>(&sm.k[o])), qf[st], sa);
+        da = mfma32(as_bf16x8(*reinterpret_cast<const u32x4*>(&sm.v[o])), df[st], da);
+      }
 #pragma unroll
       for (int hs = 0; hs < 2; ++hs) {
         u32x4 u;
@@ -514,29 +486,27 @@ attn_bwd_dq_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ 
 #pragma unroll
           for (int e = 0; e < 2; ++e) {
             const int i = 8 * hs + 2 * j + e;
-            float pv_ = __builtin_amdgcn_exp2f(fmaf(s[kb][i], c, -lse2));
+            float pv_ = __builtin_amdgcn_exp2f(fmaf(sa[i], c, -lse2));
             if (need_mask) {
               const int kk = kv0 + kb * 32 + 16 * hs + 8 * half + 2 * j + e;
               if (kk > lim) pv_ = 0.f;
             }
-            dsv[e] = pv_ * (dp[kb][i] - dl) * scale;
+            dsv[e] = pv_ * (da[i] - dl) * scale;
           }
           u[j] = pack_bf16x2(dsv[0], dsv[1]);
         }
         dsf[kb][hs] = as_bf16x8(u);
       }
+    }
 
     // dQ^T += K^T dS^T
 #pragma unroll
-    for (int cb = 0; cb < NCB; ++cb) {
-      const uint16_t* tp = &sm.kt[(cb * 32 + l32) * QSmem<D>::TS + 8 * half];
+    for (int cb = 0; cb < NCB; ++cb)
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int hs = 0; hs < 2; ++hs)
-          acc[cb] = mfma32(as_bf16x8(*reinterpret_cast<const u32x4*>(tp + kb * 32 + hs * 16)),
-                           dsf[kb][hs], acc[cb]);
-    }
+          acc[cb] = mfma32(tr_frag<D>(sm.k, lane, 32 * kb + 16 * hs, 32 * cb), dsf[kb][hs], acc[cb]);
   }
 
   if (qrow < lq) {

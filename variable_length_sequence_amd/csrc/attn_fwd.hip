@@ -17,9 +17,10 @@
 //   * the key rows of the MFMA A operand are permuted (bits 2 and 3 of the row
 //     swapped) so that the fp32 S^T values a lane holds are, after rounding
 //     P to bf16, exactly the B operand of O^T += V^T P^T with no shuffles;
-//   * K tiles are staged in LDS row-major, V tiles transposed (d-major), both
-//     padded by 16 B per row; the next tile's global loads are issued before
-//     the current tile's MFMAs;
+//   * K and V tiles are staged in LDS row-major with XOR-swizzled 16-byte
+//     chunks; the V^T operand is read with the gfx950 transpose read
+//     (ds_read_b64_tr_b16), so no transposed copy is stored; the next tile's
+//     global loads are issued before the current tile's MFMAs;
 //   * work items are ordered longest first and the workgroup id is remapped
 //     so all q heads of one item run on the same XCD (shared K/V in its L2).
 #include <hip/hip_runtime.h>
@@ -40,74 +41,52 @@ constexpr int kThreads = 256;
 
 template <int D>
 struct FwdSmem {
-  static constexpr int KS = D + 8;   // K tile row stride (elements)
-  static constexpr int VS = BK + 8;  // V^T tile row stride (elements)
-  uint16_t k[BK * KS];
-  uint16_t vt[D * VS];
+  // K and V tiles, row-major with swizzled chunks; key row r is kept at LDS
+  // row swap_bits23(r) (the row order the MFMA operands want)
+  uint16_t k[BK * D];
+  uint16_t v[BK * D];
 };
 
-// Global loads of one K/V tile into registers (zero rows past the document).
+// Global loads of one K/V tile into registers (zero rows past the document):
+// 16-byte chunks, chunk index fastest across threads.
 template <int D>
 struct TileRegs {
-  static constexpr int KCH = BK * D / 8 / kThreads;   // 16-byte K chunks per thread
-  static constexpr int VBLK = (BK / 4) * (D / 8);     // 4-key x 8-dim V blocks
-  u32x4 k[KCH];
-  u32x4 v[4];
+  static constexpr int NCH = D / 8;
+  static constexpr int CH = BK * NCH / kThreads;   // chunks per thread per tensor
+  u32x4 k[CH];
+  u32x4 v[CH];
 };
 
 template <int D>
 __device__ __forceinline__ void load_tile(TileRegs<D>& r, const uint16_t* __restrict__ kbase,
                                           const uint16_t* __restrict__ vbase, int64_t tok_stride,
                                           int kv0, int lk, int tid) {
-  constexpr int CPR = D / 8;  // chunks per row
+  constexpr int NCH = TileRegs<D>::NCH;
 #pragma unroll
-  for (int i = 0; i < TileRegs<D>::KCH; ++i) {
+  for (int i = 0; i < TileRegs<D>::CH; ++i) {
     const int id = tid + i * kThreads;
-    const int row = id / CPR, c8 = id % CPR;
+    const int row = id / NCH, ch = id % NCH;
     const int key = kv0 + row;
-    if (key < lk)
-      r.k[i] = *reinterpret_cast<const u32x4*>(kbase + int64_t(key) * tok_stride + c8 * 8);
-    else
+    if (key < lk) {
+      const int64_t o = int64_t(key) * tok_stride + ch * 8;
+      r.k[i] = *reinterpret_cast<const u32x4*>(kbase + o);
+      r.v[i] = *reinterpret_cast<const u32x4*>(vbase + o);
+    } else {
       r.k[i] = u32x4{0, 0, 0, 0};
-  }
-  if (tid < TileRegs<D>::VBLK) {
-    const int kg = tid % (BK / 4), c8 = tid / (BK / 4);
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int key = kv0 + kg * 4 + j;
-      if (key < lk)
-        r.v[j] = *reinterpret_cast<const u32x4*>(vbase + int64_t(key) * tok_stride + c8 * 8);
-      else
-        r.v[j] = u32x4{0, 0, 0, 0};
+      r.v[i] = u32x4{0, 0, 0, 0};
     }
   }
 }
 
 template <int D>
 __device__ __forceinline__ void store_tile(const TileRegs<D>& r, FwdSmem<D>& sm, int tid) {
-  constexpr int CPR = D / 8;
+  constexpr int NCH = TileRegs<D>::NCH;
 #pragma unroll
-  for (int i = 0; i < TileRegs<D>::KCH; ++i) {
+  for (int i = 0; i < TileRegs<D>::CH; ++i) {
     const int id = tid + i * kThreads;
-    const int row = id / CPR, c8 = id % CPR;
-    // key row r is kept at LDS row swap_bits23(r): the A-operand rows a lane
-    // needs are then consecutive LDS rows
-    *reinterpret_cast<u32x4*>(&sm.k[swap_bits23(row) * FwdSmem<D>::KS + c8 * 8]) = r.k[i];
-  }
-  if (tid < TileRegs<D>::VBLK) {
-    const int kg = tid % (BK / 4), c8 = tid / (BK / 4);
-    // transpose 4 keys x 8 dims into 8 dims x 4 keys
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      u32x2 even, odd;
-      even[0] = (r.v[0][u] & 0xffffu) | (r.v[1][u] << 16);
-      even[1] = (r.v[2][u] & 0xffffu) | (r.v[3][u] << 16);
-      odd[0] = (r.v[0][u] >> 16) | (r.v[1][u] & 0xffff0000u);
-      odd[1] = (r.v[2][u] >> 16) | (r.v[3][u] & 0xffff0000u);
-      const int c = c8 * 8 + 2 * u;
-      *reinterpret_cast<u32x2*>(&sm.vt[c * FwdSmem<D>::VS + kg * 4]) = even;
-      *reinterpret_cast<u32x2*>(&sm.vt[(c + 1) * FwdSmem<D>::VS + kg * 4]) = odd;
-    }
+    const int prow = swap_bits23(id / NCH), ch = id % NCH;
+    *reinterpret_cast<u32x4*>(&sm.k[SwzTile<D>::chunk(prow, ch)]) = r.k[i];
+    *reinterpret_cast<u32x4*>(&sm.v[SwzTile<D>::chunk(prow, ch)]) = r.v[i];
   }
 }
 
@@ -201,10 +180,9 @@ attn_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     {
       constexpr int NF = 2 * NKS;
       constexpr int kPf = 4;
-      const uint16_t* kp = &sm.k[l32 * FwdSmem<D>::KS + 8 * half];
       auto kfrag = [&](int f) {
         return as_bf16x8(*reinterpret_cast<const u32x4*>(
-            kp + (f / NKS) * 32 * FwdSmem<D>::KS + 16 * (f % NKS)));
+            &sm.k[SwzTile<D>::chunk((f / NKS) * 32 + l32, 2 * (f % NKS) + half)]));
       };
       bf16x8 kr[kPf];
 #pragma unroll
@@ -272,11 +250,9 @@ attn_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
       }
       return as_bf16x8(u);
     };
-    const uint16_t* vp = &sm.vt[l32 * FwdSmem<D>::VS + 8 * half];
-    auto vfrag = [&](int cb, int j) {
-      return as_bf16x8(*reinterpret_cast<const u32x4*>(
-          vp + cb * 32 * FwdSmem<D>::VS + (j >> 1) * 32 + (j & 1) * 16));
-    };
+    // V^T operand: column c of keys 32 kb + 16 hs + 8 half + t, read
+    // transposed from the row-major V tile
+    auto vfrag = [&](int cb, int j) { return tr_frag<D>(sm.v, lane, 16 * j, 32 * cb); };
     bf16x8 pcur = pstep(0);
     bf16x8 vr[NCB];
 #pragma unroll

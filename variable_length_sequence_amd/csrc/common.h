@@ -48,6 +48,52 @@ __device__ __forceinline__ int swap_bits23(int m) {
   return (m & ~12) | ((m & 4) << 1) | ((m & 8) >> 1);
 }
 
+// Row-major bf16 tile of D columns in LDS.  The 16-byte chunks of a row are
+// XOR-swizzled with the row index (its two 2-bit fields swapped) so that
+//  * 16 lanes reading one chunk of 16 consecutive rows (ds_read_b128),
+//  * 16 lanes writing the 16 chunks of one row, and
+//  * a transpose read (ds_read_b64_tr_b16) of 4 rows x 32 columns by 32 lanes
+// all touch distinct banks.
+template <int D>
+struct SwzTile {
+  static constexpr int NCH = D / 8;  // chunks per row
+  __device__ __forceinline__ static int swz(int row) {
+    return (((row & 3) << 2) | ((row >> 2) & 3)) & (NCH - 1);
+  }
+  // element offset of 16-byte chunk `ch` of `row`
+  __device__ __forceinline__ static int chunk(int row, int ch) {
+    return row * D + ((ch ^ swz(row)) << 3);
+  }
+  // element offset of column `col` (col % 4 == 0 for 8-byte accesses)
+  __device__ __forceinline__ static int elem(int row, int col) {
+    return row * D + (((col >> 3) ^ swz(row)) << 3) + (col & 7);
+  }
+};
+
+typedef __attribute__((ext_vector_type(4))) short s16x4;
+
+// ds_read_b64_tr_b16: within each group of 16 lanes, lane 4j + m passes the
+// address of 4 consecutive bf16 of row j, and lane i receives column i of the
+// four rows.  Two such reads give one lane 8 consecutive rows of its column:
+// the MFMA operand layout of a k-major (transposed) view of a row-major tile.
+__device__ __forceinline__ s16x4 ds_read_tr16(const uint16_t* lds_ptr) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) s16x4*)(lds_ptr));
+}
+
+// Operand fragment of lane (l = 16 g + 4 j + m) holding column c0 + 16 (g & 1)
+// + (l & 15) and rows r0 + 4 (g >> 1) + t, t = 0..3 then r0 + 8 + 4 (g >> 1) + t,
+// t = 0..3 (physical LDS rows), from a SwzTile<D>.
+template <int D>
+__device__ __forceinline__ bf16x8 tr_frag(const uint16_t* tile, int lane, int r0, int c0) {
+  const int g = lane >> 4, j = (lane >> 2) & 3, m = lane & 3;
+  const int row = r0 + 4 * (g >> 1) + j;
+  const int col = c0 + 16 * (g & 1) + 4 * m;
+  const s16x4 lo = ds_read_tr16(tile + SwzTile<D>::elem(row, col));
+  const s16x4 hi = ds_read_tr16(tile + SwzTile<D>::elem(row + 8, col));
+  return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+}
+
 // Exchange a value with the lane 32 positions away (the other half-wave).
 __device__ __forceinline__ float xor32(float x) {
   return __shfl_xor(x, 32, 64);
