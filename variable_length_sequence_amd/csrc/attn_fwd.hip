@@ -19,8 +19,9 @@
 //     P to bf16, exactly the B operand of O^T += V^T P^T with no shuffles;
 //   * K and V tiles are staged in LDS row-major with XOR-swizzled 16-byte
 //     chunks; the V^T operand is read with the gfx950 transpose read
-//     (ds_read_b64_tr_b16), so no transposed copy is stored; the next tile's
-//     global loads are issued before the current tile's MFMAs;
+//     (ds_read_b64_tr_b16), so no transposed copy is stored; tiles are
+//     double-buffered and filled by direct global->LDS loads issued one tile
+//     ahead (one barrier per tile, no staging registers);
 //   * work items are ordered longest first and the workgroup id is remapped
 //     so all q heads of one item run on the same XCD (shared K/V in its L2).
 #include <hip/hip_runtime.h>
@@ -41,52 +42,34 @@ constexpr int kThreads = 256;
 
 template <int D>
 struct FwdSmem {
-  // K and V tiles, row-major with swizzled chunks; key row r is kept at LDS
-  // row swap_bits23(r) (the row order the MFMA operands want)
-  uint16_t k[BK * D];
-  uint16_t v[BK * D];
+  // double-buffered K and V tiles, row-major with swizzled chunks; key row r
+  // is kept at LDS row swap_bits23(r) (the row order the MFMA operands want)
+  uint16_t k[2][BK * D];
+  uint16_t v[2][BK * D];
 };
 
-// Global loads of one K/V tile into registers (zero rows past the document):
-// 16-byte chunks, chunk index fastest across threads.
+// Issues the direct global->LDS loads of one K/V tile.  Each wave instruction
+// fills 1 KB of LDS (64 lanes x 16 bytes = 1024 / (2 D) rows); the lane that
+// lands on LDS row p, chunk pc fetches key row swap_bits23(p), chunk
+// pc ^ swz(p).  Rows past the document are clamped to its last row: those
+// keys are masked out, so their (finite) values never reach the result.
 template <int D>
-struct TileRegs {
-  static constexpr int NCH = D / 8;
-  static constexpr int CH = BK * NCH / kThreads;   // chunks per thread per tensor
-  u32x4 k[CH];
-  u32x4 v[CH];
-};
-
-template <int D>
-__device__ __forceinline__ void load_tile(TileRegs<D>& r, const uint16_t* __restrict__ kbase,
-                                          const uint16_t* __restrict__ vbase, int64_t tok_stride,
-                                          int kv0, int lk, int tid) {
-  constexpr int NCH = TileRegs<D>::NCH;
+__device__ __forceinline__ void issue_tile(uint16_t* lk_dst, uint16_t* lv_dst,
+                                           const uint16_t* __restrict__ kbase,
+                                           const uint16_t* __restrict__ vbase, int64_t tok_stride,
+                                           int kv0, int lk, int wave, int lane) {
+  constexpr int NCH = D / 8;
+  constexpr int ROWS_PER_LOAD = 64 / NCH;
+  constexpr int LOADS = BK / ROWS_PER_LOAD / (kThreads / 64);   // per wave per tensor
 #pragma unroll
-  for (int i = 0; i < TileRegs<D>::CH; ++i) {
-    const int id = tid + i * kThreads;
-    const int row = id / NCH, ch = id % NCH;
-    const int key = kv0 + row;
-    if (key < lk) {
-      const int64_t o = int64_t(key) * tok_stride + ch * 8;
-      r.k[i] = *reinterpret_cast<const u32x4*>(kbase + o);
-      r.v[i] = *reinterpret_cast<const u32x4*>(vbase + o);
-    } else {
-      r.k[i] = u32x4{0, 0, 0, 0};
-      r.v[i] = u32x4{0, 0, 0, 0};
-    }
-  }
-}
-
-template <int D>
-__device__ __forceinline__ void store_tile(const TileRegs<D>& r, FwdSmem<D>& sm, int tid) {
-  constexpr int NCH = TileRegs<D>::NCH;
-#pragma unroll
-  for (int i = 0; i < TileRegs<D>::CH; ++i) {
-    const int id = tid + i * kThreads;
-    const int prow = swap_bits23(id / NCH), ch = id % NCH;
-    *reinterpret_cast<u32x4*>(&sm.k[SwzTile<D>::chunk(prow, ch)]) = r.k[i];
-    *reinterpret_cast<u32x4*>(&sm.v[SwzTile<D>::chunk(prow, ch)]) = r.v[i];
+  for (int u = 0; u < LOADS; ++u) {
+    const int blk = u * (kThreads / 64) + wave;
+    const int p = blk * ROWS_PER_LOAD + lane / NCH;
+    const int pc = lane % NCH;
+    const int key = min(kv0 + swap_bits23(p), lk - 1);
+    const int64_t o = int64_t(key) * tok_stride + ((pc ^ SwzTile<D>::swz(p)) << 3);
+    load_lds16(kbase + o, lk_dst + blk * 512);
+    load_lds16(vbase + o, lv_dst + blk * 512);
   }
 }
 
@@ -152,16 +135,20 @@ attn_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
   const int wq_first = q0 + w * 32;
   const int wq_last = min(q0 + w * 32 + 31, lq - 1);
 
-  TileRegs<D> regs;
   const int n_kv = it.count;
-  if (n_kv > 0) load_tile<D>(regs, kbase, vbase, kv_tok, 0, lk, tid);
+  if (n_kv > 0) issue_tile<D>(sm.k[0], sm.v[0], kbase, vbase, kv_tok, 0, lk, w, lane);
 
   for (int kt = 0; kt < n_kv; ++kt) {
     const int kv0 = kt * BK;
-    __syncthreads();               // previous tile fully consumed
-    store_tile<D>(regs, sm, tid);
+    const int buf = kt & 1;
+    // tile kt has landed in every wave's part of buffer `buf`, and every wave
+    // is done with the other buffer (read during tile kt - 1)
+    __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-    if (kt + 1 < n_kv) load_tile<D>(regs, kbase, vbase, kv_tok, kv0 + BK, lk, tid);
+    if (kt + 1 < n_kv)
+      issue_tile<D>(sm.k[buf ^ 1], sm.v[buf ^ 1], kbase, vbase, kv_tok, kv0 + BK, lk, w, lane);
+    const uint16_t* ks = sm.k[buf];
+    const uint16_t* vs = sm.v[buf];
 
     // wave-uniform: skip tiles no query of this wave can see
     const bool wave_live = (wq_first < lq) && (!causal || kv0 <= wq_last + off);
@@ -182,7 +169,7 @@ attn_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
       constexpr int kPf = 4;
       auto kfrag = [&](int f) {
         return as_bf16x8(*reinterpret_cast<const u32x4*>(
-            &sm.k[SwzTile<D>::chunk((f / NKS) * 32 + l32, 2 * (f % NKS) + half)]));
+            &ks[SwzTile<D>::chunk((f / NKS) * 32 + l32, 2 * (f % NKS) + half)]));
       };
       bf16x8 kr[kPf];
 #pragma unroll
@@ -252,7 +239,7 @@ attn_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     };
     // V^T operand: column c of keys 32 kb + 16 hs + 8 half + t, read
     // transposed from the row-major V tile
-    auto vfrag = [&](int cb, int j) { return tr_frag<D>(sm.v, lane, 16 * j, 32 * cb); };
+    auto vfrag = [&](int cb, int j) { return tr_frag<D>(vs, lane, 16 * j, 32 * cb); };
     bf16x8 pcur = pstep(0);
     bf16x8 vr[NCB];
 #pragma unroll

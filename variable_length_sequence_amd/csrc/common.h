@@ -94,6 +94,12 @@ __device__ __forceinline__ bf16x8 tr_frag(const uint16_t* tile, int lane, int r0
   return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
 }
 
+// Direct global -> LDS copy of 16 bytes per lane: lane i's bytes land at
+// lds_base + 16 i (lds_base must be the same in every lane of the wave).
+__device__ __forceinline__ void load_lds16(const void* gsrc, uint16_t* lds_base) {
+  __builtin_amdgcn_global_load_lds(gsrc, (__attribute__((address_space(3))) void*)(lds_base), 16, 0, 0);
+}
+
 // Exchange a value with the lane 32 positions away (the other half-wave).
 __device__ __forceinline__ float xor32(float x) {
   return __shfl_xor(x, 32, 64);
