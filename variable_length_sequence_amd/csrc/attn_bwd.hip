@@ -111,14 +111,40 @@ constexpr int kKvThreads = 512;
 
 template <int D>
 struct KvSmem {
-  // Q and dO tiles, row-major with swizzled chunks; query row r is kept at LDS
-  // row swap_bits23(r).  The transposed operands (dO for dV += P^T dO, Q for
-  // dK += dS^T Q) are read from the same tiles with the transpose read.
-  uint16_t q[KB_Q * D];
-  uint16_t dout[KB_Q * D];
-  alignas(16) float lse2[KB_Q];
-  alignas(16) float delta[KB_Q];
+  // double-buffered Q and dO tiles, row-major with swizzled chunks; query row
+  // r is kept at LDS row swap_bits23(r).  The transposed operands (dO for
+  // dV += P^T dO, Q for dK += dS^T Q) are read from the same tiles with the
+  // transpose read.
+  uint16_t q[2][KB_Q * D];
+  uint16_t dout[2][KB_Q * D];
+  alignas(16) float lse2[2][KB_Q];
+  alignas(16) float delta[2][KB_Q];
 };
+
+// Direct global->LDS loads of a tile of `ROWS` rows of two [T, H, D] tensors
+// (same rows of both), spread over the NW waves of a workgroup.  The lane
+// that lands on LDS row p, chunk pc fetches source row swap_bits23(p), chunk
+// pc ^ swz(p); rows at or past `n_valid` are clamped to the last valid row
+// (those rows are masked out wherever they are used).
+template <int D, int ROWS, int NW>
+__device__ __forceinline__ void issue_pair(uint16_t* dst_a, uint16_t* dst_b,
+                                           const uint16_t* __restrict__ src_a,
+                                           const uint16_t* __restrict__ src_b,
+                                           int64_t tok_stride, int row0, int n_valid, int wave,
+                                           int lane) {
+  constexpr int NCH = D / 8;
+  constexpr int RPL = 64 / NCH;                // rows per wave load (1 KB)
+  constexpr int BLKS = ROWS / RPL;             // 1 KB blocks per tensor
+#pragma unroll
+  for (int blk = wave; blk < BLKS; blk += NW) {
+    const int p = blk * RPL + lane / NCH;
+    const int pc = lane % NCH;
+    const int row = min(row0 + swap_bits23(p), n_valid - 1);
+    const int64_t o = int64_t(row) * tok_stride + ((pc ^ SwzTile<D>::swz(p)) << 3);
+    load_lds16(src_a + o, dst_a + blk * 512);
+    load_lds16(src_b + o, dst_b + blk * 512);
+  }
+}
 
 // 8 waves: waves 0-3 accumulate dV, waves 4-7 dK, for the same four 32-key
 // blocks (wave w and w + 4 share block w & 3 and, being w apart by 4, the same
@@ -137,8 +163,6 @@ attn_bwd_dkdv_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
                      float* __restrict__ dkv_acc, int64_t total_k) {
   constexpr int NKS = D / 16;
   constexpr int NCB = D / 32;
-  constexpr int NCH = D / 8;                        // 16-byte chunks per row
-  constexpr int TCH = KB_Q * NCH;                   // chunks per tile
   __shared__ KvSmem<D> sm;
 
   const int b = blockIdx.x;
@@ -197,56 +221,58 @@ attn_bwd_dkdv_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
   const int wk_first = j0 + w * 32;
   const int n_steps = hpg * it.count;
 
-  // staging: the 2 * TCH chunks of the Q and dO tiles over all threads, chunk
-  // index fastest (coalesced global reads, conflict-free LDS writes)
-  constexpr int SPT = 2 * TCH / kKvThreads;         // chunks per thread
-  u32x4 pre[SPT];
-  float pre_lse = 0.f;
-  auto fetch = [&](int step) {
+  // Q/dO tiles arrive by direct global->LDS loads one step ahead; the per-row
+  // LSE and D values go through registers (threads 0..31 and 64..95)
+  auto issue = [&](int step, int buf) {
     const int h = h_begin + step / it.count;
     const int i0 = (it.first + step % it.count) * KB_Q;
-    const int64_t rowbase = int64_t(it.q_start) + i0;
-#pragma unroll
-    for (int u = 0; u < SPT; ++u) {
-      const int id = tid + u * kKvThreads;
-      const int t = id % TCH, row = t / NCH, ch = t % NCH;
-      const uint16_t* src = id < TCH ? q : dout;
-      pre[u] = (i0 + row < lq)
-                   ? *reinterpret_cast<const u32x4*>(src + (rowbase + row) * q_tok + int64_t(h) * D + ch * 8)
-                   : u32x4{0, 0, 0, 0};
-    }
+    const int64_t hoff = int64_t(it.q_start) * q_tok + int64_t(h) * D;
+    issue_pair<D, KB_Q, 8>(sm.q[buf], sm.dout[buf], q + hoff, dout + hoff, q_tok, i0, lq, wave,
+                           lane);
+  };
+  auto fetch_rows = [&](int step) {
+    const int h = h_begin + step / it.count;
+    const int i0 = (it.first + step % it.count) * KB_Q;
+    float x = 0.f;
     if (tid < KB_Q) {
       const int i = i0 + tid;
-      pre_lse = (i < lq) ? lse[int64_t(h) * total_q + it.q_start + i] : INFINITY;
+      x = (i < lq) ? lse[int64_t(h) * total_q + it.q_start + i] : INFINITY;
+      x = (x == -INFINITY) ? INFINITY : x * kLog2e;
     } else if (tid >= 64 && tid < 64 + KB_Q) {
       const int i = i0 + tid - 64;
-      pre_lse = (i < lq) ? delta[int64_t(h) * total_q + it.q_start + i] : 0.f;
+      x = (i < lq) ? delta[int64_t(h) * total_q + it.q_start + i] * scale : 0.f;
     }
+    return x;
+  };
+  auto store_rows = [&](float x, int buf) {
+    if (tid < KB_Q) sm.lse2[buf][tid] = x;
+    else if (tid >= 64 && tid < 64 + KB_Q) sm.delta[buf][tid - 64] = x;
   };
 
-  if (n_steps > 0) fetch(0);
+  if (n_steps > 0) {
+    issue(0, 0);
+    store_rows(fetch_rows(0), 0);
+  }
   for (int step = 0; step < n_steps; ++step) {
     const int i0 = (it.first + step % it.count) * KB_Q;
+    const int buf = step & 1;
+    __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-#pragma unroll
-    for (int u = 0; u < SPT; ++u) {
-      const int id = tid + u * kKvThreads;
-      const int t = id % TCH;
-      uint16_t* dst = id < TCH ? sm.q : sm.dout;
-      *reinterpret_cast<u32x4*>(dst + SwzTile<D>::chunk(swap_bits23(t / NCH), t % NCH)) = pre[u];
+    float nxt = 0.f;
+    if (step + 1 < n_steps) {
+      issue(step + 1, buf ^ 1);
+      nxt = fetch_rows(step + 1);
     }
-    if (tid < KB_Q) sm.lse2[tid] = (pre_lse == -INFINITY) ? INFINITY : pre_lse * kLog2e;
-    else if (tid >= 64 && tid < 64 + KB_Q) sm.delta[tid - 64] = pre_lse * scale;
-    __syncthreads();
-    if (step + 1 < n_steps) fetch(step + 1);
+    const uint16_t* qs = sm.q[buf];
+    const uint16_t* ds = sm.dout[buf];
 
     // per-query LSE (and scaled D for the dK role) of this lane's 16 queries
     // 16s + 8 half + t, read before the MFMAs so their latency is hidden
     f32x4 lr[4], dr[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      lr[j] = *reinterpret_cast<const f32x4*>(&sm.lse2[16 * (j >> 1) + 8 * half + 4 * (j & 1)]);
-      dr[j] = role ? *reinterpret_cast<const f32x4*>(&sm.delta[16 * (j >> 1) + 8 * half + 4 * (j & 1)])
+      lr[j] = *reinterpret_cast<const f32x4*>(&sm.lse2[buf][16 * (j >> 1) + 8 * half + 4 * (j & 1)]);
+      dr[j] = role ? *reinterpret_cast<const f32x4*>(&sm.delta[buf][16 * (j >> 1) + 8 * half + 4 * (j & 1)])
                    : f32x4{0.f, 0.f, 0.f, 0.f};
     }
 
@@ -259,7 +285,7 @@ attn_bwd_dkdv_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
     {
       mfma_chain<NKS, 4, 0>(
           [&](int f) {
-            return as_bf16x8(*reinterpret_cast<const u32x4*>(&sm.q[SwzTile<D>::chunk(l32, 2 * f + half)]));
+            return as_bf16x8(*reinterpret_cast<const u32x4*>(&qs[SwzTile<D>::chunk(l32, 2 * f + half)]));
           },
           [&](int f, const bf16x8& a) { sacc = mfma32(a, kf[f], sacc); });
     }
@@ -295,7 +321,7 @@ attn_bwd_dkdv_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
       for (int i = 0; i < 16; ++i) pacc[i] = 0.f;
       mfma_chain<NKS, 4, 1>(
           [&](int f) {
-            return as_bf16x8(*reinterpret_cast<const u32x4*>(&sm.dout[SwzTile<D>::chunk(l32, 2 * f + half)]));
+            return as_bf16x8(*reinterpret_cast<const u32x4*>(&ds[SwzTile<D>::chunk(l32, 2 * f + half)]));
           },
           [&](int f, const bf16x8& a) { pacc = mfma32(a, vf[f], pacc); });
 #pragma unroll
@@ -313,11 +339,12 @@ attn_bwd_dkdv_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
 
     // dV += P^T dO or dK += dS^T Q  (B operands read transposed)
     {
-      const uint16_t* bt = role == 0 ? sm.dout : sm.q;
+      const uint16_t* bt = role == 0 ? ds : qs;
       mfma_chain<2 * NCB, 4, 2>(
           [&](int f) { return tr_frag<D>(bt, lane, 16 * (f & 1), 32 * (f >> 1)); },
           [&](int f, const bf16x8& bfr) { acc[f >> 1] = mfma32(af[f & 1], bfr, acc[f >> 1]); });
     }
+    if (step + 1 < n_steps) store_rows(nxt, buf ^ 1);
   }
 
   // epilogue: lane holds column c = 32 cb + l32 of keys 32 w + 8 (v/4) + 4 half + v%4
@@ -346,10 +373,11 @@ constexpr int QB_K = kFwdBK;  // 64 keys per step
 
 template <int D>
 struct QSmem {
-  // K and V tiles, row-major with swizzled chunks; key row r at LDS row
-  // swap_bits23(r).  K^T for dQ^T += K^T dS^T is read with the transpose read.
-  uint16_t k[QB_K * D];
-  uint16_t v[QB_K * D];
+  // double-buffered K and V tiles, row-major with swizzled chunks; key row r
+  // at LDS row swap_bits23(r).  K^T for dQ^T += K^T dS^T is read with the
+  // transpose read.
+  uint16_t k[2][QB_K * D];
+  uint16_t v[2][QB_K * D];
 };
 
 template <int D>
@@ -361,8 +389,6 @@ attn_bwd_dq_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ 
                    int causal, int64_t total_q, uint16_t* __restrict__ dq) {
   constexpr int NKS = D / 16;
   constexpr int NCB = D / 32;
-  constexpr int NCH = D / 8;                      // 16-byte chunks per row
-  constexpr int SPT = QB_K * NCH / kThreads;      // chunks per thread per tensor
   __shared__ QSmem<D> sm;
 
   const int b = blockIdx.x;
@@ -422,37 +448,18 @@ attn_bwd_dq_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ 
   const int wq_first = q0 + w * 32;
   const int wq_last = min(q0 + w * 32 + 31, lq - 1);
 
-  u32x4 pk[SPT], pv[SPT];
-  auto fetch = [&](int kv0) {
-#pragma unroll
-    for (int u = 0; u < SPT; ++u) {
-      const int id = tid + u * kThreads;
-      const int row = id / NCH, ch = id % NCH;
-      if (kv0 + row < lk) {
-        const int64_t o = int64_t(kv0 + row) * kv_tok + ch * 8;
-        pk[u] = *reinterpret_cast<const u32x4*>(kbase + o);
-        pv[u] = *reinterpret_cast<const u32x4*>(vbase + o);
-      } else {
-        pk[u] = u32x4{0, 0, 0, 0};
-        pv[u] = u32x4{0, 0, 0, 0};
-      }
-    }
-  };
-
   const int n_kv = it.count;
-  if (n_kv > 0) fetch(0);
+  if (n_kv > 0) issue_pair<D, QB_K, 4>(sm.k[0], sm.v[0], kbase, vbase, kv_tok, 0, lk, w, lane);
   for (int kt = 0; kt < n_kv; ++kt) {
     const int kv0 = kt * QB_K;
+    const int buf = kt & 1;
+    __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-#pragma unroll
-    for (int u = 0; u < SPT; ++u) {
-      const int id = tid + u * kThreads;
-      const int o = SwzTile<D>::chunk(swap_bits23(id / NCH), id % NCH);
-      *reinterpret_cast<u32x4*>(&sm.k[o]) = pk[u];
-      *reinterpret_cast<u32x4*>(&sm.v[o]) = pv[u];
-    }
-    __syncthreads();
-    if (kt + 1 < n_kv) fetch(kv0 + QB_K);
+    if (kt + 1 < n_kv)
+      issue_pair<D, QB_K, 4>(sm.k[buf ^ 1], sm.v[buf ^ 1], kbase, vbase, kv_tok, kv0 + QB_K, lk, w,
+                             lane);
+    const uint16_t* ks = sm.k[buf];
+    const uint16_t* vs = sm.v[buf];
 
     const bool live = (wq_first < lq) && (!causal || kv0 <= wq_last + off);
     if (!live) continue;
@@ -474,8 +481,8 @@ attn_bwd_dq_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ 
 #pragma unroll
       for (int st = 0; st < NKS; ++st) {
         const int o = SwzTile<D>::chunk(prow, 2 * st + half);
-        sa = mfma32(as_bf16x8(*reinterpret_cast<const u32x4*>(&sm.k[o])), qf[st], sa);
-        da = mfma32(as_bf16x8(*reinterpret_cast<const u32x4*>(&sm.v[o])), df[st], da);
+        sa = mfma32(as_bf16x8(*reinterpret_cast<const u32x4*>(&ks[o])), qf[st], sa);
+        da = mfma32(as_bf16x8(*reinterpret_cast<const u32x4*>(&vs[o])), df[st], da);
       }
 #pragma unroll
       for (int hs = 0; hs < 2; ++hs) {
@@ -506,7 +513,7 @@ attn_bwd_dq_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ 
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int hs = 0; hs < 2; ++hs)
-          acc[cb] = mfma32(tr_frag<D>(sm.k, lane, 32 * kb + 16 * hs, 32 * cb), dsf[kb][hs], acc[cb]);
+          acc[cb] = mfma32(tr_frag<D>(ks, lane, 32 * kb + 16 * hs, 32 * cb), dsf[kb][hs], acc[cb]);
   }
 
   if (qrow < lq) {
