@@ -41,6 +41,9 @@ def _args():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-extra", action="store_true", help="skip the other workloads")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-mib", type=int, default=0,
+                    help="first copy this many MiB device-to-device (a plain copy of known "
+                         "size, to calibrate hardware byte counters against)")
     return ap.parse_args()
 
 
@@ -223,6 +226,13 @@ def main():
         sys.exit(1)
     vl.lib()
     dev = torch.device("cuda:0")
+    if a.copy_mib > 0:
+        n = a.copy_mib << 20
+        src = torch.ones(n // 4, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     w = workloads.longtail_16k()
     print(f"[bench] {w.name}: {len(w.lengths)} docs, {w.total} tokens, "
           f"{a.warmup} warmup + {a.steps} timed steps", file=sys.stderr, flush=True)
