@@ -177,7 +177,7 @@ attn_bwd_dkdv_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
   const int role = wave >> 2;                  // 0: dV, 1: dK
   const int w = wave & 3;                      // key block
   const int half = lane >> 5;
@@ -272,22 +272,19 @@ attn_bwd_dkdv_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       lr[j] = *reinterpret_cast<const f32x4*>(&sm.lse2[buf][16 * (j >> 1) + 8 * half + 4 * (j & 1)]);
-      dr[j] = role ? *reinterpret_cast<const f32x4*>(&sm.delta[buf][16 * (j >> 1) + 8 * half + 4 * (j & 1)])
-                   : f32x4{0.f, 0.f, 0.f, 0.f};
+      dr[j] = *reinterpret_cast<const f32x4*>(&sm.delta[buf][16 * (j >> 1) + 8 * half + 4 * (j & 1)]);
     }
 
     // S = Q K^T (rows: queries 16s + 8 half + t; cols: this wave's keys).
     // Waves whose keys this query tile cannot see still run the step, fully
     // masked: every wave meets at the next barrier anyway.
     f32x16 sacc;
-#pragma unroll
-    for (int i = 0; i < 16; ++i) sacc[i] = 0.f;
     {
       mfma_chain<NKS, 4, 0>(
           [&](int f) {
             return as_bf16x8(*reinterpret_cast<const u32x4*>(&qs[SwzTile<D>::chunk(l32, 2 * f + half)]));
           },
-          [&](int f, const bf16x8& a) { sacc = mfma32(a, kf[f], sacc); });
+          [&](int f, const bf16x8& a) { sacc = mfma32(a, kf[f], f == 0 ? f32x16{} : sacc); });
     }
 
     // P; element i holds query qb + e, e = 16 (i / 8) + i % 8.  It is visible
@@ -317,13 +314,11 @@ attn_bwd_dkdv_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
       }
     } else {
       f32x16 pacc;
-#pragma unroll
-      for (int i = 0; i < 16; ++i) pacc[i] = 0.f;
       mfma_chain<NKS, 4, 1>(
           [&](int f) {
             return as_bf16x8(*reinterpret_cast<const u32x4*>(&ds[SwzTile<D>::chunk(l32, 2 * f + half)]));
           },
-          [&](int f, const bf16x8& a) { pacc = mfma32(a, vf[f], pacc); });
+          [&](int f, const bf16x8& a) { pacc = mfma32(a, vf[f], f == 0 ? f32x16{} : pacc); });
 #pragma unroll
       for (int s = 0; s < 2; ++s) {
         u32x4 u;
@@ -402,7 +397,7 @@ attn_bwd_dq_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ 
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int w = tid >> 6;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
   const int half = lane >> 5;
   const int l32 = lane & 31;
 

@@ -6,8 +6,8 @@ path can take their inputs from here without sharing any of the method.
 
 Length mixes follow the long-tailed corpora the pages describe: most samples
 are short and a few are very long (NSP page, Section 3.1 and Figure 2a: the
-bulk of samples lie below 8K tokens and a tiny fraction exceeds 128K).  The pages' own datasets are not available; these generators stand in
-for them.
+bulk of samples lie below 8K tokens and a tiny fraction exceeds 128K).  The
+pages' own datasets are not available; these generators stand in for them.
 
 Recipe (stated once, used everywhere):
   * lengths:  ``rng = numpy.random.default_rng(seed)``, one draw per document,
