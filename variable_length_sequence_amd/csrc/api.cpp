@@ -9,7 +9,7 @@
 #include <string>
 #include <vector>
 
-#include "../../include/varlen.h"
+#include "varlen.h"
 #include "launch.h"
 #include "scheduler.h"
 

@@ -205,7 +205,7 @@ attn_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[kb][i]);
-    mx = fmaxf(mx, xor32(mx));
+    mx = halves_max(mx);
     // m_run is the reference max of the exponent.  It is moved (and O and l
     // rescaled) only when the running max exceeds it by more than 2^8 in
     // probability, so p <= 256 and most tiles skip the rescale entirely.
@@ -274,7 +274,7 @@ attn_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
   }
 
   // epilogue: O = acc / l, LSE = m scale + ln l
-  const float l_tot = l_run + xor32(l_run);
+  const float l_tot = halves_sum(l_run);
   const float inv = (l_tot > 0.f) ? 1.f / l_tot : 0.f;
   if (qrow < lq) {
     const int64_t orow = (int64_t(it.q_start) + qrow) * q_tok + int64_t(h) * D;

@@ -105,6 +105,18 @@ __device__ __forceinline__ float xor32(float x) {
   return __shfl_xor(x, 32, 64);
 }
 
+// max / sum of x over lanes l and l ^ 32, on the VALU (v_permlane32_swap):
+// the swap leaves x of lane l % 32 in one result and x of lane 32 + l % 32 in
+// the other, in every lane.
+__device__ __forceinline__ float halves_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float halves_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 // Workgroup id remapped so that consecutive logical ids land on the same XCD
 // (workgroups are dispatched round-robin over the 8 XCDs of an MI355X).
 __device__ __forceinline__ uint32_t xcd_remap(uint32_t bid, uint32_t nblocks) {

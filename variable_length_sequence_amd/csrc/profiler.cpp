@@ -8,7 +8,7 @@
 #include <string>
 #include <vector>
 
-#include "../../include/varlen.h"
+#include "varlen.h"
 
 namespace vl {
 
