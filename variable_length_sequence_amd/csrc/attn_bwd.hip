@@ -111,47 +111,30 @@ constexpr int kKvThreads = 512;
 
 template <int D>
 struct KvSmem {
-  // double-buffered Q and dO tiles, row-major with swizzled chunks; query row
-  // r is kept at LDS row swap_bits23(r).  The transposed operands (dO for
+  // double-buffered Q and dO tiles, row-major with swizzled chunks; query
+  // row r is kept at LDS row swap_bits23(r).  The transposed operands (dO for
   // dV += P^T dO, Q for dK += dS^T Q) are read from the same tiles with the
   // transpose read.
   uint16_t q[2][KB_Q * D];
   uint16_t dout[2][KB_Q * D];
-  alignas(16) float lse2[2][KB_Q];
-  alignas(16) float delta[2][KB_Q];
+  alignas(16) float lse2[2][KB_Q];   // LSE log2(e)
+  alignas(16) float delta[2][KB_Q];  // D scale
+  // P of the current step, bf16, in the A-operand layout of each dV wave
+  // (lane-major, 32 bytes per lane)
+  alignas(16) uint16_t p[4][64 * 16];
 };
 
-// Direct global->LDS loads of a tile of `ROWS` rows of two [T, H, D] tensors
-// (same rows of both), spread over the NW waves of a workgroup.  The lane
-// that lands on LDS row p, chunk pc fetches source row swap_bits23(p), chunk
-// pc ^ swz(p); rows at or past `n_valid` are clamped to the last valid row
-// (those rows are masked out wherever they are used).
-template <int D, int ROWS, int NW>
-__device__ __forceinline__ void issue_pair(uint16_t* dst_a, uint16_t* dst_b,
-                                           const uint16_t* __restrict__ src_a,
-                                           const uint16_t* __restrict__ src_b,
-                                           int64_t tok_stride, int row0, int n_valid, int wave,
-                                           int lane) {
-  constexpr int NCH = D / 8;
-  constexpr int RPL = 64 / NCH;                // rows per wave load (1 KB)
-  constexpr int BLKS = ROWS / RPL;             // 1 KB blocks per tensor
-#pragma unroll
-  for (int blk = wave; blk < BLKS; blk += NW) {
-    const int p = blk * RPL + lane / NCH;
-    const int pc = lane % NCH;
-    const int row = min(row0 + swap_bits23(p), n_valid - 1);
-    const int64_t o = int64_t(row) * tok_stride + ((pc ^ SwzTile<D>::swz(p)) << 3);
-    load_lds16(src_a + o, dst_a + blk * 512);
-    load_lds16(src_b + o, dst_b + blk * 512);
-  }
-}
-
-// 8 waves: waves 0-3 accumulate dV, waves 4-7 dK, for the same four 32-key
-// blocks (wave w and w + 4 share block w & 3 and, being w apart by 4, the same
-// SIMD).  Both roles recompute S = Q K^T; the dV role then needs only
-// P^T dO, the dK role dP = dO V^T and dS^T Q.  Splitting the roles halves the
-// accumulators a wave holds, so two waves fit per SIMD and one wave's
-// exponentials overlap the other's MFMAs.
+// 8 waves per workgroup, 128 keys of one document and one kv head; waves
+// w and w + 4 (same SIMD) share key block w & 3.  Each step (32 query rows
+// of one q head) runs in two phases separated by a barrier:
+//   phase 1: dV waves (0-3): S = Q K^T (a lane owns a key), P = exp(S - LSE)
+//            masked, P -> LDS (bf16);   dK waves (4-7): dP = dO V^T;
+//   phase 2: dV waves: dV += P^T dO;   dK waves: P from LDS,
+//            dS = P (dP - D) scale, dK += dS^T Q.
+// S is computed once, each wave holds one set of accumulators, and in each
+// phase one wave of a SIMD does its exponentials or dS while the other keeps
+// the matrix cores busy.  The step loop is unrolled by two so both tile
+// buffers have fixed addresses.
 template <int D>
 __global__ void __launch_bounds__(kKvThreads)
 attn_bwd_dkdv_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
@@ -186,7 +169,8 @@ attn_bwd_dkdv_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
   const int lq = it.lq, lk = it.lk;
   const int off = lk - lq;
   const int j0 = it.tile * KB_K;               // first key of the tile (doc-relative)
-  const int key = j0 + w * 32 + l32;           // this lane's key
+  const int kw0 = j0 + w * 32;                 // first key of this wave
+  const int key = kw0 + l32;                   // this lane's key
   const int64_t q_tok = int64_t(hq) * D;
   const int64_t kv_tok = int64_t(hkv) * D;
   const float c = scale * kLog2e;
@@ -194,21 +178,17 @@ attn_bwd_dkdv_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
   const int hpg = grp / head_split;            // q heads handled here
   const int h_begin = g * grp + split * hpg;
 
-  // K (both roles) and V (dK role) as B operands: key l32, dims 16s + 8 half ..
-  bf16x8 kf[NKS], vf[NKS];
+  // B operand of S = Q K^T (dV role: K) or dP = dO V^T (dK role: V):
+  // key l32, dims 16s + 8 half .. +8
+  bf16x8 bf[NKS];
   {
     const int64_t row = int64_t(it.k_start) + key;
-    const uint16_t* kp = k + row * kv_tok + int64_t(g) * D + 8 * half;
-    const uint16_t* vp = v + row * kv_tok + int64_t(g) * D + 8 * half;
+    const uint16_t* bp = (role == 0 ? k : v) + row * kv_tok + int64_t(g) * D + 8 * half;
 #pragma unroll
     for (int s = 0; s < NKS; ++s) {
-      u32x4 a = u32x4{0, 0, 0, 0}, bb = u32x4{0, 0, 0, 0};
-      if (key < lk) {
-        a = *reinterpret_cast<const u32x4*>(kp + 16 * s);
-        if (role) bb = *reinterpret_cast<const u32x4*>(vp + 16 * s);
-      }
-      kf[s] = as_bf16x8(a);
-      vf[s] = as_bf16x8(bb);
+      u32x4 a = u32x4{0, 0, 0, 0};
+      if (key < lk) a = *reinterpret_cast<const u32x4*>(bp + 16 * s);
+      bf[s] = as_bf16x8(a);
     }
   }
 
@@ -218,129 +198,160 @@ attn_bwd_dkdv_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
 #pragma unroll
     for (int i = 0; i < 16; ++i) acc[cb][i] = 0.f;
 
-  const int wk_first = j0 + w * 32;
   const int n_steps = hpg * it.count;
+  auto step_i0 = [&](int step) { return (it.first + step % it.count) * KB_Q; };
+  auto step_head = [&](int step) { return h_begin + step / it.count; };
+  const uint16_t* qdoc = q + int64_t(it.q_start) * q_tok;
+  const uint16_t* ddoc = dout + int64_t(it.q_start) * q_tok;
+  const PairLoader<D, KB_Q, kKvThreads / 64> loader(wave, lane, uint32_t(q_tok * 2));
 
-  // Q/dO tiles arrive by direct global->LDS loads one step ahead; the per-row
-  // LSE and D values go through registers (threads 0..31 and 64..95)
-  auto issue = [&](int step, int buf) {
-    const int h = h_begin + step / it.count;
-    const int i0 = (it.first + step % it.count) * KB_Q;
-    const int64_t hoff = int64_t(it.q_start) * q_tok + int64_t(h) * D;
-    issue_pair<D, KB_Q, 8>(sm.q[buf], sm.dout[buf], q + hoff, dout + hoff, q_tok, i0, lq, wave,
-                           lane);
+  // Q/dO tiles arrive by direct global->LDS loads one step ahead; the 32 LSE
+  // (wave 0) and D (wave 1) values of a step go through registers and are
+  // scaled when stored, so their load latency hides behind the step's
+  // compute.  Rows past the document repeat its last row (P is masked there).
+  auto issue = [&](int step, uint16_t* dq_, uint16_t* dd_) {
+    const int64_t ho = int64_t(step_head(step)) * D;
+    loader.load(qdoc + ho, ddoc + ho, q_tok, step_i0(step), lq, dq_, dd_, wave, lane);
   };
   auto fetch_rows = [&](int step) {
-    const int h = h_begin + step / it.count;
-    const int i0 = (it.first + step % it.count) * KB_Q;
     float x = 0.f;
-    if (tid < KB_Q) {
-      const int i = i0 + tid;
-      x = (i < lq) ? lse[int64_t(h) * total_q + it.q_start + i] : INFINITY;
-      x = (x == -INFINITY) ? INFINITY : x * kLog2e;
-    } else if (tid >= 64 && tid < 64 + KB_Q) {
-      const int i = i0 + tid - 64;
-      x = (i < lq) ? delta[int64_t(h) * total_q + it.q_start + i] * scale : 0.f;
+    if (wave < 2) {
+      const int i = min(step_i0(step) + l32, lq - 1);
+      x = (wave == 0 ? lse : delta)[int64_t(step_head(step)) * total_q + it.q_start + i];
     }
     return x;
   };
-  auto store_rows = [&](float x, int buf) {
-    if (tid < KB_Q) sm.lse2[buf][tid] = x;
-    else if (tid >= 64 && tid < 64 + KB_Q) sm.delta[buf][tid - 64] = x;
+  auto store_rows = [&](float x, float* l2, float* dl) {
+    if (wave < 2 && lane < KB_Q) {
+      if (wave == 0) l2[lane] = x * kLog2e;
+      else dl[lane] = x * scale;
+    }
   };
 
-  if (n_steps > 0) {
-    issue(0, 0);
-    store_rows(fetch_rows(0), 0);
-  }
-  for (int step = 0; step < n_steps; ++step) {
-    const int i0 = (it.first + step % it.count) * KB_Q;
-    const int buf = step & 1;
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
-    float nxt = 0.f;
-    if (step + 1 < n_steps) {
-      issue(step + 1, buf ^ 1);
-      nxt = fetch_rows(step + 1);
-    }
+  uint16_t* const pp = &sm.p[w][lane * 16];    // this key block's P, this lane's part
+
+  auto step = [&](int t, auto bufc) {
+    constexpr int buf = decltype(bufc)::value;
     const uint16_t* qs = sm.q[buf];
     const uint16_t* ds = sm.dout[buf];
-
-    // per-query LSE (and scaled D for the dK role) of this lane's 16 queries
-    // 16s + 8 half + t, read before the MFMAs so their latency is hidden
-    f32x4 lr[4], dr[4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      lr[j] = *reinterpret_cast<const f32x4*>(&sm.lse2[buf][16 * (j >> 1) + 8 * half + 4 * (j & 1)]);
-      dr[j] = *reinterpret_cast<const f32x4*>(&sm.delta[buf][16 * (j >> 1) + 8 * half + 4 * (j & 1)]);
+    // step t has landed; buffer buf ^ 1 and P are free
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    float rows = 0.f;
+    if (t + 1 < n_steps) {
+      issue(t + 1, sm.q[buf ^ 1], sm.dout[buf ^ 1]);
+      rows = fetch_rows(t + 1);
     }
-
-    // S = Q K^T (rows: queries 16s + 8 half + t; cols: this wave's keys).
-    // Waves whose keys this query tile cannot see still run the step, fully
-    // masked: every wave meets at the next barrier anyway.
-    f32x16 sacc;
-    {
+    const int i0 = step_i0(t);
+    // ---- phase 1
+    u32x4 pu[2];                               // dV role: P
+    f32x16 pacc;                               // dK role: dP
+    if (role == 0) {
+      // LSE of this lane's 16 queries 16s + 8 half + u, read ahead of the MFMAs
+      f32x4 lr[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        lr[j] = *reinterpret_cast<const f32x4*>(&sm.lse2[buf][16 * (j >> 1) + 8 * half + 4 * (j & 1)]);
+      // S = Q K^T (rows: queries 16s + 8 half + u; cols: this wave's keys)
+      f32x16 sacc;
       mfma_chain<NKS, 4, 0>(
           [&](int f) {
             return as_bf16x8(*reinterpret_cast<const u32x4*>(&qs[SwzTile<D>::chunk(l32, 2 * f + half)]));
           },
-          [&](int f, const bf16x8& a) { sacc = mfma32(a, kf[f], f == 0 ? f32x16{} : sacc); });
-    }
-
-    // P; element i holds query qb + e, e = 16 (i / 8) + i % 8.  It is visible
-    // iff e < lq - qb (a real row), key < lk, and (causal) e >= key - off - qb.
-    float p[16];
-    {
-      const int qb = i0 + 8 * half;
-      const int e_min = causal ? key - off - qb : INT32_MIN;
-      const int e_cap = (key < lk) ? lq - qb : INT32_MIN;
+          [&](int f, const bf16x8& a) { sacc = mfma32(a, bf[f], f == 0 ? f32x16{} : sacc); });
+      // P; element i holds query i0 + 8 half + e, e = 16 (i / 8) + i % 8
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int e = 16 * (i >> 3) + (i & 7);
-        const float pv = __builtin_amdgcn_exp2f(fmaf(sacc[i], c, -lr[i >> 2][i & 3]));
-        p[i] = (e < e_cap && e >= e_min) ? pv : 0.f;
+      for (int s2 = 0; s2 < 2; ++s2)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          float pv[2];
+#pragma unroll
+          for (int e2 = 0; e2 < 2; ++e2) {
+            const int i = 8 * s2 + 2 * j + e2;
+            pv[e2] = __builtin_amdgcn_exp2f(fmaf(sacc[i], c, -lr[i >> 2][i & 3]));
+          }
+          pu[s2][j] = pack_bf16x2(pv[0], pv[1]);
+        }
+      // Masking is needed only where the step crosses the causal diagonal or
+      // an end of the document (wave-uniform test).  Element e is visible
+      // iff e < lq - qb (a real row), key < lk, and (causal) e >= key - off - qb.
+      const bool need_mask = (i0 + KB_Q > lq) || (kw0 + 32 > lk) ||
+                             (causal && kw0 + 31 > i0 + off);
+      if (need_mask) {
+        const int qb = i0 + 8 * half;
+        const int e_min = causal ? key - off - qb : INT32_MIN;
+        const int e_cap = (key < lk) ? lq - qb : INT32_MIN;
+#pragma unroll
+        for (int s2 = 0; s2 < 2; ++s2)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const int e = 16 * s2 + 2 * j;
+            const uint32_t lo = (e < e_cap && e >= e_min) ? 0xffffu : 0u;
+            const uint32_t hi = (e + 1 < e_cap && e + 1 >= e_min) ? 0xffff0000u : 0u;
+            pu[s2][j] &= lo | hi;
+          }
       }
-    }
-
-    // A operand of the accumulation: P (dV role) or dS = P (dP - D) scale (dK role)
-    bf16x8 af[2];
-    if (role == 0) {
-#pragma unroll
-      for (int s = 0; s < 2; ++s) {
-        u32x4 u;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) u[j] = pack_bf16x2(p[8 * s + 2 * j], p[8 * s + 2 * j + 1]);
-        af[s] = as_bf16x8(u);
-      }
+      // hand P to the dK wave of this key block
+      *reinterpret_cast<u32x4*>(pp) = pu[0];
+      *reinterpret_cast<u32x4*>(pp + 8) = pu[1];
     } else {
-      f32x16 pacc;
+      // dP = dO V^T
       mfma_chain<NKS, 4, 1>(
           [&](int f) {
             return as_bf16x8(*reinterpret_cast<const u32x4*>(&ds[SwzTile<D>::chunk(l32, 2 * f + half)]));
           },
-          [&](int f, const bf16x8& a) { pacc = mfma32(a, vf[f], f == 0 ? f32x16{} : pacc); });
+          [&](int f, const bf16x8& a) { pacc = mfma32(a, bf[f], f == 0 ? f32x16{} : pacc); });
+    }
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    // ---- phase 2
+    if (role == 0) {
+      // dV += P^T dO (dO read transposed)
+      mfma_chain<2 * NCB, 4, 2>(
+          [&](int f) { return tr_frag<D>(ds, lane, 16 * (f & 1), 32 * (f >> 1)); },
+          [&](int f, const bf16x8& bfr) {
+            acc[f >> 1] = mfma32(as_bf16x8(pu[f & 1]), bfr, acc[f >> 1]);
+          });
+    } else {
+      f32x4 dr[4];
 #pragma unroll
-      for (int s = 0; s < 2; ++s) {
+      for (int j = 0; j < 4; ++j)
+        dr[j] = *reinterpret_cast<const f32x4*>(&sm.delta[buf][16 * (j >> 1) + 8 * half + 4 * (j & 1)]);
+      const u32x4 pu0 = *reinterpret_cast<const u32x4*>(pp);
+      const u32x4 pu1 = *reinterpret_cast<const u32x4*>(pp + 8);
+      // dS = P (dP - D) scale, in the A-operand layout of dK += dS^T Q
+      bf16x8 af[2];
+#pragma unroll
+      for (int s2 = 0; s2 < 2; ++s2) {
+        const u32x4 pw = s2 ? pu1 : pu0;
         u32x4 u;
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          const int i = 8 * s + 2 * j;
-          u[j] = pack_bf16x2(p[i] * fmaf(pacc[i], scale, -dr[i >> 2][i & 3]),
-                             p[i + 1] * fmaf(pacc[i + 1], scale, -dr[(i + 1) >> 2][(i + 1) & 3]));
+          const int i = 8 * s2 + 2 * j;
+          const float p0 = bf16_lo(pw[j]), p1 = bf16_hi(pw[j]);
+          u[j] = pack_bf16x2(p0 * fmaf(pacc[i], scale, -dr[i >> 2][i & 3]),
+                             p1 * fmaf(pacc[i + 1], scale, -dr[(i + 1) >> 2][(i + 1) & 3]));
         }
-        af[s] = as_bf16x8(u);
+        af[s2] = as_bf16x8(u);
       }
-    }
-
-    // dV += P^T dO or dK += dS^T Q  (B operands read transposed)
-    {
-      const uint16_t* bt = role == 0 ? ds : qs;
-      mfma_chain<2 * NCB, 4, 2>(
-          [&](int f) { return tr_frag<D>(bt, lane, 16 * (f & 1), 32 * (f >> 1)); },
+      // dK += dS^T Q (Q read transposed)
+      mfma_chain<2 * NCB, 4, 3>(
+          [&](int f) { return tr_frag<D>(qs, lane, 16 * (f & 1), 32 * (f >> 1)); },
           [&](int f, const bf16x8& bfr) { acc[f >> 1] = mfma32(af[f & 1], bfr, acc[f >> 1]); });
     }
-    if (step + 1 < n_steps) store_rows(nxt, buf ^ 1);
+    if (t + 1 < n_steps) store_rows(rows, sm.lse2[buf ^ 1], sm.delta[buf ^ 1]);
+  };
+
+  if (n_steps > 0) {
+    issue(0, sm.q[0], sm.dout[0]);
+    store_rows(fetch_rows(0), sm.lse2[0], sm.delta[0]);
   }
+  int t = 0;
+  for (; t + 1 < n_steps; t += 2) {
+    step(t, IC<0>{});
+    step(t + 1, IC<1>{});
+  }
+  if (t < n_steps) step(t, IC<0>{});
 
   // epilogue: lane holds column c = 32 cb + l32 of keys 32 w + 8 (v/4) + 4 half + v%4
   uint16_t* outp = role == 0 ? dv : dk;
@@ -349,7 +360,7 @@ attn_bwd_dkdv_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
   for (int cb = 0; cb < NCB; ++cb) {
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
-      const int kk = j0 + w * 32 + 8 * (i >> 2) + 4 * half + (i & 3);
+      const int kk = kw0 + 8 * (i >> 2) + 4 * half + (i & 3);
       if (kk < lk) {
         const int64_t idx = (int64_t(it.k_start) + kk) * kv_tok + int64_t(g) * D + cb * 32 + l32;
         if (head_split == 1)
@@ -359,7 +370,6 @@ attn_bwd_dkdv_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
       }
     }
   }
-  (void)wk_first;
 }
 
 // ---------------------------------------------------------------- dQ
@@ -431,6 +441,7 @@ attn_bwd_dq_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ 
     lse2 = (l == -INFINITY) ? INFINITY : l * kLog2e;
     dl = delta[int64_t(h) * total_q + it.q_start + qrow];
   }
+  const float dls = dl * scale;
 
   f32x16 acc[NCB];
 #pragma unroll
@@ -440,45 +451,44 @@ attn_bwd_dq_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ 
 
   const uint16_t* kbase = k + int64_t(it.k_start) * kv_tok + int64_t(g) * D;
   const uint16_t* vbase = v + int64_t(it.k_start) * kv_tok + int64_t(g) * D;
+  const PairLoader<D, QB_K, kThreads / 64> loader(w, lane, uint32_t(kv_tok * 2));
   const int wq_first = q0 + w * 32;
   const int wq_last = min(q0 + w * 32 + 31, lq - 1);
+  const int lim = causal ? min(lk - 1, qrow + off) : lk - 1;
 
-  const int n_kv = it.count;
-  if (n_kv > 0) issue_pair<D, QB_K, 4>(sm.k[0], sm.v[0], kbase, vbase, kv_tok, 0, lk, w, lane);
-  for (int kt = 0; kt < n_kv; ++kt) {
+  // one key tile (buffer index fixed at compile time, as in the forward)
+  auto tile = [&](int kt, auto bufc) {
+    constexpr int buf = decltype(bufc)::value;
     const int kv0 = kt * QB_K;
-    const int buf = kt & 1;
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-    if (kt + 1 < n_kv)
-      issue_pair<D, QB_K, 4>(sm.k[buf ^ 1], sm.v[buf ^ 1], kbase, vbase, kv_tok, kv0 + QB_K, lk, w,
-                             lane);
+    if (kt + 1 < it.count)
+      loader.load(kbase, vbase, kv_tok, kv0 + QB_K, lk, sm.k[buf ^ 1], sm.v[buf ^ 1], w, lane);
     const uint16_t* ks = sm.k[buf];
     const uint16_t* vs = sm.v[buf];
 
     const bool live = (wq_first < lq) && (!causal || kv0 <= wq_last + off);
-    if (!live) continue;
+    if (!live) return;
     const bool need_mask = (kv0 + QB_K > lk) || (causal && kv0 + QB_K - 1 > wq_first + off);
 
     // per 32-key half kb: S^T and dP^T (16 MFMAs), then dS^T packed to bf16;
     // one half at a time keeps only one pair of accumulators live
-    const int lim = causal ? min(lk - 1, qrow + off) : lk - 1;
     bf16x8 dsf[2][2];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
       f32x16 sa, da;
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        sa[i] = 0.f;
-        da[i] = 0.f;
-      }
       const int prow = kb * 32 + l32;
 #pragma unroll
       for (int st = 0; st < NKS; ++st) {
         const int o = SwzTile<D>::chunk(prow, 2 * st + half);
-        sa = mfma32(as_bf16x8(*reinterpret_cast<const u32x4*>(&ks[o])), qf[st], sa);
-        da = mfma32(as_bf16x8(*reinterpret_cast<const u32x4*>(&vs[o])), df[st], da);
+        sa = mfma32(as_bf16x8(*reinterpret_cast<const u32x4*>(&ks[o])), qf[st],
+                    st == 0 ? f32x16{} : sa);
+        da = mfma32(as_bf16x8(*reinterpret_cast<const u32x4*>(&vs[o])), df[st],
+                    st == 0 ? f32x16{} : da);
       }
+      // key kv0 + 32 kb + 8 half + e (e = 16 hs + 2 j + e2) is visible iff
+      // e <= thr
+      const int thr = need_mask ? lim - kv0 - 32 * kb - 8 * half : 64;
 #pragma unroll
       for (int hs = 0; hs < 2; ++hs) {
         u32x4 u;
@@ -489,11 +499,8 @@ attn_bwd_dq_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ 
           for (int e = 0; e < 2; ++e) {
             const int i = 8 * hs + 2 * j + e;
             float pv_ = __builtin_amdgcn_exp2f(fmaf(sa[i], c, -lse2));
-            if (need_mask) {
-              const int kk = kv0 + kb * 32 + 16 * hs + 8 * half + 2 * j + e;
-              if (kk > lim) pv_ = 0.f;
-            }
-            dsv[e] = pv_ * (da[i] - dl) * scale;
+            if (need_mask && 16 * hs + 2 * j + e > thr) pv_ = 0.f;
+            dsv[e] = pv_ * fmaf(da[i], scale, -dls);
           }
           u[j] = pack_bf16x2(dsv[0], dsv[1]);
         }
@@ -509,7 +516,16 @@ attn_bwd_dq_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ 
 #pragma unroll
         for (int hs = 0; hs < 2; ++hs)
           acc[cb] = mfma32(tr_frag<D>(ks, lane, 32 * kb + 16 * hs, 32 * cb), dsf[kb][hs], acc[cb]);
+  };
+
+  const int n_kv = it.count;
+  if (n_kv > 0) loader.load(kbase, vbase, kv_tok, 0, lk, sm.k[0], sm.v[0], w, lane);
+  int kt = 0;
+  for (; kt + 1 < n_kv; kt += 2) {
+    tile(kt, IC<0>{});
+    tile(kt + 1, IC<1>{});
   }
+  if (kt < n_kv) tile(kt, IC<0>{});
 
   if (qrow < lq) {
     const int64_t orow = (int64_t(it.q_start) + qrow) * q_tok + int64_t(h) * D;

@@ -21,7 +21,8 @@
 //     chunks; the V^T operand is read with the gfx950 transpose read
 //     (ds_read_b64_tr_b16), so no transposed copy is stored; tiles are
 //     double-buffered and filled by direct global->LDS loads issued one tile
-//     ahead (one barrier per tile, no staging registers);
+//     ahead (one barrier per tile, no staging registers); the tile loop is
+//     unrolled by two so both buffers have fixed addresses;
 //   * work items are ordered longest first and the workgroup id is remapped
 //     so all q heads of one item run on the same XCD (shared K/V in its L2).
 #include <hip/hip_runtime.h>
@@ -47,31 +48,6 @@ struct FwdSmem {
   uint16_t k[2][BK * D];
   uint16_t v[2][BK * D];
 };
-
-// Issues the direct global->LDS loads of one K/V tile.  Each wave instruction
-// fills 1 KB of LDS (64 lanes x 16 bytes = 1024 / (2 D) rows); the lane that
-// lands on LDS row p, chunk pc fetches key row swap_bits23(p), chunk
-// pc ^ swz(p).  Rows past the document are clamped to its last row: those
-// keys are masked out, so their (finite) values never reach the result.
-template <int D>
-__device__ __forceinline__ void issue_tile(uint16_t* lk_dst, uint16_t* lv_dst,
-                                           const uint16_t* __restrict__ kbase,
-                                           const uint16_t* __restrict__ vbase, int64_t tok_stride,
-                                           int kv0, int lk, int wave, int lane) {
-  constexpr int NCH = D / 8;
-  constexpr int ROWS_PER_LOAD = 64 / NCH;
-  constexpr int LOADS = BK / ROWS_PER_LOAD / (kThreads / 64);   // per wave per tensor
-#pragma unroll
-  for (int u = 0; u < LOADS; ++u) {
-    const int blk = u * (kThreads / 64) + wave;
-    const int p = blk * ROWS_PER_LOAD + lane / NCH;
-    const int pc = lane % NCH;
-    const int key = min(kv0 + swap_bits23(p), lk - 1);
-    const int64_t o = int64_t(key) * tok_stride + ((pc ^ SwzTile<D>::swz(p)) << 3);
-    load_lds16(kbase + o, lk_dst + blk * 512);
-    load_lds16(vbase + o, lv_dst + blk * 512);
-  }
-}
 
 template <int D, bool F32OUT>
 __global__ void __launch_bounds__(kThreads, 2)
@@ -130,31 +106,30 @@ attn_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
 
   const uint16_t* kbase = k + int64_t(it.k_start) * kv_tok + int64_t(g) * D;
   const uint16_t* vbase = v + int64_t(it.k_start) * kv_tok + int64_t(g) * D;
+  const PairLoader<D, BK, kThreads / 64> loader(w, lane, uint32_t(kv_tok * 2));
 
   // first and last query rows of this wave (for skipping / masking)
   const int wq_first = q0 + w * 32;
   const int wq_last = min(q0 + w * 32 + 31, lq - 1);
 
-  const int n_kv = it.count;
-  if (n_kv > 0) issue_tile<D>(sm.k[0], sm.v[0], kbase, vbase, kv_tok, 0, lk, w, lane);
-
-  for (int kt = 0; kt < n_kv; ++kt) {
+  // one key tile; the buffer index is a compile-time constant so every LDS
+  // address is a loop-invariant register plus an immediate offset
+  auto tile = [&](int kt, auto bufc) {
+    constexpr int buf = decltype(bufc)::value;
     const int kv0 = kt * BK;
-    const int buf = kt & 1;
     // tile kt has landed in every wave's part of buffer `buf`, and every wave
     // is done with the other buffer (read during tile kt - 1)
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-    if (kt + 1 < n_kv)
-      issue_tile<D>(sm.k[buf ^ 1], sm.v[buf ^ 1], kbase, vbase, kv_tok, kv0 + BK, lk, w, lane);
+    if (kt + 1 < it.count)
+      loader.load(kbase, vbase, kv_tok, kv0 + BK, lk, sm.k[buf ^ 1], sm.v[buf ^ 1], w, lane);
     const uint16_t* ks = sm.k[buf];
     const uint16_t* vs = sm.v[buf];
 
     // wave-uniform: skip tiles no query of this wave can see
     const bool wave_live = (wq_first < lq) && (!causal || kv0 <= wq_last + off);
-    if (!wave_live) continue;
+    if (!wave_live) return;
     const bool need_mask = (kv0 + BK > lk) || (causal && kv0 + BK - 1 > wq_first + off);
-
     // S^T for the two 32-key halves of the tile.  K fragments are read from
     // LDS kPf steps ahead of the MFMA that consumes them, and the schedule is
     // pinned to (1 MFMA, 1 LDS read) pairs so the read latency hides behind
@@ -190,14 +165,16 @@ attn_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     }
 
     if (need_mask) {
+      // key kv0 + 32 kb + 8 half + e (e = 16 (i / 8) + i % 8) is visible iff
+      // e <= lim - kv0 - 32 kb - 8 half
       const int lim = causal ? min(lk - 1, qrow + off) : lk - 1;
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
+      for (int kb = 0; kb < 2; ++kb) {
+        const int thr = lim - kv0 - 32 * kb - 8 * half;
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int key = kv0 + kb * 32 + 16 * (i >> 3) + 8 * half + (i & 7);
-          if (key > lim) s[kb][i] = -INFINITY;
-        }
+        for (int i = 0; i < 16; ++i)
+          if (16 * (i >> 3) + (i & 7) > thr) s[kb][i] = -INFINITY;
+      }
     }
 
     float mx = -INFINITY;
@@ -271,7 +248,16 @@ attn_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
       }
     }
     l_run += psum;
+  };
+
+  const int n_kv = it.count;
+  if (n_kv > 0) loader.load(kbase, vbase, kv_tok, 0, lk, sm.k[0], sm.v[0], w, lane);
+  int kt = 0;
+  for (; kt + 1 < n_kv; kt += 2) {
+    tile(kt, IC<0>{});
+    tile(kt + 1, IC<1>{});
   }
+  if (kt < n_kv) tile(kt, IC<0>{});
 
   // epilogue: O = acc / l, LSE = m scale + ln l
   const float l_tot = halves_sum(l_run);

@@ -94,11 +94,97 @@ __device__ __forceinline__ bf16x8 tr_frag(const uint16_t* tile, int lane, int r0
   return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
 }
 
-// Direct global -> LDS copy of 16 bytes per lane: lane i's bytes land at
-// lds_base + 16 i (lds_base must be the same in every lane of the wave).
-__device__ __forceinline__ void load_lds16(const void* gsrc, uint16_t* lds_base) {
-  __builtin_amdgcn_global_load_lds(gsrc, (__attribute__((address_space(3))) void*)(lds_base), 16, 0, 0);
+// Direct global -> LDS copy of 16 bytes per lane: lane i reads sbase + voff
+// (sbase wave-uniform, voff its own byte offset) and its bytes land at
+// lds_base + 16 i (lds_base wave-uniform).  The copy is issued from inline
+// assembly so that the compiler does not track its LDS write: it cannot tell
+// the buffers of a multi-buffered tile apart and would otherwise make every
+// transpose read wait for all copies in flight, which serialises the prefetch
+// of the next tile with the current one.  Callers order the copy against
+// reads of its destination themselves (s_waitcnt on vmcnt followed by a
+// workgroup barrier before the first read).
+__device__ __forceinline__ void load_lds16(const void* sbase, uint32_t voff, uint16_t* lds_base) {
+  const uint32_t m0 = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(
+      (__attribute__((address_space(3))) uint16_t*)lds_base));
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
+               :
+               : "v"(voff), "s"(sbase), "s"(m0)
+               : "memory", "m0");
 }
+
+// The direct loads of a pair of ROWS x D bf16 tiles (the same rows of two
+// [T, H, D] tensors) into SwzTile layout, spread over the NW waves of a
+// workgroup.  Load u of a lane fills LDS block u NW + wave (1 KB: 64 lanes x
+// 16 bytes); the lane that lands on LDS row p, chunk pc fetches source row
+// swap_bits23(p), chunk pc ^ swz(p).  The lane's byte offsets relative to the
+// tile's first row are computed once, so a tile costs one scalar base
+// pointer per tensor.  Near the end of a document, rows at or past n_valid
+// are clamped to its last row (whose values are then masked wherever used).
+template <int D, int ROWS, int NW>
+struct PairLoader {
+  static constexpr int NCH = D / 8;            // 16-byte chunks per row
+  static constexpr int RPL = 64 / NCH;         // rows per 1 KB block
+  static constexpr int BLKS = ROWS / RPL;
+  static constexpr int N = (BLKS + NW - 1) / NW;   // loads per lane per tensor
+  uint32_t voff[N];
+
+  // wave-uniform: whether load u of this wave exists
+  __device__ __forceinline__ static bool has(int u, int wave) {
+    return BLKS % NW == 0 || u * NW + wave < BLKS;
+  }
+
+  __device__ __forceinline__ static int src_row(int u, int wave, int lane) {
+    return swap_bits23((u * NW + wave) * RPL + lane / NCH);
+  }
+  __device__ __forceinline__ static uint32_t col_bytes(int u, int wave, int lane) {
+    const int p = (u * NW + wave) * RPL + lane / NCH;
+    return uint32_t(((lane % NCH) ^ SwzTile<D>::swz(p)) << 4);
+  }
+  __device__ __forceinline__ PairLoader(int wave, int lane, uint32_t row_bytes) {
+#pragma unroll
+    for (int u = 0; u < N; ++u)
+      voff[u] = uint32_t(src_row(u, wave, lane)) * row_bytes + col_bytes(u, wave, lane);
+  }
+  // a, b: first row of the tile in each tensor (wave-uniform)
+  __device__ __forceinline__ void issue(const uint16_t* a, const uint16_t* b, uint16_t* da,
+                                        uint16_t* db, int wave) const {
+#pragma unroll
+    for (int u = 0; u < N; ++u) {
+      if (!has(u, wave)) continue;
+      load_lds16(a, voff[u], da + (u * NW + wave) * 512);
+      load_lds16(b, voff[u], db + (u * NW + wave) * 512);
+    }
+  }
+  __device__ __forceinline__ void issue_clamped(const uint16_t* a, const uint16_t* b, uint16_t* da,
+                                                uint16_t* db, int wave, int lane, int n_valid,
+                                                uint32_t row_bytes) const {
+#pragma unroll
+    for (int u = 0; u < N; ++u) {
+      if (!has(u, wave)) continue;
+      const uint32_t o = uint32_t(min(src_row(u, wave, lane), n_valid - 1)) * row_bytes +
+                         col_bytes(u, wave, lane);
+      load_lds16(a, o, da + (u * NW + wave) * 512);
+      load_lds16(b, o, db + (u * NW + wave) * 512);
+    }
+  }
+  // tile of rows row0 .. row0 + ROWS - 1 of a document with n_rows rows;
+  // a, b point at the document's first row
+  __device__ __forceinline__ void load(const uint16_t* a, const uint16_t* b, int64_t row_elems,
+                                       int row0, int n_rows, uint16_t* da, uint16_t* db, int wave,
+                                       int lane) const {
+    const int64_t o = int64_t(row0) * row_elems;
+    if (row0 + ROWS <= n_rows)
+      issue(a + o, b + o, da, db, wave);
+    else
+      issue_clamped(a + o, b + o, da, db, wave, lane, n_rows - row0, uint32_t(row_elems * 2));
+  }
+};
+
+// integral constant for compile-time buffer indices
+template <int V>
+struct IC {
+  static constexpr int value = V;
+};
 
 // Exchange a value with the lane 32 positions away (the other half-wave).
 __device__ __forceinline__ float xor32(float x) {
