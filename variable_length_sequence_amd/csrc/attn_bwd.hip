@@ -198,9 +198,18 @@ attn_bwd_dkdv_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
 #pragma unroll
     for (int i = 0; i < 16; ++i) acc[cb][i] = 0.f;
 
+  // steps run over (q head, 32-row query tile) pairs, tiles innermost; the
+  // position of the current and the next step is advanced incrementally
   const int n_steps = hpg * it.count;
-  auto step_i0 = [&](int step) { return (it.first + step % it.count) * KB_Q; };
-  auto step_head = [&](int step) { return h_begin + step / it.count; };
+  const int i_begin = it.first * KB_Q;
+  const int i_end = (it.first + it.count) * KB_Q;
+  auto advance = [&](int& i0, int& h) {
+    i0 += KB_Q;
+    if (i0 == i_end) {
+      i0 = i_begin;
+      ++h;
+    }
+  };
   const uint16_t* qdoc = q + int64_t(it.q_start) * q_tok;
   const uint16_t* ddoc = dout + int64_t(it.q_start) * q_tok;
   const PairLoader<D, KB_Q, kKvThreads / 64> loader(wave, lane, uint32_t(q_tok * 2));
@@ -209,15 +218,15 @@ attn_bwd_dkdv_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
   // (wave 0) and D (wave 1) values of a step go through registers and are
   // scaled when stored, so their load latency hides behind the step's
   // compute.  Rows past the document repeat its last row (P is masked there).
-  auto issue = [&](int step, uint16_t* dq_, uint16_t* dd_) {
-    const int64_t ho = int64_t(step_head(step)) * D;
-    loader.load(qdoc + ho, ddoc + ho, q_tok, step_i0(step), lq, dq_, dd_, wave, lane);
+  auto issue = [&](int i0, int h, uint16_t* dq_, uint16_t* dd_) {
+    const int64_t ho = int64_t(h) * D;
+    loader.load(qdoc + ho, ddoc + ho, q_tok, i0, lq, dq_, dd_, wave, lane);
   };
-  auto fetch_rows = [&](int step) {
+  auto fetch_rows = [&](int i0, int h) {
     float x = 0.f;
     if (wave < 2) {
-      const int i = min(step_i0(step) + l32, lq - 1);
-      x = (wave == 0 ? lse : delta)[int64_t(step_head(step)) * total_q + it.q_start + i];
+      const int i = min(i0 + l32, lq - 1);
+      x = (wave == 0 ? lse : delta)[int64_t(h) * total_q + it.q_start + i];
     }
     return x;
   };
@@ -227,6 +236,8 @@ attn_bwd_dkdv_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
       else dl[lane] = x * scale;
     }
   };
+  int cur_i0 = i_begin;                        // step t
+  int nxt_i0 = i_begin, nxt_h = h_begin;       // step t + 1
 
   uint16_t* const pp = &sm.p[w][lane * 16];    // this key block's P, this lane's part
 
@@ -239,10 +250,10 @@ attn_bwd_dkdv_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
     __syncthreads();
     float rows = 0.f;
     if (t + 1 < n_steps) {
-      issue(t + 1, sm.q[buf ^ 1], sm.dout[buf ^ 1]);
-      rows = fetch_rows(t + 1);
+      issue(nxt_i0, nxt_h, sm.q[buf ^ 1], sm.dout[buf ^ 1]);
+      rows = fetch_rows(nxt_i0, nxt_h);
     }
-    const int i0 = step_i0(t);
+    const int i0 = cur_i0;
     // ---- phase 1
     u32x4 pu[2];                               // dV role: P
     f32x16 pacc;                               // dK role: dP
@@ -253,12 +264,15 @@ attn_bwd_dkdv_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
       for (int j = 0; j < 4; ++j)
         lr[j] = *reinterpret_cast<const f32x4*>(&sm.lse2[buf][16 * (j >> 1) + 8 * half + 4 * (j & 1)]);
       // S = Q K^T (rows: queries 16s + 8 half + u; cols: this wave's keys)
+      // the S chain is on the step's critical path: let it issue first
+      __builtin_amdgcn_s_setprio(1);
       f32x16 sacc;
       mfma_chain<NKS, 4, 0>(
           [&](int f) {
             return as_bf16x8(*reinterpret_cast<const u32x4*>(&qs[SwzTile<D>::chunk(l32, 2 * f + half)]));
           },
           [&](int f, const bf16x8& a) { sacc = mfma32(a, bf[f], f == 0 ? f32x16{} : sacc); });
+      __builtin_amdgcn_s_setprio(0);
       // P; element i holds query i0 + 8 half + e, e = 16 (i / 8) + i % 8
 #pragma unroll
       for (int s2 = 0; s2 < 2; ++s2)
@@ -340,11 +354,14 @@ attn_bwd_dkdv_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
           [&](int f, const bf16x8& bfr) { acc[f >> 1] = mfma32(af[f & 1], bfr, acc[f >> 1]); });
     }
     if (t + 1 < n_steps) store_rows(rows, sm.lse2[buf ^ 1], sm.delta[buf ^ 1]);
+    cur_i0 = nxt_i0;
+    advance(nxt_i0, nxt_h);
   };
 
   if (n_steps > 0) {
-    issue(0, sm.q[0], sm.dout[0]);
-    store_rows(fetch_rows(0), sm.lse2[0], sm.delta[0]);
+    issue(nxt_i0, nxt_h, sm.q[0], sm.dout[0]);
+    store_rows(fetch_rows(nxt_i0, nxt_h), sm.lse2[0], sm.delta[0]);
+    advance(nxt_i0, nxt_h);
   }
   int t = 0;
   for (; t + 1 < n_steps; t += 2) {
