@@ -109,32 +109,31 @@ constexpr int KB_Q = kBwdBQ;   // 32 query rows per step
 constexpr int KB_K = kBwdBK;   // 128 keys per workgroup
 constexpr int kKvThreads = 512;
 
+constexpr int kKvBufs = 3;      // steps in flight: t - 1 (dK role), t (dV role), t + 1 (loading)
+
 template <int D>
 struct KvSmem {
-  // double-buffered Q and dO tiles, row-major with swizzled chunks; query
-  // row r is kept at LDS row swap_bits23(r).  The transposed operands (dO for
-  // dV += P^T dO, Q for dK += dS^T Q) are read from the same tiles with the
-  // transpose read.
-  uint16_t q[2][KB_Q * D];
-  uint16_t dout[2][KB_Q * D];
-  alignas(16) float lse2[2][KB_Q];   // LSE log2(e)
-  alignas(16) float delta[2][KB_Q];  // D scale
-  // P of the current step, bf16, in the A-operand layout of each dV wave
-  // (lane-major, 32 bytes per lane)
-  alignas(16) uint16_t p[4][64 * 16];
+  // Q and dO tiles, row-major with swizzled chunks; query row r is kept at
+  // LDS row swap_bits23(r).  The transposed operands (dO for dV += P^T dO, Q
+  // for dK += dS^T Q) are read from the same tiles with the transpose read.
+  uint16_t q[kKvBufs][KB_Q * D];
+  uint16_t dout[kKvBufs][KB_Q * D];
+  alignas(16) float lse2[kKvBufs][KB_Q];   // LSE log2(e)
+  alignas(16) float delta[kKvBufs][KB_Q];  // D scale
+  // P of the last two steps, bf16, in the A-operand layout of each dV wave:
+  // [step parity][key block][operand half][lane][8]
+  alignas(16) uint16_t p[2][4][2][64 * 8];
 };
 
 // 8 waves per workgroup, 128 keys of one document and one kv head; waves
-// w and w + 4 (same SIMD) share key block w & 3.  Each step (32 query rows
-// of one q head) runs in two phases separated by a barrier:
-//   phase 1: dV waves (0-3): S = Q K^T (a lane owns a key), P = exp(S - LSE)
-//            masked, P -> LDS (bf16);   dK waves (4-7): dP = dO V^T;
-//   phase 2: dV waves: dV += P^T dO;   dK waves: P from LDS,
-//            dS = P (dP - D) scale, dK += dS^T Q.
-// S is computed once, each wave holds one set of accumulators, and in each
-// phase one wave of a SIMD does its exponentials or dS while the other keeps
-// the matrix cores busy.  The step loop is unrolled by two so both tile
-// buffers have fixed addresses.
+// w and w + 4 (same SIMD) share key block w & 3.  Iteration t:
+//  * waves 0-3 (dV role) take step t: S = Q K^T (a lane owns a key),
+//    P = exp(S - LSE) masked, P -> LDS (bf16), dV += P^T dO;
+//  * waves 4-7 (dK role) take step t - 1: dP = dO V^T, P from LDS,
+//    dS = P (dP - D) scale, dK += dS^T Q.
+// Both roles run the same two MFMA chains on role-dependent LDS tiles (only
+// the elementwise middle differs), so the accumulators have one home; the
+// two waves of a SIMD work on different steps and overlap freely.
 template <int D>
 __global__ void __launch_bounds__(kKvThreads)
 attn_bwd_dkdv_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
@@ -173,10 +172,11 @@ attn_bwd_dkdv_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
   const int key = kw0 + l32;                   // this lane's key
   const int64_t q_tok = int64_t(hq) * D;
   const int64_t kv_tok = int64_t(hkv) * D;
-  const float c = scale * kLog2e;
   const int grp = hq / hkv;
   const int hpg = grp / head_split;            // q heads handled here
   const int h_begin = g * grp + split * hpg;
+  // the first chain's result x becomes fma(x, alpha, -row)
+  const float alpha = role == 0 ? scale * kLog2e : scale;
 
   // B operand of S = Q K^T (dV role: K) or dP = dO V^T (dK role: V):
   // key l32, dims 16s + 8 half .. +8
@@ -192,14 +192,32 @@ attn_bwd_dkdv_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
     }
   }
 
+  // loop-invariant element offsets of this lane's LDS reads within a tile:
+  // A fragments of the first chain (row l32, chunk 2f + half) and the two
+  // halves of the transposed B fragments of the second chain (rows
+  // 4 (g4 / 2) + j4 and + 8, columns 32 cb + 16 (g4 & 1) + 4 m4)
+  uint32_t a_off[NKS];
+#pragma unroll
+  for (int f = 0; f < NKS; ++f) a_off[f] = uint32_t(SwzTile<D>::chunk(l32, 2 * f + half));
+  uint32_t t_off[NCB][2];
+  {
+    const int g4 = lane >> 4, j4 = (lane >> 2) & 3, m4 = lane & 3;
+    const int row = 4 * (g4 >> 1) + j4;
+#pragma unroll
+    for (int cb = 0; cb < NCB; ++cb) {
+      const int col = 32 * cb + 16 * (g4 & 1) + 4 * m4;
+      t_off[cb][0] = uint32_t(SwzTile<D>::elem(row, col));
+      t_off[cb][1] = uint32_t(SwzTile<D>::elem(row + 8, col));
+    }
+  }
+
   f32x16 acc[NCB];                             // dV (role 0) or dK (role 1)
 #pragma unroll
   for (int cb = 0; cb < NCB; ++cb)
 #pragma unroll
     for (int i = 0; i < 16; ++i) acc[cb][i] = 0.f;
 
-  // steps run over (q head, 32-row query tile) pairs, tiles innermost; the
-  // position of the current and the next step is advanced incrementally
+  // steps run over (q head, 32-row query tile) pairs, tiles innermost
   const int n_steps = hpg * it.count;
   const int i_begin = it.first * KB_Q;
   const int i_end = (it.first + it.count) * KB_Q;
@@ -230,145 +248,120 @@ attn_bwd_dkdv_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
     }
     return x;
   };
-  auto store_rows = [&](float x, float* l2, float* dl) {
+  auto store_rows = [&](float x, int buf) {
     if (wave < 2 && lane < KB_Q) {
-      if (wave == 0) l2[lane] = x * kLog2e;
-      else dl[lane] = x * scale;
+      if (wave == 0) sm.lse2[buf][lane] = x * kLog2e;
+      else sm.delta[buf][lane] = x * scale;
     }
   };
-  int cur_i0 = i_begin;                        // step t
+
   int nxt_i0 = i_begin, nxt_h = h_begin;       // step t + 1
-
-  uint16_t* const pp = &sm.p[w][lane * 16];    // this key block's P, this lane's part
-
-  auto step = [&](int t, auto bufc) {
-    constexpr int buf = decltype(bufc)::value;
-    const uint16_t* qs = sm.q[buf];
-    const uint16_t* ds = sm.dout[buf];
-    // step t has landed; buffer buf ^ 1 and P are free
-    __builtin_amdgcn_s_waitcnt(0);
+  int cur_i0 = i_begin;                        // step t (dV role)
+  int prv_i0 = i_begin;                        // step t - 1 (unused by the dK role)
+  (void)prv_i0;
+  if (n_steps > 0) {
+    issue(nxt_i0, nxt_h, sm.q[0], sm.dout[0]);
+    store_rows(fetch_rows(nxt_i0, nxt_h), 0);
+    advance(nxt_i0, nxt_h);
+  }
+  int cur = 0;                                 // buffer of step t
+  for (int t = 0; t <= n_steps; ++t) {
+    const int nxt = cur == kKvBufs - 1 ? 0 : cur + 1;
+    const int prv = cur == 0 ? kKvBufs - 1 : cur - 1;
+    // step t has landed; nobody reads buffer nxt any more (step t - 2)
+    __builtin_amdgcn_s_waitcnt(kWaitAll);
     __syncthreads();
     float rows = 0.f;
     if (t + 1 < n_steps) {
-      issue(nxt_i0, nxt_h, sm.q[buf ^ 1], sm.dout[buf ^ 1]);
+      issue(nxt_i0, nxt_h, sm.q[nxt], sm.dout[nxt]);
       rows = fetch_rows(nxt_i0, nxt_h);
     }
-    const int i0 = cur_i0;
-    // ---- phase 1
-    u32x4 pu[2];                               // dV role: P
-    f32x16 pacc;                               // dK role: dP
-    if (role == 0) {
-      // LSE of this lane's 16 queries 16s + 8 half + u, read ahead of the MFMAs
-      f32x4 lr[4];
+    const int st = t - role;                   // this wave's step
+    if (st >= 0 && st < n_steps) {
+      const int sb = role == 0 ? cur : prv;    // its buffer
+      const uint16_t* tile1 = role == 0 ? sm.q[sb] : sm.dout[sb];
+      const uint16_t* tile2 = role == 0 ? sm.dout[sb] : sm.q[sb];
+      const float* rowv = role == 0 ? sm.lse2[sb] : sm.delta[sb];
+      // this lane's 16 queries 16s + 8 half + u: LSE log2(e) or D scale
+      f32x4 rr[4];
 #pragma unroll
       for (int j = 0; j < 4; ++j)
-        lr[j] = *reinterpret_cast<const f32x4*>(&sm.lse2[buf][16 * (j >> 1) + 8 * half + 4 * (j & 1)]);
-      // S = Q K^T (rows: queries 16s + 8 half + u; cols: this wave's keys)
-      // the S chain is on the step's critical path: let it issue first
-      __builtin_amdgcn_s_setprio(1);
-      f32x16 sacc;
+        rr[j] = *reinterpret_cast<const f32x4*>(&rowv[16 * (j >> 1) + 8 * half + 4 * (j & 1)]);
+      // S = Q K^T or dP = dO V^T (rows: queries 16s + 8 half + u; cols: keys)
+      f32x16 x;
       mfma_chain<NKS, 4, 0>(
-          [&](int f) {
-            return as_bf16x8(*reinterpret_cast<const u32x4*>(&qs[SwzTile<D>::chunk(l32, 2 * f + half)]));
-          },
-          [&](int f, const bf16x8& a) { sacc = mfma32(a, bf[f], f == 0 ? f32x16{} : sacc); });
-      __builtin_amdgcn_s_setprio(0);
-      // P; element i holds query i0 + 8 half + e, e = 16 (i / 8) + i % 8
-#pragma unroll
-      for (int s2 = 0; s2 < 2; ++s2)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          float pv[2];
-#pragma unroll
-          for (int e2 = 0; e2 < 2; ++e2) {
-            const int i = 8 * s2 + 2 * j + e2;
-            pv[e2] = __builtin_amdgcn_exp2f(fmaf(sacc[i], c, -lr[i >> 2][i & 3]));
-          }
-          pu[s2][j] = pack_bf16x2(pv[0], pv[1]);
-        }
-      // Masking is needed only where the step crosses the causal diagonal or
-      // an end of the document (wave-uniform test).  Element e is visible
-      // iff e < lq - qb (a real row), key < lk, and (causal) e >= key - off - qb.
-      const bool need_mask = (i0 + KB_Q > lq) || (kw0 + 32 > lk) ||
-                             (causal && kw0 + 31 > i0 + off);
-      if (need_mask) {
-        const int qb = i0 + 8 * half;
-        const int e_min = causal ? key - off - qb : INT32_MIN;
-        const int e_cap = (key < lk) ? lq - qb : INT32_MIN;
+          [&](int f) { return as_bf16x8(*reinterpret_cast<const u32x4*>(tile1 + a_off[f])); },
+          [&](int f, const bf16x8& a) { x = mfma32(a, bf[f], f == 0 ? f32x16{} : x); });
+      // element i holds query i0 + 8 half + e, e = 16 (i / 8) + i % 8
+      u32x4 au[2];
+      if (role == 0) {
+        uint16_t* pp = &sm.p[t & 1][w][0][lane * 8];
 #pragma unroll
         for (int s2 = 0; s2 < 2; ++s2)
 #pragma unroll
           for (int j = 0; j < 4; ++j) {
-            const int e = 16 * s2 + 2 * j;
-            const uint32_t lo = (e < e_cap && e >= e_min) ? 0xffffu : 0u;
-            const uint32_t hi = (e + 1 < e_cap && e + 1 >= e_min) ? 0xffff0000u : 0u;
-            pu[s2][j] &= lo | hi;
+            const int i = 8 * s2 + 2 * j;
+            au[s2][j] = pack_bf16x2(
+                __builtin_amdgcn_exp2f(fmaf(x[i], alpha, -rr[i >> 2][i & 3])),
+                __builtin_amdgcn_exp2f(fmaf(x[i + 1], alpha, -rr[(i + 1) >> 2][(i + 1) & 3])));
           }
-      }
-      // hand P to the dK wave of this key block
-      *reinterpret_cast<u32x4*>(pp) = pu[0];
-      *reinterpret_cast<u32x4*>(pp + 8) = pu[1];
-    } else {
-      // dP = dO V^T
-      mfma_chain<NKS, 4, 1>(
-          [&](int f) {
-            return as_bf16x8(*reinterpret_cast<const u32x4*>(&ds[SwzTile<D>::chunk(l32, 2 * f + half)]));
-          },
-          [&](int f, const bf16x8& a) { pacc = mfma32(a, bf[f], f == 0 ? f32x16{} : pacc); });
-    }
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
-    // ---- phase 2
-    if (role == 0) {
-      // dV += P^T dO (dO read transposed)
-      mfma_chain<2 * NCB, 4, 2>(
-          [&](int f) { return tr_frag<D>(ds, lane, 16 * (f & 1), 32 * (f >> 1)); },
-          [&](int f, const bf16x8& bfr) {
-            acc[f >> 1] = mfma32(as_bf16x8(pu[f & 1]), bfr, acc[f >> 1]);
-          });
-    } else {
-      f32x4 dr[4];
+        // Masking is needed only where the step crosses the causal diagonal or
+        // an end of the document (wave-uniform test).  Element e is visible
+        // iff e < lq - qb (a real row), key < lk, and (causal) e >= key - off - qb.
+        const int i0 = cur_i0;
+        const bool need_mask = (i0 + KB_Q > lq) || (kw0 + 32 > lk) ||
+                               (causal && kw0 + 31 > i0 + off);
+        if (need_mask) {
+          const int qb = i0 + 8 * half;
+          const int e_min = causal ? key - off - qb : INT32_MIN;
+          const int e_cap = (key < lk) ? lq - qb : INT32_MIN;
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
-        dr[j] = *reinterpret_cast<const f32x4*>(&sm.delta[buf][16 * (j >> 1) + 8 * half + 4 * (j & 1)]);
-      const u32x4 pu0 = *reinterpret_cast<const u32x4*>(pp);
-      const u32x4 pu1 = *reinterpret_cast<const u32x4*>(pp + 8);
-      // dS = P (dP - D) scale, in the A-operand layout of dK += dS^T Q
-      bf16x8 af[2];
+          for (int s2 = 0; s2 < 2; ++s2)
 #pragma unroll
-      for (int s2 = 0; s2 < 2; ++s2) {
-        const u32x4 pw = s2 ? pu1 : pu0;
-        u32x4 u;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int i = 8 * s2 + 2 * j;
-          const float p0 = bf16_lo(pw[j]), p1 = bf16_hi(pw[j]);
-          u[j] = pack_bf16x2(p0 * fmaf(pacc[i], scale, -dr[i >> 2][i & 3]),
-                             p1 * fmaf(pacc[i + 1], scale, -dr[(i + 1) >> 2][(i + 1) & 3]));
+            for (int j = 0; j < 4; ++j) {
+              const int e = 16 * s2 + 2 * j;
+              const uint32_t lo = (e < e_cap && e >= e_min) ? 0xffffu : 0u;
+              const uint32_t hi = (e + 1 < e_cap && e + 1 >= e_min) ? 0xffff0000u : 0u;
+              au[s2][j] &= lo | hi;
+            }
         }
-        af[s2] = as_bf16x8(u);
+        // hand P to the dK wave of this key block (read one iteration later)
+        *reinterpret_cast<u32x4*>(pp) = au[0];
+        *reinterpret_cast<u32x4*>(pp + 64 * 8) = au[1];
+      } else {
+        // dS = P (dP - D) scale with P of step t - 1 from the dV wave
+        const uint16_t* pp = &sm.p[(t - 1) & 1][w][0][lane * 8];
+        const u32x4 p0 = *reinterpret_cast<const u32x4*>(pp);
+        const u32x4 p1 = *reinterpret_cast<const u32x4*>(pp + 64 * 8);
+#pragma unroll
+        for (int s2 = 0; s2 < 2; ++s2) {
+          const u32x4 pw = s2 ? p1 : p0;
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const int i = 8 * s2 + 2 * j;
+            au[s2][j] = pack_bf16x2(
+                bf16_lo(pw[j]) * fmaf(x[i], alpha, -rr[i >> 2][i & 3]),
+                bf16_hi(pw[j]) * fmaf(x[i + 1], alpha, -rr[(i + 1) >> 2][(i + 1) & 3]));
+          }
+        }
       }
-      // dK += dS^T Q (Q read transposed)
-      mfma_chain<2 * NCB, 4, 3>(
-          [&](int f) { return tr_frag<D>(qs, lane, 16 * (f & 1), 32 * (f >> 1)); },
-          [&](int f, const bf16x8& bfr) { acc[f >> 1] = mfma32(af[f & 1], bfr, acc[f >> 1]); });
+      // dV += P^T dO or dK += dS^T Q (the second operand read transposed)
+      mfma_chain<2 * NCB, 4, 1>(
+          [&](int f) {
+            const uint16_t* tb = tile2 + 16 * D * (f & 1);
+            const s16x4 lo = ds_read_tr16(tb + t_off[f >> 1][0]);
+            const s16x4 hi = ds_read_tr16(tb + t_off[f >> 1][1]);
+            return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+          },
+          [&](int f, const bf16x8& bfr) {
+            acc[f >> 1] = mfma32(as_bf16x8(au[f & 1]), bfr, acc[f >> 1]);
+          });
     }
-    if (t + 1 < n_steps) store_rows(rows, sm.lse2[buf ^ 1], sm.delta[buf ^ 1]);
+    if (t + 1 < n_steps) store_rows(rows, nxt);
     cur_i0 = nxt_i0;
     advance(nxt_i0, nxt_h);
-  };
-
-  if (n_steps > 0) {
-    issue(nxt_i0, nxt_h, sm.q[0], sm.dout[0]);
-    store_rows(fetch_rows(nxt_i0, nxt_h), sm.lse2[0], sm.delta[0]);
-    advance(nxt_i0, nxt_h);
+    cur = nxt;
   }
-  int t = 0;
-  for (; t + 1 < n_steps; t += 2) {
-    step(t, IC<0>{});
-    step(t + 1, IC<1>{});
-  }
-  if (t < n_steps) step(t, IC<0>{});
 
   // epilogue: lane holds column c = 32 cb + l32 of keys 32 w + 8 (v/4) + 4 half + v%4
   uint16_t* outp = role == 0 ? dv : dk;
@@ -477,7 +470,7 @@ attn_bwd_dq_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ 
   auto tile = [&](int kt, auto bufc) {
     constexpr int buf = decltype(bufc)::value;
     const int kv0 = kt * QB_K;
-    __builtin_amdgcn_s_waitcnt(0);
+    __builtin_amdgcn_s_waitcnt(kWaitAll);
     __syncthreads();
     if (kt + 1 < it.count)
       loader.load(kbase, vbase, kv_tok, kv0 + QB_K, lk, sm.k[buf ^ 1], sm.v[buf ^ 1], w, lane);

@@ -119,7 +119,7 @@ attn_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const int kv0 = kt * BK;
     // tile kt has landed in every wave's part of buffer `buf`, and every wave
     // is done with the other buffer (read during tile kt - 1)
-    __builtin_amdgcn_s_waitcnt(0);
+    __builtin_amdgcn_s_waitcnt(kWaitAll);
     __syncthreads();
     if (kt + 1 < it.count)
       loader.load(kbase, vbase, kv_tok, kv0 + BK, lk, sm.k[buf ^ 1], sm.v[buf ^ 1], w, lane);

@@ -180,6 +180,11 @@ struct PairLoader {
   }
 };
 
+// s_waitcnt immediates (gfx9 encoding: vmcnt in bits 3:0 and 15:14, expcnt
+// in 6:4, lgkmcnt in 11:8)
+constexpr int kWaitAll = 0;           // every counter at zero
+constexpr int kWaitLgkm = 0xC07F;     // LDS / scalar memory only; loads in flight may stay
+
 // integral constant for compile-time buffer indices
 template <int V>
 struct IC {
