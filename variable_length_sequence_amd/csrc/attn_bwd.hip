@@ -287,11 +287,29 @@ attn_bwd_dkdv_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
 #pragma unroll
       for (int j = 0; j < 4; ++j)
         rr[j] = *reinterpret_cast<const f32x4*>(&rowv[16 * (j >> 1) + 8 * half + 4 * (j & 1)]);
+      // dK role: P of step t - 1 from the dV wave
+      u32x4 pr[2];
+      if (role == 1) {
+        const uint16_t* pp = &sm.p[(t - 1) & 1][w][0][lane * 8];
+        pr[0] = *reinterpret_cast<const u32x4*>(pp);
+        pr[1] = *reinterpret_cast<const u32x4*>(pp + 64 * 8);
+      }
       // S = Q K^T or dP = dO V^T (rows: queries 16s + 8 half + u; cols: keys)
       f32x16 x;
       mfma_chain<NKS, 4, 0>(
           [&](int f) { return as_bf16x8(*reinterpret_cast<const u32x4*>(tile1 + a_off[f])); },
           [&](int f, const bf16x8& a) { x = mfma32(a, bf[f], f == 0 ? f32x16{} : x); });
+      // B fragments of the second chain (transposed reads), issued now so
+      // their latency hides behind the elementwise middle
+      bf16x8 tb[2 * NCB];
+#pragma unroll
+      for (int f = 0; f < 2 * NCB; ++f) {
+        const uint16_t* tp = tile2 + 16 * D * (f & 1);
+        const s16x4 lo = ds_read_tr16(tp + t_off[f >> 1][0]);
+        const s16x4 hi = ds_read_tr16(tp + t_off[f >> 1][1]);
+        tb[f] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+      }
+      __builtin_amdgcn_sched_barrier(0);
       // element i holds query i0 + 8 half + e, e = 16 (i / 8) + i % 8
       u32x4 au[2];
       if (role == 0) {
@@ -329,13 +347,10 @@ attn_bwd_dkdv_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
         *reinterpret_cast<u32x4*>(pp) = au[0];
         *reinterpret_cast<u32x4*>(pp + 64 * 8) = au[1];
       } else {
-        // dS = P (dP - D) scale with P of step t - 1 from the dV wave
-        const uint16_t* pp = &sm.p[(t - 1) & 1][w][0][lane * 8];
-        const u32x4 p0 = *reinterpret_cast<const u32x4*>(pp);
-        const u32x4 p1 = *reinterpret_cast<const u32x4*>(pp + 64 * 8);
+        // dS = P (dP - D) scale
 #pragma unroll
         for (int s2 = 0; s2 < 2; ++s2) {
-          const u32x4 pw = s2 ? p1 : p0;
+          const u32x4 pw = pr[s2];
 #pragma unroll
           for (int j = 0; j < 4; ++j) {
             const int i = 8 * s2 + 2 * j;
@@ -345,17 +360,10 @@ attn_bwd_dkdv_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
           }
         }
       }
-      // dV += P^T dO or dK += dS^T Q (the second operand read transposed)
-      mfma_chain<2 * NCB, 4, 1>(
-          [&](int f) {
-            const uint16_t* tb = tile2 + 16 * D * (f & 1);
-            const s16x4 lo = ds_read_tr16(tb + t_off[f >> 1][0]);
-            const s16x4 hi = ds_read_tr16(tb + t_off[f >> 1][1]);
-            return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-          },
-          [&](int f, const bf16x8& bfr) {
-            acc[f >> 1] = mfma32(as_bf16x8(au[f & 1]), bfr, acc[f >> 1]);
-          });
+      // dV += P^T dO or dK += dS^T Q
+#pragma unroll
+      for (int f = 0; f < 2 * NCB; ++f)
+        acc[f >> 1] = mfma32(as_bf16x8(au[f & 1]), tb[f], acc[f >> 1]);
     }
     if (t + 1 < n_steps) store_rows(rows, nxt);
     cur_i0 = nxt_i0;
