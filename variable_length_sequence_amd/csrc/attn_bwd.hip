@@ -84,7 +84,8 @@ f32_to_bf16_kernel(const f32x4* __restrict__ src, u32x2* __restrict__ dst, int64
 // A chain of N dependent-accumulator MFMAs whose LDS operand fragment f is
 // read PF fragments ahead of its use; the schedule is pinned to (MFMA, LDS
 // read) pairs so the read latency hides behind the matrix pipe.
-template <int N, int PF, int SYNC, typename Load, typename Mac>
+// RPF is the number of LDS read instructions per fragment.
+template <int N, int PF, int SYNC, int RPF = 1, typename Load, typename Mac>
 __device__ __forceinline__ void mfma_chain(Load load, Mac mac) {
   bf16x8 r[PF];
 #pragma unroll
@@ -95,11 +96,11 @@ __device__ __forceinline__ void mfma_chain(Load load, Mac mac) {
     if (f + PF < N) r[f % PF] = load(f + PF);
     mac(f, a);
   }
-  __builtin_amdgcn_sched_group_barrier(0x100, PF, SYNC);
+  __builtin_amdgcn_sched_group_barrier(0x100, PF * RPF, SYNC);
 #pragma unroll
   for (int f = 0; f < N - PF; ++f) {
     __builtin_amdgcn_sched_group_barrier(0x008, 1, SYNC);
-    __builtin_amdgcn_sched_group_barrier(0x100, 1, SYNC);
+    __builtin_amdgcn_sched_group_barrier(0x100, RPF, SYNC);
   }
   __builtin_amdgcn_sched_group_barrier(0x008, PF, SYNC);
 }
@@ -496,14 +497,18 @@ attn_bwd_dq_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ 
     for (int kb = 0; kb < 2; ++kb) {
       f32x16 sa, da;
       const int prow = kb * 32 + l32;
-#pragma unroll
-      for (int st = 0; st < NKS; ++st) {
-        const int o = SwzTile<D>::chunk(prow, 2 * st + half);
-        sa = mfma32(as_bf16x8(*reinterpret_cast<const u32x4*>(&ks[o])), qf[st],
-                    st == 0 ? f32x16{} : sa);
-        da = mfma32(as_bf16x8(*reinterpret_cast<const u32x4*>(&vs[o])), df[st],
-                    st == 0 ? f32x16{} : da);
-      }
+      // S^T and dP^T chains interleaved; fragment f = (st, K or V), read
+      // four fragments ahead
+      mfma_chain<2 * NKS, 4, 0>(
+          [&](int f) {
+            const uint16_t* t = (f & 1) ? vs : ks;
+            return as_bf16x8(*reinterpret_cast<const u32x4*>(&t[SwzTile<D>::chunk(prow, 2 * (f >> 1) + half)]));
+          },
+          [&](int f, const bf16x8& a) {
+            const int st = f >> 1;
+            if (f & 1) da = mfma32(a, df[st], st == 0 ? f32x16{} : da);
+            else sa = mfma32(a, qf[st], st == 0 ? f32x16{} : sa);
+          });
       // key kv0 + 32 kb + 8 half + e (e = 16 hs + 2 j + e2) is visible iff
       // e <= thr
       const int thr = need_mask ? lim - kv0 - 32 * kb - 8 * half : 64;
@@ -526,14 +531,10 @@ attn_bwd_dq_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ 
       }
     }
 
-    // dQ^T += K^T dS^T
-#pragma unroll
-    for (int cb = 0; cb < NCB; ++cb)
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int hs = 0; hs < 2; ++hs)
-          acc[cb] = mfma32(tr_frag<D>(ks, lane, 32 * kb + 16 * hs, 32 * cb), dsf[kb][hs], acc[cb]);
+    // dQ^T += K^T dS^T; fragment f = (cb, kb, hs), read transposed, two ahead
+    mfma_chain<4 * NCB, 2, 1, 2>(
+        [&](int f) { return tr_frag<D>(ks, lane, 16 * (f & 3), 32 * (f >> 2)); },
+        [&](int f, const bf16x8& a) { acc[f >> 2] = mfma32(a, dsf[(f >> 1) & 1][f & 1], acc[f >> 2]); });
   };
 
   const int n_kv = it.count;

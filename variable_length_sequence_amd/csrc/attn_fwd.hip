@@ -164,6 +164,14 @@ attn_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
       __builtin_amdgcn_sched_group_barrier(0x008, kPf, 0);
     }
 
+    // V^T operand: column c of keys 32 kb + 16 hs + 8 half + t, read
+    // transposed from the row-major V tile; the fragments of the first
+    // 16-key step are requested before the softmax so their latency hides
+    auto vfrag = [&](int cb, int j) { return tr_frag<D>(vs, lane, 16 * j, 32 * cb); };
+    bf16x8 vr[NCB];
+#pragma unroll
+    for (int cb = 0; cb < NCB; ++cb) vr[cb] = vfrag(cb, 0);
+
     if (need_mask) {
       // key kv0 + 32 kb + 8 half + e (e = 16 (i / 8) + i % 8) is visible iff
       // e <= lim - kv0 - 32 kb - 8 half
@@ -214,13 +222,7 @@ attn_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
       }
       return as_bf16x8(u);
     };
-    // V^T operand: column c of keys 32 kb + 16 hs + 8 half + t, read
-    // transposed from the row-major V tile
-    auto vfrag = [&](int cb, int j) { return tr_frag<D>(vs, lane, 16 * j, 32 * cb); };
     bf16x8 pcur = pstep(0);
-    bf16x8 vr[NCB];
-#pragma unroll
-    for (int cb = 0; cb < NCB; ++cb) vr[cb] = vfrag(cb, 0);
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       bf16x8 vn[NCB];
@@ -237,14 +239,17 @@ attn_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
         for (int cb = 0; cb < NCB; ++cb) vr[cb] = vn[cb];
       }
     }
-    // per step: NCB (MFMA, LDS read, ~7 VALU) triples
+    // per MFMA of steps 0-2: the two transposed reads of the matching
+    // fragment of the next step and ~7 VALU of its exponentials
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
 #pragma unroll
       for (int cb = 0; cb < NCB; ++cb) {
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
-        __builtin_amdgcn_sched_group_barrier(0x100, 1, 1);
-        __builtin_amdgcn_sched_group_barrier(0x002, 7, 1);
+        if (j < 3) {
+          __builtin_amdgcn_sched_group_barrier(0x100, 2, 1);
+          __builtin_amdgcn_sched_group_barrier(0x002, 7, 1);
+        }
       }
     }
     l_run += psum;
