@@ -123,6 +123,44 @@ def bench_attention(vl, torch, w, steps, warmup, dev, tensors=None, profile=True
                 tflops=(ffwd + fbwd) / (ms * 1e-3) / 1e12, prof=prof)
 
 
+# kernel -> the sources its code comes from (a counter summary is valid only for
+# the sources it was taken with)
+KERNEL_SOURCES = {
+    "attn_fwd": ["attn_fwd.hip", "common.h", "launch.h"],
+    "bwd_dkdv": ["attn_bwd.hip", "common.h", "launch.h"],
+    "bwd_dq": ["attn_bwd.hip", "common.h", "launch.h"],
+}
+
+
+def sources_sha256(kernel):
+    import hashlib
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES.get(kernel, []):
+        with open(os.path.join(ROOT, "variable_length_sequence_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def measured_traffic(kernel, workload):
+    """HBM bytes per launch from the committed counter summary, or None when
+    there is none or the kernel's sources changed since it was taken."""
+    path = os.path.join(ROOT, "profiles", f"{kernel}_{workload}_hbm_traffic.txt")
+    if not os.path.exists(path):
+        return None
+    kv = {}
+    with open(path) as fh:
+        for line in fh:
+            if ":" in line and not line.startswith("#"):
+                key, val = line.split(":", 1)
+                kv[key.strip()] = val.strip()
+    if kv.get("sources_sha256") != sources_sha256(kernel):
+        return None
+    try:
+        return int(kv["traffic_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
 def attn_kernel_flops(pairs, hq, d):
     # algorithmic FLOPs each kernel must do per launch (per visible pair):
     # forward QK^T and PV; dK/dV kernel S, dP, dV, dK; dQ kernel only dQ
@@ -264,7 +302,8 @@ def main():
         "useful_tflop_per_step": round((r["flops_fwd"] + r["flops_bwd"]) / 1e12, 4),
         "roofline": {"bound": "mfma", "kernel": dom, "achieved": round(achieved, 2),
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                     "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                     "traffic": measured_traffic(dom, w.name),
                      "flops_per_launch": kflops[dom], "avg_launch_ms": round(dom_avg, 5)},
         "kernels": ktab,
     }
