@@ -37,8 +37,8 @@ PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 def _args():
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-extra", action="store_true", help="skip the other workloads")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-mib", type=int, default=0,
@@ -110,9 +110,13 @@ def bench_attention(vl, torch, w, steps, warmup, dev, tensors=None, profile=True
         step()
     if profile:
         vl.profile_enable(True)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
     with Timer(torch) as tm:
-        for _ in range(steps):
+        ev[0].record()
+        for i in range(steps):
             step()
+            ev[i + 1].record()
+    per_step = sorted(ev[i].elapsed_time(ev[i + 1]) for i in range(steps))
     prof = vl.profile_read() if profile else {}
     if profile:
         vl.profile_enable(False)
@@ -120,7 +124,8 @@ def bench_attention(vl, torch, w, steps, warmup, dev, tensors=None, profile=True
     ms = tm.wall_ms / steps
     del q, k, v, do
     return dict(ms=ms, event_ms=tm.event_ms / steps, pairs=pairs, flops_fwd=ffwd, flops_bwd=fbwd,
-                tflops=(ffwd + fbwd) / (ms * 1e-3) / 1e12, prof=prof)
+                tflops=(ffwd + fbwd) / (ms * 1e-3) / 1e12, prof=prof,
+                median_ms=per_step[len(per_step) // 2], min_ms=per_step[0])
 
 
 # kernel -> the sources its code comes from (a counter summary is valid only for
@@ -192,6 +197,33 @@ def cpu_baseline(w):
             "host_cpus": os.cpu_count(), "affinity": len(os.sched_getaffinity(0)),
             "sample": f"full {w.name} batch, fp64 numpy forward + backward "
                       f"(O, LSE, dQ, dK, dV) of all {len(w.lengths)} documents x {w.hq} heads"}
+
+
+def measured_gemm_peak(torch, dev, n=8192, reps=20):
+    """bf16 GEMM throughput of the vendor library (hipBLASLt via torch.matmul) on
+    one n x n x n product: a measured stand-in for the reachable MFMA peak."""
+    a = torch.randn(n, n, device=dev, dtype=torch.bfloat16)
+    b = torch.randn(n, n, device=dev, dtype=torch.bfloat16)
+    for _ in range(3):
+        torch.matmul(a, b)
+    with Timer(torch) as tm:
+        for _ in range(reps):
+            torch.matmul(a, b)
+    del a, b
+    return round(2 * n ** 3 * reps / (tm.event_ms * 1e-3) / 1e12, 1)
+
+
+def measured_copy_gbs(torch, dev, nbytes, reps=10):
+    """Device-to-device copy of nbytes (read + write counted): the reference for
+    the bandwidth-bound kernels."""
+    src = torch.empty(nbytes // 2, dtype=torch.bfloat16, device=dev).fill_(1)
+    dst = [torch.empty_like(src) for _ in range(2)]
+    dst[0].copy_(src)
+    with Timer(torch) as tm:
+        for i in range(reps):
+            dst[i % 2].copy_(src)
+    del src, dst
+    return round(2 * nbytes * reps / (tm.event_ms * 1e-3) / 1e9, 1)
 
 
 def bench_permute(vl, torch, dev, steps):
@@ -299,6 +331,8 @@ def main():
                    "head_dim": w.d, "causal": True, "length_seed": 0,
                    "lengths": "lognormal(median 512, sigma 1.2) clipped [64, 8192]"},
         "pct_mfma_peak": round(100 * r["tflops"] / PEAK_BF16_TFLOPS, 2),
+        "step_ms_median": round(r["median_ms"], 4),
+        "step_ms_min": round(r["min_ms"], 4),
         "useful_tflop_per_step": round((r["flops_fwd"] + r["flops_bwd"]) / 1e12, 4),
         "roofline": {"bound": "mfma", "kernel": dom, "achieved": round(achieved, 2),
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
@@ -313,7 +347,11 @@ def main():
         extra = {}
         print("[bench] permute", file=sys.stderr, flush=True)
         prof, by = bench_permute(vl, torch, dev, 10)
-        extra["ulysses_permute_49152x32x128_P8"] = kernel_table(prof, {}, by)
+        perm = kernel_table(prof, {}, by)
+        perm["device_copy_same_bytes_gbs"] = measured_copy_gbs(torch, dev, by["sp_seq2head"] // 2)
+        extra["ulysses_permute_49152x32x128_P8"] = perm
+        print("[bench] measured GEMM peak", file=sys.stderr, flush=True)
+        extra["measured_bf16_gemm_tflops"] = measured_gemm_peak(torch, dev)
         print("[bench] ring share", file=sys.stderr, flush=True)
         extra["ring_256k_chunk7"] = bench_ring(vl, torch, dev, 2)
         torch.cuda.empty_cache()
