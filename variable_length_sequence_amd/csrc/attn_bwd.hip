@@ -8,7 +8,8 @@
 //   dV_j = sum_i P_ij dO_i,  dK_j = scale sum_i dS_ij Q_i,  dQ_i = scale sum_j dS_ij K_j.
 //
 // Three kernels, no atomics on dQ:
-//   1. bwd_pre: D = rowsum(dO * O) in fp32, [Hq, T].
+//   1. bwd_pre: D = rowsum(dO * O) in fp32, [Hq, T]; clears the fp32 dK/dV
+//      accumulator when kernel 2 uses it.
 //   2. dkdv: one workgroup per (128-key tile of a document, kv head[, slice of
 //      its q heads]); each wave owns 32 keys and keeps their K, V operands and
 //      fp32 dK, dV accumulators in registers while 32-row query tiles of every
@@ -35,10 +36,16 @@ namespace {
 constexpr int kThreads = 256;
 
 // ---------------------------------------------------------------- D = rowsum(dO O)
+// It also clears the fp32 dK/dV accumulator (acc_n4 float4s; 0 when the
+// dK/dV kernel writes its results directly).
 template <int D>
 __global__ void __launch_bounds__(kThreads)
 bwd_pre_kernel(const uint16_t* __restrict__ o, const uint16_t* __restrict__ dout,
-               float* __restrict__ delta, int64_t total_q, int hq) {
+               float* __restrict__ delta, int64_t total_q, int hq, f32x4* __restrict__ dkv_acc,
+               int64_t acc_n4) {
+  for (int64_t i = int64_t(blockIdx.x) * kThreads + threadIdx.x; i < acc_n4;
+       i += int64_t(gridDim.x) * kThreads)
+    dkv_acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
   constexpr int LPR = D / 8;                 // lanes per (row, head)
   constexpr int RPB = kThreads / LPR;        // rows per block
   const int sub = threadIdx.x / LPR;
@@ -62,13 +69,6 @@ bwd_pre_kernel(const uint16_t* __restrict__ o, const uint16_t* __restrict__ dout
       delta[int64_t(h) * total_q + t] = acc;
     }
   }
-}
-
-__global__ void __launch_bounds__(kThreads)
-fill_zero_kernel(f32x4* __restrict__ p, int64_t n4) {
-  for (int64_t i = int64_t(blockIdx.x) * kThreads + threadIdx.x; i < n4;
-       i += int64_t(gridDim.x) * kThreads)
-    p[i] = f32x4{0.f, 0.f, 0.f, 0.f};
 }
 
 // fp32 [T, H, D] accumulator -> bf16
@@ -237,7 +237,7 @@ attn_bwd_dkdv_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
   // (wave 0) and D (wave 1) values of a step go through registers and are
   // scaled when stored, so their load latency hides behind the step's
   // compute.  Rows past the document repeat its last row (P is masked there).
-  auto issue = [&](int i0, int h, uint16_t* dq_, uint16_t* dd_) {
+  auto issue = [&](int i0, int h, uint32_t dq_, uint32_t dd_) {
     const int64_t ho = int64_t(h) * D;
     loader.load(qdoc + ho, ddoc + ho, q_tok, i0, lq, dq_, dd_, wave, lane);
   };
@@ -261,7 +261,7 @@ attn_bwd_dkdv_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
   int prv_i0 = i_begin;                        // step t - 1 (unused by the dK role)
   (void)prv_i0;
   if (n_steps > 0) {
-    issue(nxt_i0, nxt_h, sm.q[0], sm.dout[0]);
+    issue(nxt_i0, nxt_h, lds_addr(sm.q[0]), lds_addr(sm.dout[0]));
     store_rows(fetch_rows(nxt_i0, nxt_h), 0);
     advance(nxt_i0, nxt_h);
   }
@@ -274,7 +274,8 @@ attn_bwd_dkdv_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
     __syncthreads();
     float rows = 0.f;
     if (t + 1 < n_steps) {
-      issue(nxt_i0, nxt_h, sm.q[nxt], sm.dout[nxt]);
+      issue(nxt_i0, nxt_h, lds_addr(sm.q[0]) + uint32_t(nxt) * (KB_Q * D * 2),
+            lds_addr(sm.dout[0]) + uint32_t(nxt) * (KB_Q * D * 2));
       rows = fetch_rows(nxt_i0, nxt_h);
     }
     const int st = t - role;                   // this wave's step
@@ -482,7 +483,8 @@ attn_bwd_dq_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ 
     __builtin_amdgcn_s_waitcnt(kWaitAll);
     __syncthreads();
     if (kt + 1 < it.count)
-      loader.load(kbase, vbase, kv_tok, kv0 + QB_K, lk, sm.k[buf ^ 1], sm.v[buf ^ 1], w, lane);
+      loader.load(kbase, vbase, kv_tok, kv0 + QB_K, lk, lds_addr(sm.k[buf ^ 1]),
+                  lds_addr(sm.v[buf ^ 1]), w, lane);
     const uint16_t* ks = sm.k[buf];
     const uint16_t* vs = sm.v[buf];
 
@@ -538,7 +540,8 @@ attn_bwd_dq_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ 
   };
 
   const int n_kv = it.count;
-  if (n_kv > 0) loader.load(kbase, vbase, kv_tok, 0, lk, sm.k[0], sm.v[0], w, lane);
+  if (n_kv > 0)
+    loader.load(kbase, vbase, kv_tok, 0, lk, lds_addr(sm.k[0]), lds_addr(sm.v[0]), w, lane);
   int kt = 0;
   for (; kt + 1 < n_kv; kt += 2) {
     tile(kt, IC<0>{});
@@ -575,22 +578,15 @@ hipError_t run_bwd(const AttnShape& s, const uint16_t* q, const uint16_t* k, con
                    int32_t head_split, uint16_t* dq, uint16_t* dk, uint16_t* dv, float* delta,
                    float* dkv_acc, hipStream_t stream) {
   const int n_cu = device_cus();
-  {
+  const int64_t kv_elems = s.total_k * s.hkv * D;
+  const int64_t acc_n4 = head_split > 1 ? 2 * kv_elems / 4 : 0;
+  if (s.total_q > 0 || acc_n4 > 0) {
     constexpr int RPB = kThreads / (D / 8);
-    const int64_t want = (s.total_q * s.hq + RPB - 1) / RPB;
+    const int64_t want = std::max((s.total_q * s.hq + RPB - 1) / RPB, (acc_n4 + kThreads - 1) / kThreads);
     const int blocks = int(std::max<int64_t>(1, std::min<int64_t>(want, int64_t(n_cu) * 16)));
     ProfScope prof("bwd_pre", stream);
-    if (s.total_q > 0)
-      hipLaunchKernelGGL((bwd_pre_kernel<D>), dim3(blocks), dim3(kThreads), 0, stream, o, dout,
-                         delta, s.total_q, s.hq);
-  }
-  const int64_t kv_elems = s.total_k * s.hkv * D;
-  if (head_split > 1 && kv_elems > 0) {
-    const int64_t n4 = 2 * kv_elems / 4;
-    const int blocks = int(std::min<int64_t>((n4 + kThreads - 1) / kThreads, int64_t(n_cu) * 16));
-    ProfScope prof("bwd_dkv_zero", stream);
-    hipLaunchKernelGGL(fill_zero_kernel, dim3(blocks), dim3(kThreads), 0, stream,
-                       reinterpret_cast<f32x4*>(dkv_acc), n4);
+    hipLaunchKernelGGL((bwd_pre_kernel<D>), dim3(blocks), dim3(kThreads), 0, stream, o, dout,
+                       delta, s.total_q, s.hq, reinterpret_cast<f32x4*>(dkv_acc), acc_n4);
   }
   if (n_bwd > 0) {
     const int groups = (n_bwd + 7) / 8;

@@ -122,7 +122,8 @@ attn_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     __builtin_amdgcn_s_waitcnt(kWaitAll);
     __syncthreads();
     if (kt + 1 < it.count)
-      loader.load(kbase, vbase, kv_tok, kv0 + BK, lk, sm.k[buf ^ 1], sm.v[buf ^ 1], w, lane);
+      loader.load(kbase, vbase, kv_tok, kv0 + BK, lk, lds_addr(sm.k[buf ^ 1]),
+                  lds_addr(sm.v[buf ^ 1]), w, lane);
     const uint16_t* ks = sm.k[buf];
     const uint16_t* vs = sm.v[buf];
 
@@ -256,7 +257,8 @@ attn_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
   };
 
   const int n_kv = it.count;
-  if (n_kv > 0) loader.load(kbase, vbase, kv_tok, 0, lk, sm.k[0], sm.v[0], w, lane);
+  if (n_kv > 0)
+    loader.load(kbase, vbase, kv_tok, 0, lk, lds_addr(sm.k[0]), lds_addr(sm.v[0]), w, lane);
   int kt = 0;
   for (; kt + 1 < n_kv; kt += 2) {
     tile(kt, IC<0>{});

@@ -94,18 +94,31 @@ __device__ __forceinline__ bf16x8 tr_frag(const uint16_t* tile, int lane, int r0
   return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
 }
 
+// Byte address of an LDS object (the 32-bit LDS address space).
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return static_cast<uint32_t>(
+      reinterpret_cast<uintptr_t>((const __attribute__((address_space(3))) void*)p));
+}
+
 // Direct global -> LDS copy of 16 bytes per lane: lane i reads sbase + voff
-// (sbase wave-uniform, voff its own byte offset) and its bytes land at
-// lds_base + 16 i (lds_base wave-uniform).  The copy is issued from inline
+// (sbase wave-uniform, voff its own byte offset) and its bytes land at LDS
+// byte address lds + 16 i (lds wave-uniform).  The copy is issued from inline
 // assembly so that the compiler does not track its LDS write: it cannot tell
 // the buffers of a multi-buffered tile apart and would otherwise make every
 // transpose read wait for all copies in flight, which serialises the prefetch
 // of the next tile with the current one.  Callers order the copy against
 // reads of its destination themselves (s_waitcnt on vmcnt followed by a
 // workgroup barrier before the first read).
-__device__ __forceinline__ void load_lds16(const void* sbase, uint32_t voff, uint16_t* lds_base) {
-  const uint32_t m0 = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(
-      (__attribute__((address_space(3))) uint16_t*)lds_base));
+__device__ __forceinline__ void load_lds16(const void* sbase, uint32_t voff, uint32_t lds) {
+  // both bases are wave-uniform; readfirstlane keeps them in scalar registers
+  // even where the compiler cannot prove it
+  // (readfirstlane returns int: each half goes back through uint32_t so the
+  // low half is zero-extended, not sign-extended, into the 64-bit address)
+  const uint64_t a = reinterpret_cast<uint64_t>(sbase);
+  const uint32_t lo = uint32_t(__builtin_amdgcn_readfirstlane(int(uint32_t(a))));
+  const uint32_t hi = uint32_t(__builtin_amdgcn_readfirstlane(int(uint32_t(a >> 32))));
+  sbase = reinterpret_cast<const void*>(uint64_t(lo) | (uint64_t(hi) << 32));
+  const uint32_t m0 = uint32_t(__builtin_amdgcn_readfirstlane(int(lds)));
   asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
                :
                : "v"(voff), "s"(sbase), "s"(m0)
@@ -146,31 +159,31 @@ struct PairLoader {
       voff[u] = uint32_t(src_row(u, wave, lane)) * row_bytes + col_bytes(u, wave, lane);
   }
   // a, b: first row of the tile in each tensor (wave-uniform)
-  __device__ __forceinline__ void issue(const uint16_t* a, const uint16_t* b, uint16_t* da,
-                                        uint16_t* db, int wave) const {
+  __device__ __forceinline__ void issue(const uint16_t* a, const uint16_t* b, uint32_t da,
+                                        uint32_t db, int wave) const {
 #pragma unroll
     for (int u = 0; u < N; ++u) {
       if (!has(u, wave)) continue;
-      load_lds16(a, voff[u], da + (u * NW + wave) * 512);
-      load_lds16(b, voff[u], db + (u * NW + wave) * 512);
+      load_lds16(a, voff[u], da + (u * NW + wave) * 1024);
+      load_lds16(b, voff[u], db + (u * NW + wave) * 1024);
     }
   }
-  __device__ __forceinline__ void issue_clamped(const uint16_t* a, const uint16_t* b, uint16_t* da,
-                                                uint16_t* db, int wave, int lane, int n_valid,
+  __device__ __forceinline__ void issue_clamped(const uint16_t* a, const uint16_t* b, uint32_t da,
+                                                uint32_t db, int wave, int lane, int n_valid,
                                                 uint32_t row_bytes) const {
 #pragma unroll
     for (int u = 0; u < N; ++u) {
       if (!has(u, wave)) continue;
       const uint32_t o = uint32_t(min(src_row(u, wave, lane), n_valid - 1)) * row_bytes +
                          col_bytes(u, wave, lane);
-      load_lds16(a, o, da + (u * NW + wave) * 512);
-      load_lds16(b, o, db + (u * NW + wave) * 512);
+      load_lds16(a, o, da + (u * NW + wave) * 1024);
+      load_lds16(b, o, db + (u * NW + wave) * 1024);
     }
   }
   // tile of rows row0 .. row0 + ROWS - 1 of a document with n_rows rows;
   // a, b point at the document's first row
   __device__ __forceinline__ void load(const uint16_t* a, const uint16_t* b, int64_t row_elems,
-                                       int row0, int n_rows, uint16_t* da, uint16_t* db, int wave,
+                                       int row0, int n_rows, uint32_t da, uint32_t db, int wave,
                                        int lane) const {
     const int64_t o = int64_t(row0) * row_elems;
     if (row0 + ROWS <= n_rows)
