@@ -29,10 +29,13 @@ int hip_fail(hipError_t e, const char* what) {
 
 // ------------------------------------------------------------ work-list cache
 struct Plan {
-  vl::DevItem* dev = nullptr;
+  vl::DevItem* dev = nullptr;   // one allocation: the items, then their XCD slots
+  int32_t* slot = nullptr;
   int32_t n = 0;
+  int32_t rows = 0;             // items of the longest XCD list
   int32_t max_count = 0;
   int64_t total_count = 0;
+  vl::ItemMap map() const { return vl::ItemMap{dev, slot, rows}; }
 };
 
 std::mutex g_mu;
@@ -73,8 +76,11 @@ int get_plan(int pass, int causal, const int32_t* cu_q, const int32_t* cu_k, int
       pass == 0 ? vl::fwd_items(docs, causal != 0, vl::kFwdBQ, vl::kFwdBK)
                 : vl::bwd_items(docs, causal != 0, vl::kBwdBQ, vl::kBwdBK);
   const std::vector<vl::DevItem> di = vl::device_items(docs, items);
+  int32_t rows = 0;
+  const std::vector<int32_t> slots = vl::xcd_slots(items, vl::kXcds, rows);
   Plan p;
   p.n = int32_t(di.size());
+  p.rows = rows;
   for (const auto& it : items) {
     p.max_count = std::max(p.max_count, it.count);
     p.total_count += it.count;
@@ -85,13 +91,18 @@ int get_plan(int pass, int causal, const int32_t* cu_q, const int32_t* cu_k, int
       (void)hipDeviceSynchronize();
       clear_plans_locked();
     }
-    e = hipMalloc(&p.dev, di.size() * sizeof(vl::DevItem));
+    const size_t b_items = di.size() * sizeof(vl::DevItem);
+    std::vector<char> host(b_items + slots.size() * sizeof(int32_t));
+    std::memcpy(host.data(), di.data(), b_items);
+    std::memcpy(host.data() + b_items, slots.data(), slots.size() * sizeof(int32_t));
+    e = hipMalloc(&p.dev, host.size());
     if (e != hipSuccess) return hip_fail(e, "hipMalloc(work list)");
-    e = hipMemcpy(p.dev, di.data(), di.size() * sizeof(vl::DevItem), hipMemcpyHostToDevice);
+    e = hipMemcpy(p.dev, host.data(), host.size(), hipMemcpyHostToDevice);
     if (e != hipSuccess) {
       (void)hipFree(p.dev);
       return hip_fail(e, "hipMemcpy(work list)");
     }
+    p.slot = reinterpret_cast<int32_t*>(reinterpret_cast<char*>(p.dev) + b_items);
   }
   g_plans.emplace(key, p);
   out = p;
@@ -155,7 +166,7 @@ int varlen_attn_fwd(const void* q, const void* k, const void* v, const int32_t* 
     if (rc) return rc;
     vl::AttnShape s{total_q, total_k, n_heads_q, n_heads_kv, head_dim,
                     resolve_scale(softmax_scale, head_dim), causal != 0};
-    hipError_t e = vl::launch_attn_fwd(s, q, k, v, p.dev, p.n, out_dtype, out, lse,
+    hipError_t e = vl::launch_attn_fwd(s, q, k, v, p.map(), out_dtype, out, lse,
                                        reinterpret_cast<hipStream_t>(stream));
     if (e != hipSuccess) return hip_fail(e, "attn_fwd launch");
     return VL_OK;
@@ -221,8 +232,8 @@ int varlen_attn_bwd(const void* q, const void* k, const void* v, const void* out
                                               align256(size_t(total_q) * size_t(n_heads_q) * 4));
     vl::AttnShape s{total_q, total_k, n_heads_q, n_heads_kv, head_dim,
                     resolve_scale(softmax_scale, head_dim), causal != 0};
-    hipError_t e = vl::launch_attn_bwd(s, q, k, v, out, dout, lse, pf.dev, pf.n, pb.dev, pb.n,
-                                       split, dq, dk, dv, delta, dkv_acc, st);
+    hipError_t e = vl::launch_attn_bwd(s, q, k, v, out, dout, lse, pf.map(), pb.map(), split, dq,
+                                       dk, dv, delta, dkv_acc, st);
     if (e != hipSuccess) return hip_fail(e, "attn_bwd launch");
     return VL_OK;
   } catch (const std::exception& ex) {

@@ -140,22 +140,23 @@ __global__ void __launch_bounds__(kKvThreads)
 attn_bwd_dkdv_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
                      const uint16_t* __restrict__ v, const uint16_t* __restrict__ dout,
                      const float* __restrict__ lse, const float* __restrict__ delta,
-                     const DevItem* __restrict__ items, int n_items, int hq, int hkv,
-                     int head_split, float scale, int causal, int64_t total_q,
+                     const DevItem* __restrict__ items, const int32_t* __restrict__ slot,
+                     int hq, int hkv, int head_split, float scale, int causal, int64_t total_q,
                      uint16_t* __restrict__ dk, uint16_t* __restrict__ dv,
                      float* __restrict__ dkv_acc, int64_t total_k) {
   constexpr int NKS = D / 16;
   constexpr int NCB = D / 32;
   __shared__ KvSmem<D> sm;
 
+  // workgroup -> (item, kv head, q-head slice) on XCD b % 8's item list
   const int b = blockIdx.x;
-  const int xcd = b & 7;
-  const int r = b >> 3;
+  const int xcd = b & (kXcds - 1);
+  const int r = b / kXcds;
   const int per_item = hkv * head_split;
-  const int item_idx = (r / per_item) * 8 + xcd;
+  const int item_idx = slot[(r / per_item) * kXcds + xcd];
   const int g = (r % per_item) / head_split;
   const int split = r % head_split;
-  if (item_idx >= n_items) return;
+  if (item_idx < 0) return;
   const DevItem it = items[item_idx];
 
   const int tid = threadIdx.x;
@@ -410,18 +411,18 @@ __global__ void __launch_bounds__(kThreads, 2)
 attn_bwd_dq_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
                    const uint16_t* __restrict__ v, const uint16_t* __restrict__ dout,
                    const float* __restrict__ lse, const float* __restrict__ delta,
-                   const DevItem* __restrict__ items, int n_items, int hq, int hkv, float scale,
-                   int causal, int64_t total_q, uint16_t* __restrict__ dq) {
+                   const DevItem* __restrict__ items, const int32_t* __restrict__ slot, int hq,
+                   int hkv, float scale, int causal, int64_t total_q, uint16_t* __restrict__ dq) {
   constexpr int NKS = D / 16;
   constexpr int NCB = D / 32;
   __shared__ QSmem<D> sm;
 
   const int b = blockIdx.x;
-  const int xcd = b & 7;
-  const int r = b >> 3;
-  const int item_idx = (r / hq) * 8 + xcd;
+  const int xcd = b & (kXcds - 1);
+  const int r = b / kXcds;
+  const int item_idx = slot[(r / hq) * kXcds + xcd];
   const int h = r % hq;
-  if (item_idx >= n_items) return;
+  if (item_idx < 0) return;
   const DevItem it = items[item_idx];
   const int g = h / (hq / hkv);
 
@@ -574,9 +575,9 @@ int device_cus() {
 template <int D>
 hipError_t run_bwd(const AttnShape& s, const uint16_t* q, const uint16_t* k, const uint16_t* v,
                    const uint16_t* o, const uint16_t* dout, const float* lse,
-                   const DevItem* fwd_list, int32_t n_fwd, const DevItem* bwd_list, int32_t n_bwd,
-                   int32_t head_split, uint16_t* dq, uint16_t* dk, uint16_t* dv, float* delta,
-                   float* dkv_acc, hipStream_t stream) {
+                   const ItemMap& fwd_map, const ItemMap& bwd_map, int32_t head_split,
+                   uint16_t* dq, uint16_t* dk, uint16_t* dv, float* delta, float* dkv_acc,
+                   hipStream_t stream) {
   const int n_cu = device_cus();
   const int64_t kv_elems = s.total_k * s.hkv * D;
   const int64_t acc_n4 = head_split > 1 ? 2 * kv_elems / 4 : 0;
@@ -588,13 +589,12 @@ hipError_t run_bwd(const AttnShape& s, const uint16_t* q, const uint16_t* k, con
     hipLaunchKernelGGL((bwd_pre_kernel<D>), dim3(blocks), dim3(kThreads), 0, stream, o, dout,
                        delta, s.total_q, s.hq, reinterpret_cast<f32x4*>(dkv_acc), acc_n4);
   }
-  if (n_bwd > 0) {
-    const int groups = (n_bwd + 7) / 8;
-    const dim3 grid(unsigned(groups) * 8u * unsigned(s.hkv * head_split));
+  if (bwd_map.rows > 0) {
+    const dim3 grid(unsigned(bwd_map.rows) * unsigned(kXcds) * unsigned(s.hkv * head_split));
     ProfScope prof("bwd_dkdv", stream);
     hipLaunchKernelGGL((attn_bwd_dkdv_kernel<D>), grid, dim3(kKvThreads), 0, stream, q, k, v, dout,
-                       lse, delta, bwd_list, n_bwd, s.hq, s.hkv, head_split, s.scale, s.causal,
-                       s.total_q, dk, dv, dkv_acc, s.total_k);
+                       lse, delta, bwd_map.items, bwd_map.slot, s.hq, s.hkv, head_split, s.scale,
+                       s.causal, s.total_q, dk, dv, dkv_acc, s.total_k);
   }
   if (head_split > 1 && kv_elems > 0) {
     const int64_t n4 = kv_elems / 4;
@@ -606,12 +606,12 @@ hipError_t run_bwd(const AttnShape& s, const uint16_t* q, const uint16_t* k, con
                        reinterpret_cast<const f32x4*>(dkv_acc + kv_elems),
                        reinterpret_cast<u32x2*>(dv), n4);
   }
-  if (n_fwd > 0) {
-    const int groups = (n_fwd + 7) / 8;
-    const dim3 grid(unsigned(groups) * 8u * unsigned(s.hq));
+  if (fwd_map.rows > 0) {
+    const dim3 grid(unsigned(fwd_map.rows) * unsigned(kXcds) * unsigned(s.hq));
     ProfScope prof("bwd_dq", stream);
     hipLaunchKernelGGL((attn_bwd_dq_kernel<D>), grid, dim3(kThreads), 0, stream, q, k, v, dout, lse,
-                       delta, fwd_list, n_fwd, s.hq, s.hkv, s.scale, s.causal, s.total_q, dq);
+                       delta, fwd_map.items, fwd_map.slot, s.hq, s.hkv, s.scale, s.causal,
+                       s.total_q, dq);
   }
   return hipGetLastError();
 }
@@ -620,9 +620,9 @@ hipError_t run_bwd(const AttnShape& s, const uint16_t* q, const uint16_t* k, con
 
 hipError_t launch_attn_bwd(const AttnShape& s, const void* q, const void* k, const void* v,
                            const void* o, const void* dout, const float* lse,
-                           const DevItem* fwd_list, int32_t n_fwd, const DevItem* bwd_list,
-                           int32_t n_bwd, int32_t head_split, void* dq, void* dk, void* dv,
-                           float* delta, float* dkv_acc, hipStream_t stream) {
+                           const ItemMap& fwd_map, const ItemMap& bwd_map, int32_t head_split,
+                           void* dq, void* dk, void* dv, float* delta, float* dkv_acc,
+                           hipStream_t stream) {
   auto* Q = reinterpret_cast<const uint16_t*>(q);
   auto* K = reinterpret_cast<const uint16_t*>(k);
   auto* V = reinterpret_cast<const uint16_t*>(v);
@@ -632,10 +632,10 @@ hipError_t launch_attn_bwd(const AttnShape& s, const void* q, const void* k, con
   auto* DK = reinterpret_cast<uint16_t*>(dk);
   auto* DV = reinterpret_cast<uint16_t*>(dv);
   if (s.d == 128)
-    return run_bwd<128>(s, Q, K, V, O, DO, lse, fwd_list, n_fwd, bwd_list, n_bwd, head_split, DQ,
-                        DK, DV, delta, dkv_acc, stream);
-  return run_bwd<64>(s, Q, K, V, O, DO, lse, fwd_list, n_fwd, bwd_list, n_bwd, head_split, DQ, DK,
-                     DV, delta, dkv_acc, stream);
+    return run_bwd<128>(s, Q, K, V, O, DO, lse, fwd_map, bwd_map, head_split, DQ, DK, DV, delta,
+                        dkv_acc, stream);
+  return run_bwd<64>(s, Q, K, V, O, DO, lse, fwd_map, bwd_map, head_split, DQ, DK, DV, delta,
+                     dkv_acc, stream);
 }
 
 }  // namespace vl

@@ -52,21 +52,22 @@ struct FwdSmem {
 template <int D, bool F32OUT>
 __global__ void __launch_bounds__(kThreads, 2)
 attn_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
-                const uint16_t* __restrict__ v, const DevItem* __restrict__ items, int n_items,
-                int hq, int hkv, float scale, int causal, void* __restrict__ out,
+                const uint16_t* __restrict__ v, const DevItem* __restrict__ items,
+                const int32_t* __restrict__ slot, int hq, int hkv, float scale, int causal,
+                void* __restrict__ out,
                 float* __restrict__ lse, int64_t total_q) {
   constexpr int NKS = D / 16;  // k-steps over the head dim
   constexpr int NCB = D / 32;  // 32-wide blocks of the head dim
   __shared__ FwdSmem<D> sm;
 
-  // workgroup -> (item, head): the 8 XCDs take items round-robin, and all
-  // heads of one item stay on one XCD
+  // workgroup -> (item, head): XCD b % 8 runs its own item list, longest
+  // first, and all heads of one item stay on that XCD (shared K/V in its L2)
   const int b = blockIdx.x;
-  const int xcd = b & 7;
-  const int r = b >> 3;
-  const int item_idx = (r / hq) * 8 + xcd;
+  const int xcd = b & (kXcds - 1);
+  const int r = b / kXcds;
+  const int item_idx = slot[(r / hq) * kXcds + xcd];
   const int h = r % hq;
-  if (item_idx >= n_items) return;
+  if (item_idx < 0) return;
   const DevItem it = items[item_idx];
   const int g = h / (hq / hkv);
 
@@ -131,129 +132,140 @@ attn_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const bool wave_live = (wq_first < lq) && (!causal || kv0 <= wq_last + off);
     if (!wave_live) return;
     const bool need_mask = (kv0 + BK > lk) || (causal && kv0 + BK - 1 > wq_first + off);
-    // S^T for the two 32-key halves of the tile.  K fragments are read from
-    // LDS kPf steps ahead of the MFMA that consumes them, and the schedule is
-    // pinned to (1 MFMA, 1 LDS read) pairs so the read latency hides behind
-    // the matrix pipe.
-    f32x16 s[2];
+    // key kv0 + 32 kb + 8 half + e (e = 16 (i / 8) + i % 8) of S^T half kb
+    // is visible iff e <= lim - kv0 - 32 kb - 8 half
+    const int lim = causal ? min(lk - 1, qrow + off) : lk - 1;
+    auto mask = [&](f32x16& x, int kb) {
+      const int thr = lim - kv0 - 32 * kb - 8 * half;
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) s[kb][i] = 0.f;
-    {
-      constexpr int NF = 2 * NKS;
-      constexpr int kPf = 4;
-      auto kfrag = [&](int f) {
-        return as_bf16x8(*reinterpret_cast<const u32x4*>(
-            &ks[SwzTile<D>::chunk((f / NKS) * 32 + l32, 2 * (f % NKS) + half)]));
-      };
-      bf16x8 kr[kPf];
-#pragma unroll
-      for (int f = 0; f < kPf; ++f) kr[f] = kfrag(f);
-#pragma unroll
-      for (int f = 0; f < NF; ++f) {
-        const bf16x8 a = kr[f % kPf];
-        if (f + kPf < NF) kr[f % kPf] = kfrag(f + kPf);
-        s[f / NKS] = mfma32(a, qf[f % NKS], s[f / NKS]);
-      }
-      __builtin_amdgcn_sched_group_barrier(0x100, kPf, 0);
-#pragma unroll
-      for (int f = 0; f < NF - kPf; ++f) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-      }
-      __builtin_amdgcn_sched_group_barrier(0x008, kPf, 0);
-    }
-
-    // V^T operand: column c of keys 32 kb + 16 hs + 8 half + t, read
-    // transposed from the row-major V tile; the fragments of the first
-    // 16-key step are requested before the softmax so their latency hides
-    auto vfrag = [&](int cb, int j) { return tr_frag<D>(vs, lane, 16 * j, 32 * cb); };
-    bf16x8 vr[NCB];
-#pragma unroll
-    for (int cb = 0; cb < NCB; ++cb) vr[cb] = vfrag(cb, 0);
-
-    if (need_mask) {
-      // key kv0 + 32 kb + 8 half + e (e = 16 (i / 8) + i % 8) is visible iff
-      // e <= lim - kv0 - 32 kb - 8 half
-      const int lim = causal ? min(lk - 1, qrow + off) : lk - 1;
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        const int thr = lim - kv0 - 32 * kb - 8 * half;
-#pragma unroll
-        for (int i = 0; i < 16; ++i)
-          if (16 * (i >> 3) + (i & 7) > thr) s[kb][i] = -INFINITY;
-      }
-    }
-
-    float mx = -INFINITY;
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[kb][i]);
-    mx = halves_max(mx);
-    // m_run is the reference max of the exponent.  It is moved (and O and l
-    // rescaled) only when the running max exceeds it by more than 2^8 in
-    // probability, so p <= 256 and most tiles skip the rescale entirely.
-    const float m_new = fmaxf(m_run, mx);
-    const bool grow = (m_new - m_run) * c > 8.f;   // false while both are -inf
-    if (__ballot(grow)) {
-      const float alpha = grow ? __builtin_amdgcn_exp2f((m_run - m_new) * c) : 1.f;
-      m_run = grow ? m_new : m_run;
-      l_run *= alpha;
-#pragma unroll
-      for (int cb = 0; cb < NCB; ++cb)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) acc[cb][i] *= alpha;
-    }
-    const float mc = (m_run == -INFINITY) ? 0.f : m_run * c;
-
-    // P (bf16) for the four 16-key steps j = (kb, hs), and O^T += V^T P^T.
-    // The exponentials of step j+1 are computed while step j's MFMAs run.
-    float psum = 0.f;
-    auto pstep = [&](int j) {
-      const int kb = j >> 1, hs = j & 1;
-      u32x4 u;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const float p0 = __builtin_amdgcn_exp2f(fmaf(s[kb][8 * hs + 2 * e], c, -mc));
-        const float p1 = __builtin_amdgcn_exp2f(fmaf(s[kb][8 * hs + 2 * e + 1], c, -mc));
-        psum += p0 + p1;
-        u[e] = pack_bf16x2(p0, p1);
-      }
-      return as_bf16x8(u);
+      for (int i = 0; i < 16; ++i)
+        if (16 * (i >> 3) + (i & 7) > thr) x[i] = -INFINITY;
     };
-    bf16x8 pcur = pstep(0);
+
+    // The tile runs as four MFMA blocks of eight, each paired with work of
+    // another block so the matrix pipe and the VALU run together:
+    //   A: S^T of keys 0-31          | K reads
+    //   B: S^T of keys 32-63         | K reads, V^T reads, softmax of keys 0-31
+    //   C: O^T += V^T P^T, keys 0-31 | V^T reads, softmax of keys 32-63
+    //   D: O^T += V^T P^T, keys 32-63
+    // Each 32-key half updates the running max on its own (online softmax is
+    // order free), so the rescale decision of a half only waits for its own
+    // scores.
+    auto kfrag = [&](int f) {
+      return as_bf16x8(*reinterpret_cast<const u32x4*>(
+          &ks[SwzTile<D>::chunk((f / NKS) * 32 + l32, 2 * (f % NKS) + half)]));
+    };
+    // V^T operand of step j (keys 16 j .. 16 j + 15): dims 32 cb + l32
+    auto vfrag = [&](int cb, int j) { return tr_frag<D>(vs, lane, 16 * j, 32 * cb); };
+
+    // softmax of one half: P (bf16, two 16-key steps), the half's reference
+    // max and row sum; returns whether the reference max moved
+    float m_use = m_run, psum = 0.f;
+    auto softmax_half = [&](const f32x16& x, bf16x8* p) {
+      float mx = -INFINITY;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      bf16x8 vn[NCB];
-      if (j + 1 < 4) {
+      for (int i = 0; i < 16; ++i) mx = fmaxf(mx, x[i]);
+      mx = halves_max(mx);
+      // m_run is the reference max of the exponent.  It moves (and O and l
+      // are rescaled) only when the running max exceeds it by more than 2^8
+      // in probability, so p <= 256 and most halves skip the rescale.
+      const float m_new = fmaxf(m_run, mx);
+      const bool grow = (m_new - m_run) * c > 8.f;   // false while both are -inf
+      m_use = grow ? m_new : m_run;
+      const float mc = (m_use == -INFINITY) ? 0.f : m_use * c;
+      psum = 0.f;
 #pragma unroll
-        for (int cb = 0; cb < NCB; ++cb) vn[cb] = vfrag(cb, j + 1);
-      }
-      const bf16x8 pnext = (j + 1 < 4) ? pstep(j + 1) : pcur;
+      for (int hs = 0; hs < 2; ++hs) {
+        u32x4 u;
 #pragma unroll
-      for (int cb = 0; cb < NCB; ++cb) acc[cb] = mfma32(vr[cb], pcur, acc[cb]);
-      pcur = pnext;
-      if (j + 1 < 4) {
-#pragma unroll
-        for (int cb = 0; cb < NCB; ++cb) vr[cb] = vn[cb];
-      }
-    }
-    // per MFMA of steps 0-2: the two transposed reads of the matching
-    // fragment of the next step and ~7 VALU of its exponentials
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-#pragma unroll
-      for (int cb = 0; cb < NCB; ++cb) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
-        if (j < 3) {
-          __builtin_amdgcn_sched_group_barrier(0x100, 2, 1);
-          __builtin_amdgcn_sched_group_barrier(0x002, 7, 1);
+        for (int e = 0; e < 4; ++e) {
+          const float p0 = __builtin_amdgcn_exp2f(fmaf(x[8 * hs + 2 * e], c, -mc));
+          const float p1 = __builtin_amdgcn_exp2f(fmaf(x[8 * hs + 2 * e + 1], c, -mc));
+          psum += p0 + p1;
+          u[e] = pack_bf16x2(p0, p1);
         }
+        p[hs] = as_bf16x8(u);
+      }
+      return grow;
+    };
+    auto commit_half = [&](bool grow) {
+      if (__ballot(grow)) {
+        const float alpha = grow ? __builtin_amdgcn_exp2f((m_run - m_use) * c) : 1.f;
+        l_run *= alpha;
+#pragma unroll
+        for (int cb = 0; cb < NCB; ++cb)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) acc[cb][i] *= alpha;
+      }
+      m_run = m_use;
+      l_run += psum;
+    };
+
+    constexpr int kPf = 4;   // K fragments in flight
+    bf16x8 kr[kPf];
+#pragma unroll
+    for (int f = 0; f < kPf; ++f) kr[f] = kfrag(f);
+    // A: S^T of keys 0-31
+    f32x16 s0, s1;
+#pragma unroll
+    for (int f = 0; f < NKS; ++f) {
+      const bf16x8 a = kr[f % kPf];
+      kr[f % kPf] = kfrag(f + kPf);
+      s0 = mfma32(a, qf[f], f == 0 ? f32x16{} : s0);
+    }
+#pragma unroll
+    for (int f = 0; f < NKS; ++f) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+    if (need_mask) mask(s0, 0);
+    // B: S^T of keys 32-63, V^T of keys 0-31 requested, softmax of keys 0-31
+    bf16x8 vr[2 * NCB];
+    bf16x8 p0[2];
+    bool g0;
+    {
+#pragma unroll
+      for (int f = NKS; f < 2 * NKS; ++f) {
+        const bf16x8 a = kr[f % kPf];
+        if (f + kPf < 2 * NKS) kr[f % kPf] = kfrag(f + kPf);
+        s1 = mfma32(a, qf[f - NKS], f == NKS ? f32x16{} : s1);
+      }
+#pragma unroll
+      for (int i = 0; i < 2 * NCB; ++i) vr[i] = vfrag(i % NCB, i / NCB);
+      g0 = softmax_half(s0, p0);
+      // per MFMA: its K read (first four), two V^T reads, ~10 VALU
+#pragma unroll
+      for (int f = 0; f < NKS; ++f) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
+        if (f < kPf) __builtin_amdgcn_sched_group_barrier(0x100, 1, 1);
+        __builtin_amdgcn_sched_group_barrier(0x100, 2 * (2 * NCB) / NKS, 1);
+        __builtin_amdgcn_sched_group_barrier(0x002, 10, 1);
       }
     }
-    l_run += psum;
+    commit_half(g0);
+    if (need_mask) mask(s1, 1);
+    // C: O^T += V^T P^T for keys 0-31, V^T of keys 32-63 requested, softmax
+    // of keys 32-63
+    bf16x8 p1[2];
+    bool g1;
+    {
+#pragma unroll
+      for (int i = 0; i < 2 * NCB; ++i) {
+        acc[i % NCB] = mfma32(vr[i], p0[i / NCB], acc[i % NCB]);
+        vr[i] = vfrag(i % NCB, 2 + i / NCB);
+      }
+      g1 = softmax_half(s1, p1);
+#pragma unroll
+      for (int i = 0; i < 2 * NCB; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 2);
+        __builtin_amdgcn_sched_group_barrier(0x100, 2, 2);
+        __builtin_amdgcn_sched_group_barrier(0x002, 10, 2);
+      }
+    }
+    commit_half(g1);
+    // D: O^T += V^T P^T for keys 32-63
+#pragma unroll
+    for (int i = 0; i < 2 * NCB; ++i) acc[i % NCB] = mfma32(vr[i], p1[i / NCB], acc[i % NCB]);
   };
 
   const int n_kv = it.count;
@@ -298,18 +310,17 @@ attn_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
 }  // namespace
 
 hipError_t launch_attn_fwd(const AttnShape& s, const void* q, const void* k, const void* v,
-                           const DevItem* items, int32_t n_items, int32_t out_dtype, void* out,
-                           float* lse, hipStream_t stream) {
-  if (n_items == 0) return hipSuccess;
-  const int groups = (n_items + 7) / 8;
-  const dim3 grid(unsigned(groups) * 8u * unsigned(s.hq));
+                           const ItemMap& map, int32_t out_dtype, void* out, float* lse,
+                           hipStream_t stream) {
+  if (map.rows == 0) return hipSuccess;
+  const dim3 grid(unsigned(map.rows) * unsigned(kXcds) * unsigned(s.hq));
   const auto* qq = reinterpret_cast<const uint16_t*>(q);
   const auto* kk = reinterpret_cast<const uint16_t*>(k);
   const auto* vv = reinterpret_cast<const uint16_t*>(v);
   ProfScope prof("attn_fwd", stream);
 #define VL_FWD(DD, F32)                                                                        \
   hipLaunchKernelGGL((attn_fwd_kernel<DD, F32>), grid, dim3(kThreads), 0, stream, qq, kk, vv,   \
-                     items, n_items, s.hq, s.hkv, s.scale, s.causal, out, lse, s.total_q)
+                     map.items, map.slot, s.hq, s.hkv, s.scale, s.causal, out, lse, s.total_q)
   if (s.d == 128) {
     if (out_dtype == 1) VL_FWD(128, true); else VL_FWD(128, false);
   } else {

@@ -221,14 +221,4 @@ __device__ __forceinline__ float halves_sum(float x) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
-// Workgroup id remapped so that consecutive logical ids land on the same XCD
-// (workgroups are dispatched round-robin over the 8 XCDs of an MI355X).
-__device__ __forceinline__ uint32_t xcd_remap(uint32_t bid, uint32_t nblocks) {
-  const uint32_t nx = 8;
-  const uint32_t per = nblocks / nx;           // full rounds
-  const uint32_t full = per * nx;
-  if (bid >= full) return bid;                 // ragged tail: identity
-  return (bid % nx) * per + bid / nx;
-}
-
 }  // namespace vl

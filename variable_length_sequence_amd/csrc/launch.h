@@ -27,6 +27,18 @@ constexpr int kFwdBK = 64;
 constexpr int kBwdBQ = 32;    // dK/dV kernel: query rows per step
 constexpr int kBwdBK = 128;   // dK/dV kernel: 4 waves x 32 keys
 
+// The work items of one pass and their assignment to the 8 XCDs: workgroup
+// b runs on XCD b % 8 (dispatch order), and the j-th item of XCD x is
+// items[slot[j * 8 + x]] (slot -1: none).  Every item is run for units_per_item
+// consecutive workgroups of its XCD (q heads, or kv heads x head slices).
+constexpr int kXcds = 8;
+
+struct ItemMap {
+  const DevItem* items;
+  const int32_t* slot;   // [rows * kXcds]
+  int32_t rows;          // items of the longest XCD list
+};
+
 struct AttnShape {
   int64_t total_q, total_k;
   int32_t hq, hkv, d;
@@ -35,16 +47,16 @@ struct AttnShape {
 };
 
 hipError_t launch_attn_fwd(const AttnShape& s, const void* q, const void* k, const void* v,
-                           const DevItem* items, int32_t n_items, int32_t out_dtype, void* out,
-                           float* lse, hipStream_t stream);
+                           const ItemMap& map, int32_t out_dtype, void* out, float* lse,
+                           hipStream_t stream);
 
 // Backward: D_i = dO_i . O_i, then dK/dV over the kv-tile list, then dQ over
 // the query-tile list.  dkv_acc is fp32 [2, total_k, hkv, d] scratch used when
 // q heads of one group are split over several workgroups (head_split > 1).
 hipError_t launch_attn_bwd(const AttnShape& s, const void* q, const void* k, const void* v,
                            const void* o, const void* dout, const float* lse,
-                           const DevItem* fwd_list, int32_t n_fwd, const DevItem* bwd_list,
-                           int32_t n_bwd, int32_t head_split, void* dq, void* dk, void* dv,
+                           const ItemMap& fwd_map, const ItemMap& bwd_map,
+                           int32_t head_split, void* dq, void* dk, void* dv,
                            float* delta, float* dkv_acc, hipStream_t stream);
 
 }  // namespace vl

@@ -122,4 +122,20 @@ std::vector<DevItem> device_items(const std::vector<Doc>& docs, const std::vecto
   return out;
 }
 
+std::vector<int32_t> xcd_slots(const std::vector<Item>& items, int n_xcd, int32_t& rows) {
+  std::vector<std::vector<int32_t>> lists(size_t(std::max(n_xcd, 1)));
+  std::vector<int64_t> load(lists.size(), 0);
+  for (size_t i = 0; i < items.size(); ++i) {
+    const size_t x = size_t(std::min_element(load.begin(), load.end()) - load.begin());
+    lists[x].push_back(int32_t(i));
+    load[x] += int64_t(items[i].count) + 1;
+  }
+  rows = 0;
+  for (const auto& l : lists) rows = std::max(rows, int32_t(l.size()));
+  std::vector<int32_t> slots(size_t(rows) * lists.size(), -1);
+  for (size_t x = 0; x < lists.size(); ++x)
+    for (size_t j = 0; j < lists[x].size(); ++j) slots[j * lists.size() + x] = lists[x][j];
+  return slots;
+}
+
 }  // namespace vl

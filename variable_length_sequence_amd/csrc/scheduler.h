@@ -51,4 +51,13 @@ int64_t issued_pairs(const std::vector<Item>& items, int bq, int bk);
 
 std::vector<DevItem> device_items(const std::vector<Doc>& docs, const std::vector<Item>& items);
 
+// Assignment of an LPT-ordered item list to the n_xcd XCDs of the device:
+// each item, in list order, goes to the XCD with the least work so far
+// (weight count + 1: its tiles plus its start-up), so every XCD keeps the
+// longest-first order and all XCDs end within about one short item of each
+// other (round-robin dealing would give the first XCD the longest item of
+// every round).  Returns slots[j * n_xcd + x] = index of the j-th item of XCD
+// x, or -1; rows = the longest XCD list.
+std::vector<int32_t> xcd_slots(const std::vector<Item>& items, int n_xcd, int32_t& rows);
+
 }  // namespace vl
