@@ -219,15 +219,17 @@ attn_bwd_dkdv_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
 #pragma unroll
     for (int i = 0; i < 16; ++i) acc[cb][i] = 0.f;
 
-  // steps run over (q head, 32-row query tile) pairs, tiles innermost
+  // Steps run over (32-row query tile, q head) pairs, heads innermost and
+  // tiles from the end of the document back to the first one this key tile
+  // sees: the workgroups of the other key tiles of the document (and kv
+  // head) then stream the same query rows at the same time, which they share
+  // in the L2 instead of each fetching them from memory.
   const int n_steps = hpg * it.count;
-  const int i_begin = it.first * KB_Q;
-  const int i_end = (it.first + it.count) * KB_Q;
+  const int i_last = (it.first + it.count - 1) * KB_Q;
   auto advance = [&](int& i0, int& h) {
-    i0 += KB_Q;
-    if (i0 == i_end) {
-      i0 = i_begin;
-      ++h;
+    if (++h == h_begin + hpg) {
+      h = h_begin;
+      i0 -= KB_Q;
     }
   };
   const uint16_t* qdoc = q + int64_t(it.q_start) * q_tok;
@@ -257,10 +259,8 @@ attn_bwd_dkdv_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
     }
   };
 
-  int nxt_i0 = i_begin, nxt_h = h_begin;       // step t + 1
-  int cur_i0 = i_begin;                        // step t (dV role)
-  int prv_i0 = i_begin;                        // step t - 1 (unused by the dK role)
-  (void)prv_i0;
+  int nxt_i0 = i_last, nxt_h = h_begin;        // step t + 1
+  int cur_i0 = i_last;                         // step t (dV role)
   if (n_steps > 0) {
     issue(nxt_i0, nxt_h, lds_addr(sm.q[0]), lds_addr(sm.dout[0]));
     store_rows(fetch_rows(nxt_i0, nxt_h), 0);
