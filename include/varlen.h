@@ -186,6 +186,35 @@ VL_API int varlen_schedule_export(const int32_t* cu_seqlens_q, const int32_t* cu
                            int32_t* bq, int32_t* bk);
 
 /*
+ * varlen_ring_block - host-only: one (query chunk, key chunk) block of ring
+ * attention over a packed causal batch.  The packed token axis is cut into
+ * contiguous chunks, one per ring rank, and every block of the chunk grid has
+ * one of the attention patterns of the HSAP page, Figure 3 (Section 3.2):
+ * A1 the diagonal block (causal within each document), A2 every pair
+ * visible, A3 the top rows see every key, A4 every row sees the right-hand
+ * keys, A5 the top rows see the right-hand keys, N nothing visible.
+ *
+ *   cu_seqlens   host int32 [n_docs + 1] of the whole packed batch
+ *   q_begin, q_end, k_begin, k_end   token ranges of the query and key
+ *                chunks: equal (the diagonal block) or disjoint
+ *   cu_q_out, cu_k_out  host int32 [n_docs + 1]: per document, its tokens
+ *                inside the query chunk and inside the key chunk
+ *   causal_out   the causal flag of the block's attention call
+ *   cls_out      0 N, 1 A1, 2 A2, 3 A3, 4 A4, 5 A5
+ * varlen_attn_fwd(q[q_begin:q_end], k[k_begin:k_end], v[k_begin:k_end],
+ * cu_q_out, cu_k_out, causal = *causal_out) then computes the block's partial
+ * (O, LSE) (skip class N), and attn_lse_merge over the key chunks gives the
+ * rows of the query chunk; varlen_attn_bwd of the block with the merged O and
+ * LSE gives its share of dq, dk and dv (the shares sum to the gradients).
+ * Errors: VL_EINVAL (null pointer, ranges out of order or overlapping
+ * unequally), VL_ESEQLENS.
+ */
+VL_API int varlen_ring_block(const int32_t* cu_seqlens, int32_t n_docs,
+                             int64_t q_begin, int64_t q_end, int64_t k_begin, int64_t k_end,
+                             int32_t* cu_q_out, int32_t* cu_k_out,
+                             int32_t* causal_out, int32_t* cls_out);
+
+/*
  * varlen_profile_enable / varlen_profile_read - optional per-kernel timing.
  * While enabled, every kernel the library launches is bracketed by two HIP
  * events recorded on its launch stream.  Enabling clears earlier records.

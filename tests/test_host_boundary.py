@@ -157,3 +157,87 @@ def test_schedule_export_rejects():
     items = np.zeros(4, np.int32)
     assert L.varlen_schedule_export(ip(ok), ip(ok), 2, 1, 0, 128, ip(items), 0, ctypes.byref(n),
                                     None, None, None, None) == -6
+
+
+# ---------------------------------------------------------------- ring blocks
+def _brute_block(cu, qr, kr):
+    """Visible pairs of a (query chunk, key chunk) block of the packed causal
+    batch with document mask, straight from the definition."""
+    a = np.asarray(cu)
+    doc = np.searchsorted(a, np.arange(int(a[-1])), side="right") - 1
+    x = np.arange(*qr)
+    y = np.arange(*kr)
+    return (doc[x][:, None] == doc[y][None, :]) & (y[None, :] <= x[:, None])
+
+
+def _block_from_call(cu_q, cu_k, causal):
+    """Visible pairs of the attention call varlen_ring_block describes."""
+    lq = np.diff(cu_q)
+    lk = np.diff(cu_k)
+    vis = np.zeros((int(cu_q[-1]), int(cu_k[-1])), dtype=bool)
+    for b in range(len(lq)):
+        for i in range(lq[b]):
+            for j in range(lk[b]):
+                if not causal or j <= i + lk[b] - lq[b]:
+                    vis[cu_q[b] + i, cu_k[b] + j] = True
+    return vis
+
+
+def test_ring_blocks_reproduce_hsap_figure3():
+    lines = [ln.split() for ln in open(os.path.join(ROOT, "tests", "golden", "hsap_fig3_step1.txt"))
+             if ln.strip() and not ln.startswith("#")]
+    cu = [int(x) for x in lines[0][1:]]
+    chunk = int(lines[1][1])
+    fig = lines[2:]
+    n = int(cu[-1]) // chunk
+    for r in range(n):
+        for s in range(n):
+            cq, ck, causal, cls = vl.varlen_ring_block(cu, (r * chunk, (r + 1) * chunk),
+                                                       (s * chunk, (s + 1) * chunk))
+            assert cls == fig[r][s], (r, s, cls, fig[r][s])
+            vis = _brute_block(cu, (r * chunk, (r + 1) * chunk), (s * chunk, (s + 1) * chunk))
+            if cls != "N":
+                assert np.array_equal(_block_from_call(cq, ck, causal), vis), (r, s)
+            else:
+                assert not vis.any()
+
+
+def test_ring_blocks_random_packings_match_brute_force():
+    rng = np.random.default_rng(7)
+    for trial in range(30):
+        lens = workloads.random_lengths(rng, int(rng.integers(1, 7)), 0, 40)
+        cu = _cu(lens)
+        total = int(cu[-1])
+        if total == 0:
+            continue
+        n = int(rng.integers(1, 6))
+        bounds = np.linspace(0, total, n + 1).astype(int)
+        for r in range(n):
+            for s in range(n):
+                qr, kr = (bounds[r], bounds[r + 1]), (bounds[s], bounds[s + 1])
+                cq, ck, causal, cls = vl.varlen_ring_block(cu, qr, kr)
+                assert cq[-1] == qr[1] - qr[0] and ck[-1] == kr[1] - kr[0]
+                vis = _brute_block(cu, qr, kr)
+                assert causal == (tuple(qr) == tuple(kr))   # equal ranges: the diagonal
+                if cls == "N":
+                    assert not vis.any()
+                else:
+                    assert np.array_equal(_block_from_call(cq, ck, causal), vis), (trial, r, s)
+                # the class names the pattern (oracle's classifier on equal chunks)
+                if not causal and cls != "N":
+                    rows, cols = vis.any(axis=1), vis.any(axis=0)
+                    assert (cls == "A2") == bool(vis.all())
+                    assert (cls in ("A2", "A3")) == bool(cols.all())
+                    assert (cls in ("A2", "A4")) == bool(rows.all())
+
+
+def test_ring_block_rejects_overlapping_unequal_chunks():
+    cu = [0, 10, 30]
+    with pytest.raises(vl.VarlenError) as e:
+        vl.varlen_ring_block(cu, (0, 20), (10, 30))
+    assert e.value.code == -1
+    with pytest.raises(vl.VarlenError):
+        vl.varlen_ring_block(cu, (0, 40), (0, 40))
+    with pytest.raises(vl.VarlenError) as e:
+        vl.varlen_ring_block([0, 5, 3], (0, 3), (0, 3))
+    assert e.value.code == -3

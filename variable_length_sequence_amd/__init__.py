@@ -11,6 +11,7 @@ Entry points (same names as the C ABI in ``include/varlen.h``):
   attn_lse_merge(o_parts, lse_parts, out_dtype=bf16) -> (o, lse)
   sp_seq2head(x, sp_degree) -> y ;  sp_head2seq(y) -> x
   varlen_schedule_export(cu_q, cu_k, causal, pass_, head_dim) -> dict (host only)
+  varlen_ring_block(cu, q_range, k_range) -> (cu_q, cu_k, causal, cls) (host only)
 """
 from __future__ import annotations
 
@@ -30,7 +31,9 @@ STATUS = {0: "VL_OK", -1: "VL_EINVAL", -2: "VL_ESHAPE", -3: "VL_ESEQLENS",
 EXPORTS = ["varlen_attn_fwd", "varlen_attn_bwd_workspace_size", "varlen_attn_bwd",
            "attn_lse_merge", "sp_seq2head", "sp_head2seq", "varlen_schedule_export",
            "varlen_last_error", "varlen_cache_clear", "varlen_version", "varlen_profile_enable",
-           "varlen_profile_read"]
+           "varlen_profile_read", "varlen_ring_block"]
+
+RING_CLASSES = ("N", "A1", "A2", "A3", "A4", "A5")
 
 
 class VarlenError(RuntimeError):
@@ -72,6 +75,8 @@ def lib():
     L.varlen_schedule_export.argtypes = [pi32, pi32, i32, i32, i32, i32, pi32, i64, pi64, pi64,
                                          pi64, pi32, pi32]
     L.varlen_schedule_export.restype = ctypes.c_int
+    L.varlen_ring_block.argtypes = [pi32, i32, i64, i64, i64, i64, pi32, pi32, pi32, pi32]
+    L.varlen_ring_block.restype = ctypes.c_int
     L.varlen_last_error.argtypes = []
     L.varlen_last_error.restype = ctypes.c_char_p
     L.varlen_cache_clear.argtypes = []
@@ -231,6 +236,21 @@ def varlen_schedule_export(cu_q, cu_k, causal: bool, pass_: int, head_dim: int) 
                                     ctypes.byref(bk)))
     return {"items": items[:n.value], "useful_pairs": useful.value, "issued_pairs": issued.value,
             "bq": bq.value, "bk": bk.value}
+
+
+def varlen_ring_block(cu, q_range, k_range):
+    """Host-only: the attention call of one (query chunk, key chunk) block of
+    ring attention over a packed causal batch -> (cu_q, cu_k, causal, cls),
+    cls one of RING_CLASSES ("N": no call needed)."""
+    c = _cu_host(cu)
+    n = len(c) - 1
+    cq = np.zeros(n + 1, dtype=np.int32)
+    ck = np.zeros(n + 1, dtype=np.int32)
+    causal, cls = ctypes.c_int32(0), ctypes.c_int32(0)
+    _check(lib().varlen_ring_block(_iptr(c), n, int(q_range[0]), int(q_range[1]), int(k_range[0]),
+                                   int(k_range[1]), _iptr(cq), _iptr(ck), ctypes.byref(causal),
+                                   ctypes.byref(cls)))
+    return cq, ck, bool(causal.value), RING_CLASSES[cls.value]
 
 
 def profile_enable(on: bool = True):

@@ -316,6 +316,26 @@ int sp_head2seq(const void* y, void* x, int64_t n_tokens, int32_t n_heads, int32
   }
 }
 
+int varlen_ring_block(const int32_t* cu_seqlens, int32_t n_docs, int64_t q_begin, int64_t q_end,
+                      int64_t k_begin, int64_t k_end, int32_t* cu_q_out, int32_t* cu_k_out,
+                      int32_t* causal_out, int32_t* cls_out) {
+  try {
+    g_err.clear();
+    if (!cu_seqlens || !cu_q_out || !cu_k_out || !causal_out || !cls_out)
+      return fail(VL_EINVAL, "null argument");
+    if (n_docs < 0) return fail(VL_EINVAL, "n_docs must be >= 0");
+    std::string err;
+    if (!vl::validate_cu(cu_seqlens, n_docs, cu_seqlens[n_docs], err))
+      return fail(VL_ESEQLENS, "cu_seqlens: " + err);
+    if (!vl::ring_block(cu_seqlens, n_docs, q_begin, q_end, k_begin, k_end, cu_q_out, cu_k_out,
+                        *causal_out, *cls_out, err))
+      return fail(VL_EINVAL, err);
+    return VL_OK;
+  } catch (const std::exception& ex) {
+    return fail(VL_EINVAL, std::string("internal error: ") + ex.what());
+  }
+}
+
 int varlen_schedule_export(const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
                            int32_t n_docs, int32_t causal, int32_t pass, int32_t head_dim,
                            int32_t* items, int64_t cap, int64_t* n_items, int64_t* useful_pairs,

@@ -138,4 +138,52 @@ std::vector<int32_t> xcd_slots(const std::vector<Item>& items, int n_xcd, int32_
   return slots;
 }
 
+bool ring_block(const int32_t* cu, int32_t n_docs, int64_t q_begin, int64_t q_end,
+                int64_t k_begin, int64_t k_end, int32_t* cu_q, int32_t* cu_k, int32_t& causal,
+                int32_t& cls, std::string& err) {
+  const int64_t total = cu[n_docs];
+  if (q_begin < 0 || q_begin > q_end || q_end > total || k_begin < 0 || k_begin > k_end ||
+      k_end > total) {
+    err = "chunk ranges must satisfy 0 <= begin <= end <= total tokens";
+    return false;
+  }
+  const bool diagonal = q_begin == k_begin && q_end == k_end;
+  const bool keys_before = k_end <= q_begin;
+  const bool keys_after = k_begin >= q_end;
+  if (!diagonal && !keys_before && !keys_after) {
+    err = "the query and key chunks must be equal or disjoint";
+    return false;
+  }
+  // per-document overlap with each chunk; the document spanning both chunks
+  // (at most one when they are disjoint) is the only one with visible pairs
+  cu_q[0] = 0;
+  cu_k[0] = 0;
+  int32_t spanning = -1;
+  for (int32_t b = 0; b < n_docs; ++b) {
+    const int64_t lo = cu[b], hi = cu[b + 1];
+    const int64_t lq = std::max<int64_t>(0, std::min(hi, q_end) - std::max(lo, q_begin));
+    const int64_t lk = std::max<int64_t>(0, std::min(hi, k_end) - std::max(lo, k_begin));
+    cu_q[b + 1] = cu_q[b] + int32_t(lq);
+    cu_k[b + 1] = cu_k[b] + int32_t(lk);
+    if (lq > 0 && lk > 0) spanning = b;
+  }
+  if (diagonal) {
+    causal = 1;
+    cls = kRingA1;
+    return true;
+  }
+  causal = 0;
+  if (keys_after || spanning < 0) {
+    cls = kRingN;   // keys after the queries, or no document in both chunks
+    return true;
+  }
+  // the spanning document covers the top rows of the query chunk and the
+  // right-hand columns of the key chunk
+  const int64_t rows = cu_q[spanning + 1] - cu_q[spanning];
+  const int64_t cols = cu_k[spanning + 1] - cu_k[spanning];
+  const bool all_rows = rows == q_end - q_begin, all_cols = cols == k_end - k_begin;
+  cls = all_rows ? (all_cols ? kRingA2 : kRingA4) : (all_cols ? kRingA3 : kRingA5);
+  return true;
+}
+
 }  // namespace vl

@@ -60,4 +60,15 @@ std::vector<DevItem> device_items(const std::vector<Doc>& docs, const std::vecto
 // x, or -1; rows = the longest XCD list.
 std::vector<int32_t> xcd_slots(const std::vector<Item>& items, int n_xcd, int32_t& rows);
 
+// One (query chunk, key chunk) block of ring attention over a packed causal
+// batch (HSAP page, Section 3.2, Figure 3).  Fills per-document token counts
+// inside each chunk (as cumulative arrays of n_docs + 1 entries), the causal
+// flag of the block's attention call and its class (RingClass).  Supported:
+// equal ranges (the diagonal) and disjoint ranges.  Returns false with err
+// set for anything else.
+enum RingClass { kRingN = 0, kRingA1 = 1, kRingA2 = 2, kRingA3 = 3, kRingA4 = 4, kRingA5 = 5 };
+bool ring_block(const int32_t* cu, int32_t n_docs, int64_t q_begin, int64_t q_end,
+                int64_t k_begin, int64_t k_end, int32_t* cu_q, int32_t* cu_k, int32_t& causal,
+                int32_t& cls, std::string& err);
+
 }  // namespace vl
