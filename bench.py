@@ -273,10 +273,28 @@ def bench_ring(vl, torch, dev, steps):
     flops = 4 * w.d * pairs * w.hq
     merge_bytes = n * (c * w.hq * w.d * 4 + c * w.hq * 4) + c * w.hq * w.d * 2 + c * w.hq * 4
     ms = tm.wall_ms / steps
+
+    # the same share with the merge folded into the forward's epilogue
+    o_acc = torch.empty(c, w.hq, w.d, dtype=torch.float32, device=dev)
+    lse_acc = torch.empty(w.hq, c, dtype=torch.float32, device=dev)
+
+    def step_acc():
+        o_acc.zero_()
+        lse_acc.fill_(float("-inf"))
+        for j in range(n):
+            vl.varlen_attn_fwd_acc(qd, kd[j * c:(j + 1) * c], vd[j * c:(j + 1) * c], one, one,
+                                   o_acc, lse_acc, causal=(j == qc))
+    step_acc()
+    with Timer(torch) as tm2:
+        for _ in range(steps):
+            step_acc()
+    ms2 = tm2.wall_ms / steps
     return {"workload": w.name, "ms_per_step": round(ms, 3),
             "tflops": round(flops / (ms * 1e-3) / 1e12, 2), "useful_tflop": round(flops / 1e12, 3),
             "kernels": kernel_table(prof, {}, {"lse_merge": merge_bytes}),
-            "attn_fwd_avg_ms": round(prof["attn_fwd"][1] / prof["attn_fwd"][0], 4)}
+            "attn_fwd_avg_ms": round(prof["attn_fwd"][1] / prof["attn_fwd"][0], 4),
+            "fused_merge": {"ms_per_step": round(ms2, 3),
+                            "tflops": round(flops / (ms2 * 1e-3) / 1e12, 2)}}
 
 
 def main():

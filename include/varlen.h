@@ -81,6 +81,31 @@ VL_API int varlen_attn_fwd(const void* q, const void* k, const void* v,
                     void* out, float* lse, void* stream);
 
 /*
+ * varlen_attn_fwd_acc - the forward over one key chunk folded into running
+ * fp32 (O, LSE) accumulators: the online combination of ring attention
+ * (HSAP page, Section 2.2.1) with its copy/rescale step (Section 3.1,
+ * Table 1), which the page leaves as separate operations, done in the
+ * forward kernel's epilogue.  Per query row and head, with (O, LSE) of this
+ * call's keys:  M = max(LSE_acc, LSE),  w_acc = exp(LSE_acc - M),
+ * w = exp(LSE - M),  O_acc <- (w_acc O_acc + w O) / (w_acc + w),
+ * LSE_acc <- M + ln(w_acc + w); rows where both are -inf keep O_acc.
+ * Calling it once per key chunk, from o_acc = 0 and lse_acc = -inf, gives
+ * the result of attn_lse_merge over the chunks' partials (up to fp32
+ * rounding) without storing them.
+ *
+ *   q, k, v, cu_*, sizes, scale, causal   as varlen_attn_fwd
+ *   o_acc        fp32 [total_q, n_heads_q, head_dim], read and written
+ *   lse_acc      fp32 [n_heads_q, total_q], read and written
+ * Errors: as varlen_attn_fwd.
+ */
+VL_API int varlen_attn_fwd_acc(const void* q, const void* k, const void* v,
+                        const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
+                        int32_t n_docs, int64_t total_q, int64_t total_k,
+                        int32_t n_heads_q, int32_t n_heads_kv, int32_t head_dim,
+                        float softmax_scale, int32_t causal, float* o_acc, float* lse_acc,
+                        void* stream);
+
+/*
  * varlen_attn_bwd_workspace_size - bytes of device workspace varlen_attn_bwd
  * needs for these sizes (fp32 per-row terms and kv-gradient accumulators).
  */

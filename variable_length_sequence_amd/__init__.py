@@ -31,7 +31,7 @@ STATUS = {0: "VL_OK", -1: "VL_EINVAL", -2: "VL_ESHAPE", -3: "VL_ESEQLENS",
 EXPORTS = ["varlen_attn_fwd", "varlen_attn_bwd_workspace_size", "varlen_attn_bwd",
            "attn_lse_merge", "sp_seq2head", "sp_head2seq", "varlen_schedule_export",
            "varlen_last_error", "varlen_cache_clear", "varlen_version", "varlen_profile_enable",
-           "varlen_profile_read", "varlen_ring_block"]
+           "varlen_profile_read", "varlen_ring_block", "varlen_attn_fwd_acc"]
 
 RING_CLASSES = ("N", "A1", "A2", "A3", "A4", "A5")
 
@@ -61,6 +61,9 @@ def lib():
     L.varlen_attn_fwd.argtypes = [vp, vp, vp, pi32, pi32, i32, i64, i64, i32, i32, i32, f32, i32,
                                   i32, vp, vp, vp]
     L.varlen_attn_fwd.restype = ctypes.c_int
+    L.varlen_attn_fwd_acc.argtypes = [vp, vp, vp, pi32, pi32, i32, i64, i64, i32, i32, i32, f32,
+                                      i32, vp, vp, vp]
+    L.varlen_attn_fwd_acc.restype = ctypes.c_int
     L.varlen_attn_bwd_workspace_size.argtypes = [i64, i64, i32, i32, i32]
     L.varlen_attn_bwd_workspace_size.restype = ctypes.c_size_t
     L.varlen_attn_bwd.argtypes = [vp, vp, vp, vp, vp, vp, pi32, pi32, i32, i64, i64, i32, i32, i32,
@@ -145,6 +148,27 @@ def varlen_attn_fwd(q, k, v, cu_q, cu_k, causal: bool = True, scale: Optional[fl
                                  len(cq) - 1, tq, tk, hq, hkv, d, float(scale or 0.0), int(causal),
                                  od, _dev_ptr(out), _dev_ptr(lse), _stream()))
     return out, lse
+
+
+def varlen_attn_fwd_acc(q, k, v, cu_q, cu_k, o_acc, lse_acc, causal: bool = True,
+                        scale: Optional[float] = None):
+    """Forward over these keys folded into running fp32 accumulators o_acc
+    [Tq,Hq,d] and lse_acc [Hq,Tq] (in place; start from 0 and -inf)."""
+    import torch
+    cq, ck = _cu_host(cu_q), _cu_host(cu_k)
+    tq, hq, d = q.shape
+    tk, hkv, _ = k.shape
+    for t in (q, k, v):
+        if t.dtype != torch.bfloat16:
+            raise TypeError("q, k and v must be bfloat16")
+    if o_acc.dtype != torch.float32 or lse_acc.dtype != torch.float32:
+        raise TypeError("o_acc and lse_acc must be float32")
+    if tuple(o_acc.shape) != (tq, hq, d) or tuple(lse_acc.shape) != (hq, tq):
+        raise ValueError("o_acc must be [Tq, Hq, d] and lse_acc [Hq, Tq]")
+    _check(lib().varlen_attn_fwd_acc(_dev_ptr(q), _dev_ptr(k), _dev_ptr(v), _iptr(cq), _iptr(ck),
+                                     len(cq) - 1, tq, tk, hq, hkv, d, float(scale or 0.0),
+                                     int(causal), _dev_ptr(o_acc), _dev_ptr(lse_acc), _stream()))
+    return o_acc, lse_acc
 
 
 def varlen_attn_bwd(q, k, v, o, do, lse, cu_q, cu_k, causal: bool = True,

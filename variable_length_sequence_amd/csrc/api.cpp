@@ -166,7 +166,36 @@ int varlen_attn_fwd(const void* q, const void* k, const void* v, const int32_t* 
     if (rc) return rc;
     vl::AttnShape s{total_q, total_k, n_heads_q, n_heads_kv, head_dim,
                     resolve_scale(softmax_scale, head_dim), causal != 0};
-    hipError_t e = vl::launch_attn_fwd(s, q, k, v, p.map(), out_dtype, out, lse,
+    hipError_t e = vl::launch_attn_fwd(s, q, k, v, p.map(), out_dtype == VL_F32 ? vl::kOutF32 : vl::kOutBf16, out, lse,
+                                       reinterpret_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(e, "attn_fwd launch");
+    return VL_OK;
+  } catch (const std::exception& ex) {
+    return fail(VL_EHIP, std::string("internal error: ") + ex.what());
+  } catch (...) {
+    return fail(VL_EHIP, "internal error");
+  }
+}
+
+int varlen_attn_fwd_acc(const void* q, const void* k, const void* v, const int32_t* cu_seqlens_q,
+                        const int32_t* cu_seqlens_k, int32_t n_docs, int64_t total_q,
+                        int64_t total_k, int32_t n_heads_q, int32_t n_heads_kv, int32_t head_dim,
+                        float softmax_scale, int32_t causal, float* o_acc, float* lse_acc,
+                        void* stream) {
+  try {
+    g_err.clear();
+    int rc = check_attn_common(q, k, v, cu_seqlens_q, cu_seqlens_k, n_docs, total_q, total_k,
+                               n_heads_q, n_heads_kv, head_dim);
+    if (rc) return rc;
+    if (!o_acc || !lse_acc) return fail(VL_EINVAL, "o_acc and lse_acc must be non-null");
+    if (reinterpret_cast<uintptr_t>(o_acc) % 16) return fail(VL_EINVAL, "o_acc must be 16-byte aligned");
+    if (total_q == 0) return VL_OK;
+    Plan p;
+    rc = get_plan(0, causal != 0, cu_seqlens_q, cu_seqlens_k, n_docs, p);
+    if (rc) return rc;
+    vl::AttnShape s{total_q, total_k, n_heads_q, n_heads_kv, head_dim,
+                    resolve_scale(softmax_scale, head_dim), causal != 0};
+    hipError_t e = vl::launch_attn_fwd(s, q, k, v, p.map(), vl::kOutAcc, o_acc, lse_acc,
                                        reinterpret_cast<hipStream_t>(stream));
     if (e != hipSuccess) return hip_fail(e, "attn_fwd launch");
     return VL_OK;

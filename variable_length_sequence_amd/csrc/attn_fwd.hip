@@ -49,7 +49,9 @@ struct FwdSmem {
   uint16_t v[2][BK * D];
 };
 
-template <int D, bool F32OUT>
+// OUT: kOutBf16 / kOutF32 write O and LSE; kOutAcc folds them into fp32
+// running (O, LSE) accumulators (see the epilogue).
+template <int D, int OUT>
 __global__ void __launch_bounds__(kThreads, 2)
 attn_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
                 const uint16_t* __restrict__ v, const DevItem* __restrict__ items,
@@ -283,26 +285,56 @@ attn_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
   const float inv = (l_tot > 0.f) ? 1.f / l_tot : 0.f;
   if (qrow < lq) {
     const int64_t orow = (int64_t(it.q_start) + qrow) * q_tok + int64_t(h) * D;
-#pragma unroll
-    for (int cb = 0; cb < NCB; ++cb)
-#pragma unroll
-      for (int gq = 0; gq < 4; ++gq) {
-        const int cc = cb * 32 + 8 * gq + 4 * half;
-        if constexpr (F32OUT) {
-          f32x4 o4;
-#pragma unroll
-          for (int j = 0; j < 4; ++j) o4[j] = acc[cb][4 * gq + j] * inv;
-          *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(out) + orow + cc) = o4;
-        } else {
-          u32x2 o2;
-          o2[0] = pack_bf16x2(acc[cb][4 * gq] * inv, acc[cb][4 * gq + 1] * inv);
-          o2[1] = pack_bf16x2(acc[cb][4 * gq + 2] * inv, acc[cb][4 * gq + 3] * inv);
-          *reinterpret_cast<u32x2*>(reinterpret_cast<uint16_t*>(out) + orow + cc) = o2;
-        }
+    const int64_t lrow = int64_t(h) * total_q + it.q_start + qrow;
+    const float lv = (l_tot > 0.f) ? (m_run * scale + __logf(l_tot)) : -INFINITY;
+    if constexpr (OUT == kOutAcc) {
+      // Fold this key chunk's (O, LSE) into the running pair (the online
+      // combination of ring attention: HSAP page, Section 2.2.1, with its
+      // rescale step done here instead of in a separate pass, Section 3.1):
+      // M = max(LSE_a, LSE), w = exp(. - M), O_a = (w_a O_a + w O) / (w_a + w),
+      // LSE_a = M + ln(w_a + w).  Two -inf LSEs leave the pair unchanged.
+      float* oa = reinterpret_cast<float*>(out);
+      const float la = lse[lrow];
+      const float mm = fmaxf(la, lv);
+      float ca = 1.f, cn = 0.f, ln = la;
+      if (mm != -INFINITY) {
+        const float wa = __expf(la - mm), wn = __expf(lv - mm);
+        const float rden = 1.f / (wa + wn);
+        ca = wa * rden;
+        cn = wn * rden * inv;
+        ln = mm + __logf(wa + wn);
       }
-    if (half == 0) {
-      const float lv = (l_tot > 0.f) ? (m_run * scale + __logf(l_tot)) : -INFINITY;
-      lse[int64_t(h) * total_q + it.q_start + qrow] = lv;
+#pragma unroll
+      for (int cb = 0; cb < NCB; ++cb)
+#pragma unroll
+        for (int gq = 0; gq < 4; ++gq) {
+          const int cc = cb * 32 + 8 * gq + 4 * half;
+          f32x4 o4 = *reinterpret_cast<const f32x4*>(oa + orow + cc);
+#pragma unroll
+          for (int j = 0; j < 4; ++j) o4[j] = fmaf(ca, o4[j], cn * acc[cb][4 * gq + j]);
+          *reinterpret_cast<f32x4*>(oa + orow + cc) = o4;
+        }
+      // the one load of LSE_a above (both half-waves) precedes this store
+      if (half == 0) lse[lrow] = ln;
+    } else {
+#pragma unroll
+      for (int cb = 0; cb < NCB; ++cb)
+#pragma unroll
+        for (int gq = 0; gq < 4; ++gq) {
+          const int cc = cb * 32 + 8 * gq + 4 * half;
+          if constexpr (OUT == kOutF32) {
+            f32x4 o4;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) o4[j] = acc[cb][4 * gq + j] * inv;
+            *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(out) + orow + cc) = o4;
+          } else {
+            u32x2 o2;
+            o2[0] = pack_bf16x2(acc[cb][4 * gq] * inv, acc[cb][4 * gq + 1] * inv);
+            o2[1] = pack_bf16x2(acc[cb][4 * gq + 2] * inv, acc[cb][4 * gq + 3] * inv);
+            *reinterpret_cast<u32x2*>(reinterpret_cast<uint16_t*>(out) + orow + cc) = o2;
+          }
+        }
+      if (half == 0) lse[lrow] = lv;
     }
   }
 }
@@ -310,7 +342,7 @@ attn_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
 }  // namespace
 
 hipError_t launch_attn_fwd(const AttnShape& s, const void* q, const void* k, const void* v,
-                           const ItemMap& map, int32_t out_dtype, void* out, float* lse,
+                           const ItemMap& map, int32_t out_kind, void* out, float* lse,
                            hipStream_t stream) {
   if (map.rows == 0) return hipSuccess;
   const dim3 grid(unsigned(map.rows) * unsigned(kXcds) * unsigned(s.hq));
@@ -318,13 +350,17 @@ hipError_t launch_attn_fwd(const AttnShape& s, const void* q, const void* k, con
   const auto* kk = reinterpret_cast<const uint16_t*>(k);
   const auto* vv = reinterpret_cast<const uint16_t*>(v);
   ProfScope prof("attn_fwd", stream);
-#define VL_FWD(DD, F32)                                                                        \
-  hipLaunchKernelGGL((attn_fwd_kernel<DD, F32>), grid, dim3(kThreads), 0, stream, qq, kk, vv,   \
+#define VL_FWD(DD, OUTK)                                                                       \
+  hipLaunchKernelGGL((attn_fwd_kernel<DD, OUTK>), grid, dim3(kThreads), 0, stream, qq, kk, vv,  \
                      map.items, map.slot, s.hq, s.hkv, s.scale, s.causal, out, lse, s.total_q)
   if (s.d == 128) {
-    if (out_dtype == 1) VL_FWD(128, true); else VL_FWD(128, false);
+    if (out_kind == kOutAcc) VL_FWD(128, kOutAcc);
+    else if (out_kind == kOutF32) VL_FWD(128, kOutF32);
+    else VL_FWD(128, kOutBf16);
   } else {
-    if (out_dtype == 1) VL_FWD(64, true); else VL_FWD(64, false);
+    if (out_kind == kOutAcc) VL_FWD(64, kOutAcc);
+    else if (out_kind == kOutF32) VL_FWD(64, kOutF32);
+    else VL_FWD(64, kOutBf16);
   }
 #undef VL_FWD
   return hipGetLastError();

@@ -46,8 +46,11 @@ struct AttnShape {
   int32_t causal;
 };
 
+// out_kind: kOutBf16 / kOutF32 write O (bf16 / fp32) and LSE; kOutAcc folds
+// O and LSE into running fp32 accumulators held in out and lse.
+constexpr int kOutBf16 = 0, kOutF32 = 1, kOutAcc = 2;
 hipError_t launch_attn_fwd(const AttnShape& s, const void* q, const void* k, const void* v,
-                           const ItemMap& map, int32_t out_dtype, void* out, float* lse,
+                           const ItemMap& map, int32_t out_kind, void* out, float* lse,
                            hipStream_t stream);
 
 // Backward: D_i = dO_i . O_i, then dK/dV over the kv-tile list, then dQ over
