@@ -244,6 +244,34 @@ def bench_permute(vl, torch, dev, steps):
     return prof, {"sp_seq2head": nbytes, "sp_head2seq": nbytes}
 
 
+def bench_qkv_permute(vl, torch, dev, steps):
+    """Fused Q/K/V pack and gradient unpack of a 384K sequence's shard with
+    32 query / 4 kv heads over 8 ranks (each kv head sent to 2 ranks)."""
+    n, hq, hkv, d, P = 49152, 32, 4, 128, 8
+    g = torch.Generator(device=dev).manual_seed(0)
+    bf = torch.bfloat16
+
+    def xset():
+        return [torch.randn(n, h, d, generator=g, device=dev).to(bf) for h in (hq, hkv, hkv)]
+
+    def yset():
+        return [torch.randn(P, n, h, d, generator=g, device=dev).to(bf) for h in (hq // P, 1, 1)]
+
+    xs, ys = [xset(), xset()], [yset(), yset()]
+    for i in range(2):
+        vl.sp_qkv_seq2head(*xs[i], P, out=ys[i])
+        vl.sp_qkv_head2seq(*ys[i], hkv, out=xs[i])
+    vl.profile_enable(True)
+    for i in range(steps):
+        vl.sp_qkv_seq2head(*xs[i % 2], P, out=ys[i % 2])     # alternate buffers: > MALL
+        vl.sp_qkv_head2seq(*ys[(i + 1) % 2], hkv, out=xs[(i + 1) % 2])
+    prof = vl.profile_read()
+    vl.profile_enable(False)
+    nbytes = sum(t.numel() * 2 for t in xs[0]) + sum(t.numel() * 2 for t in ys[0])
+    del xs, ys
+    return prof, {"sp_qkv_seq2head": nbytes, "sp_qkv_head2seq": nbytes}
+
+
 def bench_ring(vl, torch, dev, steps):
     import numpy as np
     import workloads
@@ -368,6 +396,9 @@ def main():
         perm = kernel_table(prof, {}, by)
         perm["device_copy_same_bytes_gbs"] = measured_copy_gbs(torch, dev, by["sp_seq2head"] // 2)
         extra["ulysses_permute_49152x32x128_P8"] = perm
+        print("[bench] qkv permute", file=sys.stderr, flush=True)
+        prof, by = bench_qkv_permute(vl, torch, dev, 10)
+        extra["ulysses_qkv_permute_49152_q32_kv4_d128_P8"] = kernel_table(prof, {}, by)
         print("[bench] measured GEMM peak", file=sys.stderr, flush=True)
         extra["measured_bf16_gemm_tflops"] = measured_gemm_peak(torch, dev)
         print("[bench] ring share", file=sys.stderr, flush=True)

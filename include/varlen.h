@@ -190,6 +190,72 @@ VL_API int sp_head2seq(const void* y, void* x, int64_t n_tokens, int32_t n_heads
                 int32_t head_dim, int32_t sp_degree, int32_t elem_bytes, void* stream);
 
 /*
+ * sp_qkv_seq2head - the send-side packs of Q, K and V for one Ulysses
+ * exchange in a single launch, with the kv heads of grouped-query attention
+ * split over the ranks (HSAP page, Section 2.2.2; BASP page, Section II-C and
+ * Figure 2: Q, K and V are all moved from the sequence split to the head
+ * split; NSP page, Section 2.1).  After the exchange rank p holds query heads
+ * [p Hq/P, (p+1) Hq/P); query head h reads kv head h * Hkv / Hq, so rank p
+ * needs hk kv heads:
+ *   Hkv >= P:  hk = Hkv/P, kv heads [p hk, (p+1) hk)
+ *   Hkv <  P:  hk = 1, kv head p / (P/Hkv), sent to each of the P/Hkv ranks
+ *              that read it (replicated)
+ *   yq[p, t, j, :] = q[t, p*Hq/P + j, :]
+ *   yk[p, t, j, :] = k[t, g0(p) + j, :]   (likewise yv), g0 as above
+ *
+ *   q            [n_tokens, n_heads_q, head_dim]
+ *   k, v         [n_tokens, n_heads_kv, head_dim]
+ *   yq           [sp_degree, n_tokens, n_heads_q / sp_degree, head_dim]
+ *   yk, yv       [sp_degree, n_tokens, hk, head_dim]
+ *   dtype        VL_BF16 or VL_F32 (element size only: the pack is a copy)
+ *   sp_degree and n_heads_kv divide n_heads_q; one of sp_degree, n_heads_kv
+ *   divides the other; head_dim * element size a multiple of 4 bytes; every
+ *   pointer 4-byte aligned.  No output may overlap an input or another
+ *   output.  Bit-exact copy.
+ * Errors: VL_EINVAL, VL_ESHAPE, VL_EUNSUPPORTED, VL_EHIP.
+ */
+VL_API int sp_qkv_seq2head(const void* q, const void* k, const void* v, void* yq, void* yk,
+                    void* yv, int64_t n_tokens, int32_t n_heads_q, int32_t n_heads_kv,
+                    int32_t head_dim, int32_t sp_degree, int32_t dtype, void* stream);
+
+/*
+ * sp_qkv_head2seq - the receive-side unpacks of dQ, dK and dV after the
+ * gradient exchange, in a single launch: the adjoint of sp_qkv_seq2head.
+ *   dq[t, p*Hq/P + j, :] = yq[p, t, j, :]
+ *   Hkv >= P:  dk[t, p hk + j, :] = yk[p, t, j, :]        (likewise dv)
+ *   Hkv <  P:  dk[t, g, :] = sum over the r = P/Hkv ranks p = g r .. g r + r - 1
+ *              of yk[p, t, 0, :], added in that order in fp32 and rounded once
+ *              to the output dtype (bf16: nearest, ties to even)
+ * Arguments and constraints as sp_qkv_seq2head, with the [P, n, h, d]
+ * tensors as sources and dq [n, Hq, d], dk/dv [n, Hkv, d] as destinations.
+ * Deterministic; bit-exact copy when Hkv >= P.
+ */
+VL_API int sp_qkv_head2seq(const void* yq, const void* yk, const void* yv, void* dq, void* dk,
+                    void* dv, int64_t n_tokens, int32_t n_heads_q, int32_t n_heads_kv,
+                    int32_t head_dim, int32_t sp_degree, int32_t dtype, void* stream);
+
+/*
+ * basp_shard - host-only: batch-aware sequence partitioning (BASP page,
+ * Section IV-A/B, Algorithms 1 and 2, Figure 4).  world ranks, a micro-batch
+ * of `batch` sequences of seq_len tokens each.  Ranks form groups of
+ * K = world / batch consecutive ranks (group g = ranks g K .. g K + K - 1);
+ * group g takes sequence g and its rank at local position l = rank mod K
+ * holds tokens [l seq_len / K, (l+1) seq_len / K), so each group runs its own
+ * K-way exchange (sp_degree = K).  batch > world falls back to data
+ * parallelism: K = 1 and rank r holds sequences [r b, (r+1) b), b =
+ * batch / world, whole.
+ *
+ *   outputs      group, group_size (K), sequences [seq_begin, seq_end),
+ *                tokens [tok_begin, tok_end) of each of them
+ * Errors: VL_EINVAL (null output), VL_ESHAPE (rank out of range, world not a
+ * multiple of batch (or batch of world when batch > world), seq_len not a
+ * multiple of K).
+ */
+VL_API int basp_shard(int32_t rank, int32_t world, int32_t batch, int64_t seq_len,
+               int32_t* group, int32_t* group_size, int32_t* seq_begin, int32_t* seq_end,
+               int64_t* tok_begin, int64_t* tok_end);
+
+/*
  * varlen_schedule_export - host-only: the work list the kernels run for these
  * cu_seqlens (no GPU needed).  Documents are cut into query tiles of *bq rows
  * and key tiles of *bk rows, never crossing a document; tile pairs holding no

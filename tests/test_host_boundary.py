@@ -241,3 +241,44 @@ def test_ring_block_rejects_overlapping_unequal_chunks():
     with pytest.raises(vl.VarlenError) as e:
         vl.varlen_ring_block([0, 5, 3], (0, 3), (0, 3))
     assert e.value.code == -3
+
+
+def test_qkv_permute_rejects_bad_arguments():
+    L = vl.lib()
+    a, b, c = (ctypes.c_void_p(FAKE * m) for m in (1, 64, 128))
+    x, y, z = (ctypes.c_void_p(FAKE * m) for m in (256, 512, 1024))
+    ok = (a, b, c, x, y, z)
+    for fn in (L.sp_qkv_seq2head, L.sp_qkv_head2seq):
+        assert fn(*ok, 16, 6, 2, 128, 4, 0, None) == -2        # 4 does not divide Hq = 6
+        assert fn(*ok, 16, 8, 3, 128, 4, 0, None) == -2        # Hkv = 3 does not divide 8
+        assert fn(*ok, 16, 12, 3, 128, 2, 0, None) == -2       # neither of 2, 3 divides the other
+        assert fn(*ok, 16, 8, 2, 128, 4, 2, None) == -1        # dtype
+        assert fn(*ok, 16, 8, 2, 1, 4, 0, None) == -4          # a bf16 head of 2 bytes
+        assert fn(None, b, c, x, y, z, 16, 8, 2, 128, 4, 0, None) == -1
+        assert fn(a, b, c, x, y, ctypes.c_void_p(FAKE * 1024 + 2), 16, 8, 2, 128, 4, 0,
+                  None) == -1                                  # misaligned
+        assert fn(a, b, c, x, x, z, 16, 8, 2, 128, 4, 0, None) == -1   # outputs overlap
+        assert fn(a, b, c, a, y, z, 16, 8, 2, 128, 4, 0, None) == -1   # output on an input
+        assert fn(*ok, -1, 8, 2, 128, 4, 0, None) == -2
+        assert fn(*ok, 0, 8, 2, 128, 4, 0, None) == 0           # nothing to do
+
+
+@pytest.mark.parametrize("N,B", [(1, 1), (8, 1), (8, 2), (8, 4), (8, 8), (6, 3), (4, 8), (2, 6)])
+def test_basp_shard_matches_oracle(N, B):
+    from oracle import sp_groups
+    L = 48
+    K = sp_groups.group_size(N, B)
+    for r in range(N):
+        got = vl.basp_shard(r, N, B, L)
+        assert (got["seq_begin"], got["seq_end"], got["tok_begin"], got["tok_end"]) == \
+            sp_groups.shard(r, N, B, L)
+        assert got["group_size"] == K
+        assert r in sp_groups.groups(N, B)[got["group"]]
+
+
+@pytest.mark.parametrize("args", [(0, 4, 3, 12), (0, 3, 2, 12), (0, 8, 2, 10), (0, 4, 6, 8),
+                                  (4, 4, 2, 8), (-1, 4, 2, 8), (0, 0, 1, 4), (0, 4, 2, -2)])
+def test_basp_shard_rejects(args):
+    with pytest.raises(vl.VarlenError) as e:
+        vl.basp_shard(*args)
+    assert e.value.code == -2

@@ -10,6 +10,9 @@ Entry points (same names as the C ABI in ``include/varlen.h``):
   varlen_attn_bwd(q, k, v, o, do, lse, cu_q, cu_k, causal=True, scale=None) -> (dq, dk, dv)
   attn_lse_merge(o_parts, lse_parts, out_dtype=bf16) -> (o, lse)
   sp_seq2head(x, sp_degree) -> y ;  sp_head2seq(y) -> x
+  sp_qkv_seq2head(q, k, v, sp_degree) -> (yq, yk, yv)
+  sp_qkv_head2seq(yq, yk, yv, n_heads_kv) -> (dq, dk, dv)
+  basp_shard(rank, world, batch, seq_len) -> dict (host only)
   varlen_schedule_export(cu_q, cu_k, causal, pass_, head_dim) -> dict (host only)
   varlen_ring_block(cu, q_range, k_range) -> (cu_q, cu_k, causal, cls) (host only)
 """
@@ -31,7 +34,8 @@ STATUS = {0: "VL_OK", -1: "VL_EINVAL", -2: "VL_ESHAPE", -3: "VL_ESEQLENS",
 EXPORTS = ["varlen_attn_fwd", "varlen_attn_bwd_workspace_size", "varlen_attn_bwd",
            "attn_lse_merge", "sp_seq2head", "sp_head2seq", "varlen_schedule_export",
            "varlen_last_error", "varlen_cache_clear", "varlen_version", "varlen_profile_enable",
-           "varlen_profile_read", "varlen_ring_block", "varlen_attn_fwd_acc"]
+           "varlen_profile_read", "varlen_ring_block", "varlen_attn_fwd_acc", "sp_qkv_seq2head",
+           "sp_qkv_head2seq", "basp_shard"]
 
 RING_CLASSES = ("N", "A1", "A2", "A3", "A4", "A5")
 
@@ -75,6 +79,11 @@ def lib():
     for n in ("sp_seq2head", "sp_head2seq"):
         getattr(L, n).argtypes = [vp, vp, i64, i32, i32, i32, i32, vp]
         getattr(L, n).restype = ctypes.c_int
+    for n in ("sp_qkv_seq2head", "sp_qkv_head2seq"):
+        getattr(L, n).argtypes = [vp, vp, vp, vp, vp, vp, i64, i32, i32, i32, i32, i32, vp]
+        getattr(L, n).restype = ctypes.c_int
+    L.basp_shard.argtypes = [i32, i32, i32, i64, pi32, pi32, pi32, pi32, pi64, pi64]
+    L.basp_shard.restype = ctypes.c_int
     L.varlen_schedule_export.argtypes = [pi32, pi32, i32, i32, i32, i32, pi32, i64, pi64, pi64,
                                          pi64, pi32, pi32]
     L.varlen_schedule_export.restype = ctypes.c_int
@@ -242,6 +251,63 @@ def sp_head2seq(y, out=None):
     _check(lib().sp_head2seq(_dev_ptr(y), _dev_ptr(out), n, P * h, d, P, y.element_size(),
                              _stream()))
     return out
+
+
+def _qkv_dtype(*ts):
+    import torch
+    dts = {t.dtype for t in ts}
+    if len(dts) != 1 or dts.pop() not in (torch.bfloat16, torch.float32):
+        raise TypeError("tensors must all be bfloat16 or all float32")
+    return VL_BF16 if ts[0].dtype == torch.bfloat16 else VL_F32
+
+
+def sp_qkv_seq2head(q, k, v, sp_degree: int, out=None):
+    """Pack q [n,Hq,d], k/v [n,Hkv,d] for the Ulysses exchange in one launch.
+
+    Returns (yq [P,n,Hq/P,d], yk, yv [P,n,hk,d]) with hk = Hkv/P, or 1 with each
+    kv head replicated to the P/Hkv ranks that read it when Hkv < P."""
+    import torch
+    n, hq, d = q.shape
+    hkv = k.shape[1]
+    if k.shape != v.shape or k.shape[0] != n or k.shape[2] != d:
+        raise ValueError("k and v must be [n, Hkv, d] with q's n and d")
+    hk = hkv // sp_degree if hkv >= sp_degree else 1
+    if out is None:
+        out = (torch.empty((sp_degree, n, hq // sp_degree, d), dtype=q.dtype, device=q.device),
+               torch.empty((sp_degree, n, hk, d), dtype=q.dtype, device=q.device),
+               torch.empty((sp_degree, n, hk, d), dtype=q.dtype, device=q.device))
+    dt = _qkv_dtype(q, k, v, *out)
+    _check(lib().sp_qkv_seq2head(_dev_ptr(q), _dev_ptr(k), _dev_ptr(v), *map(_dev_ptr, out), n, hq,
+                                 hkv, d, sp_degree, dt, _stream()))
+    return out
+
+
+def sp_qkv_head2seq(yq, yk, yv, n_heads_kv: int, out=None):
+    """Unpack (dq, dk, dv) after the gradient exchange in one launch; the
+    adjoint of sp_qkv_seq2head (replicated kv heads are summed in fp32)."""
+    import torch
+    P, n, hq, d = yq.shape
+    if yk.shape != yv.shape:
+        raise ValueError("yk and yv must have the same shape")
+    if out is None:
+        out = (torch.empty((n, P * hq, d), dtype=yq.dtype, device=yq.device),
+               torch.empty((n, n_heads_kv, d), dtype=yq.dtype, device=yq.device),
+               torch.empty((n, n_heads_kv, d), dtype=yq.dtype, device=yq.device))
+    dt = _qkv_dtype(yq, yk, yv, *out)
+    _check(lib().sp_qkv_head2seq(_dev_ptr(yq), _dev_ptr(yk), _dev_ptr(yv), *map(_dev_ptr, out), n,
+                                 P * hq, n_heads_kv, d, P, dt, _stream()))
+    return out
+
+
+def basp_shard(rank: int, world: int, batch: int, seq_len: int) -> dict:
+    """Host-only: the batch-aware group and token shard of ``rank``."""
+    i32 = [ctypes.c_int32(0) for _ in range(4)]
+    i64 = [ctypes.c_int64(0) for _ in range(2)]
+    _check(lib().basp_shard(rank, world, batch, seq_len, *map(ctypes.byref, i32),
+                            *map(ctypes.byref, i64)))
+    g, k, s0, s1 = (x.value for x in i32)
+    return {"group": g, "group_size": k, "seq_begin": s0, "seq_end": s1,
+            "tok_begin": i64[0].value, "tok_end": i64[1].value}
 
 
 def varlen_schedule_export(cu_q, cu_k, causal: bool, pass_: int, head_dim: int) -> dict:

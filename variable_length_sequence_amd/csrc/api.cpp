@@ -345,6 +345,100 @@ int sp_head2seq(const void* y, void* x, int64_t n_tokens, int32_t n_heads, int32
   }
 }
 
+static int qkv_common(const void* const src[3], void* const dst[3], int64_t n_tokens,
+                      int32_t n_heads_q, int32_t n_heads_kv, int32_t head_dim, int32_t sp_degree,
+                      int32_t dtype, int dir, void* stream) {
+  g_err.clear();
+  if (n_tokens < 0 || n_heads_q <= 0 || n_heads_kv <= 0 || head_dim <= 0 || sp_degree <= 0)
+    return fail(VL_ESHAPE, "sizes must be positive");
+  if (n_heads_q % sp_degree) return fail(VL_ESHAPE, "sp_degree must divide n_heads_q");
+  if (n_heads_q % n_heads_kv) return fail(VL_ESHAPE, "n_heads_kv must divide n_heads_q");
+  if (n_heads_kv % sp_degree && sp_degree % n_heads_kv)
+    return fail(VL_ESHAPE, "one of sp_degree, n_heads_kv must divide the other");
+  if (dtype != VL_BF16 && dtype != VL_F32) return fail(VL_EINVAL, "dtype must be VL_BF16 or VL_F32");
+  const int64_t eb = dtype == VL_BF16 ? 2 : 4;
+  if (head_dim * eb % 4) return fail(VL_EUNSUPPORTED, "head_dim * element size must be a multiple of 4 bytes");
+  if (n_tokens >= (int64_t(1) << 31)) return fail(VL_ESHAPE, "n_tokens must fit int32");
+  if (int64_t(n_heads_q) * head_dim * eb >= (int64_t(1) << 30))
+    return fail(VL_ESHAPE, "a token row must be below 1 GiB");
+  if (n_tokens == 0) return VL_OK;
+  const int64_t hk = n_heads_kv >= sp_degree ? n_heads_kv / sp_degree : 1;
+  // bytes of the [n, H, d] side and of the [P, n, hs, d] side, for Q, K, V
+  const int64_t xb[3] = {n_tokens * n_heads_q * head_dim * eb, n_tokens * n_heads_kv * head_dim * eb,
+                         n_tokens * n_heads_kv * head_dim * eb};
+  const int64_t yb[3] = {xb[0], sp_degree * n_tokens * hk * head_dim * eb,
+                         sp_degree * n_tokens * hk * head_dim * eb};
+  const char* lo[6];
+  int64_t len[6];
+  for (int i = 0; i < 3; ++i) {
+    if (!src[i] || !dst[i]) return fail(VL_EINVAL, "tensors must be non-null");
+    if ((reinterpret_cast<uintptr_t>(src[i]) | reinterpret_cast<uintptr_t>(dst[i])) % 4)
+      return fail(VL_EINVAL, "tensors must be 4-byte aligned");
+    lo[i] = reinterpret_cast<const char*>(src[i]);
+    lo[3 + i] = reinterpret_cast<const char*>(dst[i]);
+    len[i] = dir == 0 ? xb[i] : yb[i];
+    len[3 + i] = dir == 0 ? yb[i] : xb[i];
+  }
+  // an output may overlap no input and no other output (inputs may alias each other)
+  for (int a = 3; a < 6; ++a)
+    for (int b = 0; b < 6; ++b)
+      if (a != b && lo[a] < lo[b] + len[b] && lo[b] < lo[a] + len[a])
+        return fail(VL_EINVAL, "an output overlaps another tensor");
+  vl::QkvTensors t{{src[0], src[1], src[2]}, {dst[0], dst[1], dst[2]}};
+  hipError_t e = vl::launch_sp_qkv(t, n_tokens, n_heads_q, n_heads_kv, head_dim, sp_degree, dtype,
+                                   dir, reinterpret_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "sp_qkv launch");
+  return VL_OK;
+}
+
+int sp_qkv_seq2head(const void* q, const void* k, const void* v, void* yq, void* yk, void* yv,
+                    int64_t n_tokens, int32_t n_heads_q, int32_t n_heads_kv, int32_t head_dim,
+                    int32_t sp_degree, int32_t dtype, void* stream) {
+  try {
+    const void* src[3] = {q, k, v};
+    void* dst[3] = {yq, yk, yv};
+    return qkv_common(src, dst, n_tokens, n_heads_q, n_heads_kv, head_dim, sp_degree, dtype, 0,
+                      stream);
+  } catch (...) {
+    return fail(VL_EHIP, "internal error");
+  }
+}
+
+int sp_qkv_head2seq(const void* yq, const void* yk, const void* yv, void* dq, void* dk, void* dv,
+                    int64_t n_tokens, int32_t n_heads_q, int32_t n_heads_kv, int32_t head_dim,
+                    int32_t sp_degree, int32_t dtype, void* stream) {
+  try {
+    const void* src[3] = {yq, yk, yv};
+    void* dst[3] = {dq, dk, dv};
+    return qkv_common(src, dst, n_tokens, n_heads_q, n_heads_kv, head_dim, sp_degree, dtype, 1,
+                      stream);
+  } catch (...) {
+    return fail(VL_EHIP, "internal error");
+  }
+}
+
+int basp_shard(int32_t rank, int32_t world, int32_t batch, int64_t seq_len, int32_t* group,
+               int32_t* group_size, int32_t* seq_begin, int32_t* seq_end, int64_t* tok_begin,
+               int64_t* tok_end) {
+  try {
+    g_err.clear();
+    if (!group || !group_size || !seq_begin || !seq_end || !tok_begin || !tok_end)
+      return fail(VL_EINVAL, "null argument");
+    vl::BaspShard sh;
+    std::string err;
+    if (!vl::basp_shard(rank, world, batch, seq_len, sh, err)) return fail(VL_ESHAPE, err);
+    *group = sh.group;
+    *group_size = sh.group_size;
+    *seq_begin = sh.seq_begin;
+    *seq_end = sh.seq_end;
+    *tok_begin = sh.tok_begin;
+    *tok_end = sh.tok_end;
+    return VL_OK;
+  } catch (...) {
+    return fail(VL_EINVAL, "internal error");
+  }
+}
+
 int varlen_ring_block(const int32_t* cu_seqlens, int32_t n_docs, int64_t q_begin, int64_t q_end,
                       int64_t k_begin, int64_t k_end, int32_t* cu_q_out, int32_t* cu_k_out,
                       int32_t* causal_out, int32_t* cls_out) {

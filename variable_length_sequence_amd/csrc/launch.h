@@ -14,6 +14,19 @@ hipError_t launch_sp_permute(const void* src, void* dst, int64_t n_tokens, int32
                              int32_t head_dim, int32_t sp_degree, int32_t elem_bytes, int dir,
                              hipStream_t stream);
 
+// Q, K and V (or dQ, dK, dV) of one Ulysses exchange in one launch, with the
+// kv heads of grouped-query attention split over the ranks (replicated when
+// n_heads_kv < sp_degree; their gradients summed on the way back).
+// dir 0: src = x-side tensors [n, H, d], dst = [P, n, hs, d];
+// dir 1: src = [P, n, hs, d], dst = [n, H, d].  dtype VL_BF16 (0) / VL_F32 (1).
+struct QkvTensors {
+  const void* src[3];
+  void* dst[3];
+};
+hipError_t launch_sp_qkv(const QkvTensors& t, int64_t n_tokens, int32_t n_heads_q,
+                         int32_t n_heads_kv, int32_t head_dim, int32_t sp_degree, int32_t dtype,
+                         int dir, hipStream_t stream);
+
 constexpr int kMaxMergeParts = 64;
 
 hipError_t launch_lse_merge(int32_t n_parts, const void* const* o_parts,

@@ -186,4 +186,25 @@ bool ring_block(const int32_t* cu, int32_t n_docs, int64_t q_begin, int64_t q_en
   return true;
 }
 
+bool basp_shard(int32_t rank, int32_t world, int32_t batch, int64_t seq_len, BaspShard& out,
+                std::string& err) {
+  if (world <= 0 || batch <= 0) return err = "world and batch must be positive", false;
+  if (rank < 0 || rank >= world) return err = "rank out of range", false;
+  if (seq_len < 0) return err = "seq_len must be >= 0", false;
+  if (batch > world) {
+    // more sequences than ranks: plain data parallelism, whole sequences
+    if (batch % world) return err = "batch must be a multiple of world when batch > world", false;
+    const int32_t per = batch / world;
+    out = BaspShard{rank, 1, rank * per, (rank + 1) * per, 0, seq_len};
+    return true;
+  }
+  if (world % batch) return err = "world must be a multiple of batch", false;
+  const int32_t k = world / batch;
+  if (seq_len % k) return err = "seq_len must be a multiple of the group size", false;
+  const int32_t g = rank / k, l = rank % k;
+  const int64_t chunk = seq_len / k;
+  out = BaspShard{g, k, g, g + 1, l * chunk, (l + 1) * chunk};
+  return true;
+}
+
 }  // namespace vl

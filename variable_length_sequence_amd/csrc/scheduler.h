@@ -71,4 +71,18 @@ bool ring_block(const int32_t* cu, int32_t n_docs, int64_t q_begin, int64_t q_en
                 int64_t k_begin, int64_t k_end, int32_t* cu_q, int32_t* cu_k, int32_t& causal,
                 int32_t& cls, std::string& err);
 
+// Batch-aware sequence partitioning (BASP page, Section IV-A/B, Algorithms 1
+// and 2): world ranks and a micro-batch of `batch` sequences of seq_len
+// tokens.  Groups are K = world / batch consecutive ranks; group g takes
+// sequence g and its rank at local position l holds tokens
+// [l seq_len / K, (l+1) seq_len / K).  batch > world falls back to data
+// parallelism (K = 1, rank r holds sequences [r b, (r+1) b), b = batch/world,
+// whole).  Returns false with err set when the sizes do not divide.
+struct BaspShard {
+  int32_t group, group_size, seq_begin, seq_end;
+  int64_t tok_begin, tok_end;
+};
+bool basp_shard(int32_t rank, int32_t world, int32_t batch, int64_t seq_len, BaspShard& out,
+                std::string& err);
+
 }  // namespace vl
