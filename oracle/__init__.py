@@ -16,12 +16,13 @@ Modules
   schedule   cu_seqlens validation, the tile work lists and the pair counts,
              and the packed-chunk attention-pattern map
   sp_groups  batch-aware sequence-parallel groups and token shards
+  router     the NSP planner: SP tree, per-GPU cost model, beam-search routing
 
 Every function cites the passage of the pages it follows (page title and
 section / equation / figure).  Where the pages are silent, the reading taken is
 named in the docstring.
 """
-from . import attention, merge, permute, schedule, sp_groups  # noqa: F401
+from . import attention, merge, permute, router, schedule, sp_groups  # noqa: F401
 from .attention import (attn_fwd, attn_bwd, attn_fwd_rows, attn_bwd_dq_rows,  # noqa: F401
                         attn_bwd_dkv_rows)
 from .merge import lse_merge  # noqa: F401
