@@ -272,6 +272,28 @@ def bench_qkv_permute(vl, torch, dev, steps):
     return prof, {"sp_qkv_seq2head": nbytes, "sp_qkv_head2seq": nbytes}
 
 
+def bench_router(vl, reps=20):
+    """Host-only: NSP routing of the Pareto batch onto a 64-GPU SP tree with
+    the cost model fed by this library's measured throughput curve."""
+    import workloads
+    w = workloads.mixed_128k()
+    P = 64
+    cm = vl.ulysses_cost_model(w.hq, w.hkv, w.d, sp_max=P)
+    budget = 2.0 * sum(w.lengths) / P
+    t0 = time.perf_counter()
+    for _ in range(reps):
+        r = vl.nsp_route(w.lengths, P, P, cm, budget, 8, 16, True)
+    us = (time.perf_counter() - t0) / reps * 1e6
+    static = vl.nsp_plan_cost(w.lengths, [(0, 0)] * len(w.lengths), P, P, cm)
+    leaves = vl.nsp_route(w.lengths, P, P, cm, budget, 0, 1)
+    degs = sorted({P >> d for d, _ in r["plan"]}, reverse=True)
+    return {"samples": len(w.lengths), "gpus": P, "prefix": 8, "beam": 16, "monotone": True,
+            "us_per_plan": round(us, 1), "load_ms": round(r["load"] * 1e3, 4),
+            "static_sp64_load_ms": round(static["load"] * 1e3, 4),
+            "leaves_only_load_ms": round(leaves["load"] * 1e3, 4), "sp_degrees_used": degs,
+            "within_budget": r["within_budget"]}
+
+
 def bench_ring(vl, torch, dev, steps):
     import numpy as np
     import workloads
@@ -399,6 +421,8 @@ def main():
         print("[bench] qkv permute", file=sys.stderr, flush=True)
         prof, by = bench_qkv_permute(vl, torch, dev, 10)
         extra["ulysses_qkv_permute_49152_q32_kv4_d128_P8"] = kernel_table(prof, {}, by)
+        print("[bench] router", file=sys.stderr, flush=True)
+        extra["nsp_route_mixed_128k_64gpus"] = bench_router(vl)
         print("[bench] measured GEMM peak", file=sys.stderr, flush=True)
         extra["measured_bf16_gemm_tflops"] = measured_gemm_peak(torch, dev)
         print("[bench] ring share", file=sys.stderr, flush=True)

@@ -306,6 +306,82 @@ VL_API int varlen_ring_block(const int32_t* cu_seqlens, int32_t n_docs,
                              int32_t* causal_out, int32_t* cls_out);
 
 /*
+ * vl_cost_model - the per-GPU cost model the NSP planner scores plans with
+ * (NSP page, Section 4.1.2).  For a sample of length L routed to an SP tree
+ * node of degree s, each of the node's GPUs pays, per pass (fwd / bwd):
+ *   compute   flops_per_pair * L (L + 1) / 2 / s FLOPs at the per-GPU
+ *             throughput measured for documents of length L (piecewise
+ *             linear between curve points, clamped outside);
+ *   exchange  for s > 1, per phase (prologue, epilogue),
+ *             ((s - 1) / s) * (L / s) * bytes_per_token[phase] / a2a_gbs, plus
+ *             a latency alpha (s - 1) once per non-empty node and phase (the
+ *             alpha-beta all-to-all model of the BASP page, Section IV);
+ *   dense     (L / s) * dense_*_flops_per_token / dense_tflops.
+ *
+ *   n_points, curve_len[n_points] (strictly increasing, > 0),
+ *   fwd_tflops / bwd_tflops[n_points] (> 0): host arrays, read during the call
+ *   bytes_per_token: fwd prologue, fwd epilogue, bwd prologue, bwd epilogue
+ */
+typedef struct vl_cost_model {
+  int32_t n_points;
+  const double* curve_len;
+  const double* fwd_tflops;
+  const double* bwd_tflops;
+  double fwd_flops_per_pair;
+  double bwd_flops_per_pair;
+  double bytes_per_token[4];
+  double a2a_gbs;
+  double a2a_alpha_us;
+  double dense_fwd_flops_per_token;
+  double dense_bwd_flops_per_token;
+  double dense_tflops;
+} vl_cost_model;
+
+/*
+ * nsp_route - host-only: route a batch of samples onto the SP tree (NSP page,
+ * Section 4.1.1 Definition 1 and Figure 4; Section 4.1.3 Algorithm 1).
+ * The tree over sp_max = 2^K GPUs has nodes (depth d, index i), an SP group
+ * of degree 2^(K-d) on ranks [i 2^(K-d), (i+1) 2^(K-d)); n_gpus / sp_max
+ * trees sit side by side.  Samples are taken longest first (ties by index);
+ * the first `prefix` are searched with a beam of `beam` states (every
+ * enabled node tried, states whose token peak max_p T_p exceeds
+ * token_budget dropped, the `beam` with the smallest max_p C_p kept, ties in
+ * generation order); each surviving state is completed by placing the rest,
+ * longest first, on the least-loaded node of the deepest enabled level that
+ * keeps the budget (else the one with the smallest token load); the completed
+ * state with the smallest max_p C_p is returned.  T_p = sum of L_j / |R| over
+ * the nodes on p's chain; C_p = forward + backward stage time of GPU p.
+ *
+ *   lengths       [n_samples] host, >= 0
+ *   level_mask    bit d enables depth d (-1: all)
+ *   monotone      non-zero: a longer sample never takes a smaller SP degree
+ *                 than a shorter one
+ *   node_depth, node_index   [n_samples] outputs: the node of each sample
+ *   gpu_fwd, gpu_bwd, gpu_tokens   [n_gpus] outputs (each may be NULL)
+ *   within_budget            output: 1 if max_p T_p <= token_budget (may be NULL)
+ * Work is O(prefix * beam * nodes * n_gpus).  If no prefix extension keeps
+ * the budget, the `beam` with the smallest token peak are kept and the plan
+ * is reported over budget.
+ * Errors: VL_EINVAL (null, negative or non-finite input, bad cost model),
+ * VL_ESHAPE (sp_max not a power of two dividing n_gpus, no level enabled).
+ */
+VL_API int nsp_route(const int64_t* lengths, int32_t n_samples, int32_t n_gpus, int32_t sp_max,
+              const vl_cost_model* cost, double token_budget, int32_t prefix, int32_t beam,
+              int32_t monotone, int32_t level_mask, int32_t* node_depth, int32_t* node_index,
+              double* gpu_fwd, double* gpu_bwd, double* gpu_tokens, int32_t* within_budget);
+
+/*
+ * nsp_plan_cost - host-only: the per-GPU forward / backward stage times and
+ * token loads of a given plan (node_depth / node_index per sample, as
+ * nsp_route returns them) under the same cost model.
+ * Errors: VL_EINVAL, VL_ESHAPE (a node outside the tree).
+ */
+VL_API int nsp_plan_cost(const int64_t* lengths, int32_t n_samples, int32_t n_gpus,
+                  int32_t sp_max, const vl_cost_model* cost, const int32_t* node_depth,
+                  const int32_t* node_index, double* gpu_fwd, double* gpu_bwd,
+                  double* gpu_tokens);
+
+/*
  * varlen_profile_enable / varlen_profile_read - optional per-kernel timing.
  * While enabled, every kernel the library launches is bracketed by two HIP
  * events recorded on its launch stream.  Enabling clears earlier records.

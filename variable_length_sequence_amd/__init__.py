@@ -13,6 +13,8 @@ Entry points (same names as the C ABI in ``include/varlen.h``):
   sp_qkv_seq2head(q, k, v, sp_degree) -> (yq, yk, yv)
   sp_qkv_head2seq(yq, yk, yv, n_heads_kv) -> (dq, dk, dv)
   basp_shard(rank, world, batch, seq_len) -> dict (host only)
+  nsp_route(lengths, n_gpus, sp_max, cost, token_budget, prefix, beam) -> dict (host only)
+  nsp_plan_cost(lengths, plan, n_gpus, sp_max, cost) -> dict (host only)
   varlen_schedule_export(cu_q, cu_k, causal, pass_, head_dim) -> dict (host only)
   varlen_ring_block(cu, q_range, k_range) -> (cu_q, cu_k, causal, cls) (host only)
 """
@@ -20,6 +22,7 @@ from __future__ import annotations
 
 import ctypes
 import os
+from dataclasses import dataclass
 from typing import List, Optional, Sequence
 
 import numpy as np
@@ -35,7 +38,7 @@ EXPORTS = ["varlen_attn_fwd", "varlen_attn_bwd_workspace_size", "varlen_attn_bwd
            "attn_lse_merge", "sp_seq2head", "sp_head2seq", "varlen_schedule_export",
            "varlen_last_error", "varlen_cache_clear", "varlen_version", "varlen_profile_enable",
            "varlen_profile_read", "varlen_ring_block", "varlen_attn_fwd_acc", "sp_qkv_seq2head",
-           "sp_qkv_head2seq", "basp_shard"]
+           "sp_qkv_head2seq", "basp_shard", "nsp_route", "nsp_plan_cost"]
 
 RING_CLASSES = ("N", "A1", "A2", "A3", "A4", "A5")
 
@@ -46,6 +49,16 @@ class VarlenError(RuntimeError):
     def __init__(self, code: int, msg: str):
         super().__init__(f"{STATUS.get(code, code)}: {msg}")
         self.code = code
+
+
+class _CostModelC(ctypes.Structure):
+    _fields_ = [("n_points", ctypes.c_int32), ("curve_len", ctypes.POINTER(ctypes.c_double)),
+                ("fwd_tflops", ctypes.POINTER(ctypes.c_double)),
+                ("bwd_tflops", ctypes.POINTER(ctypes.c_double)),
+                ("fwd_flops_per_pair", ctypes.c_double), ("bwd_flops_per_pair", ctypes.c_double),
+                ("bytes_per_token", ctypes.c_double * 4), ("a2a_gbs", ctypes.c_double),
+                ("a2a_alpha_us", ctypes.c_double), ("dense_fwd_flops_per_token", ctypes.c_double),
+                ("dense_bwd_flops_per_token", ctypes.c_double), ("dense_tflops", ctypes.c_double)]
 
 
 _lib = None
@@ -84,6 +97,13 @@ def lib():
         getattr(L, n).restype = ctypes.c_int
     L.basp_shard.argtypes = [i32, i32, i32, i64, pi32, pi32, pi32, pi32, pi64, pi64]
     L.basp_shard.restype = ctypes.c_int
+    pd = ctypes.POINTER(ctypes.c_double)
+    L.nsp_route.argtypes = [pi64, i32, i32, i32, ctypes.POINTER(_CostModelC), ctypes.c_double, i32,
+                            i32, i32, i32, pi32, pi32, pd, pd, pd, pi32]
+    L.nsp_route.restype = ctypes.c_int
+    L.nsp_plan_cost.argtypes = [pi64, i32, i32, i32, ctypes.POINTER(_CostModelC), pi32, pi32, pd,
+                                pd, pd]
+    L.nsp_plan_cost.restype = ctypes.c_int
     L.varlen_schedule_export.argtypes = [pi32, pi32, i32, i32, i32, i32, pi32, i64, pi64, pi64,
                                          pi64, pi32, pi32]
     L.varlen_schedule_export.restype = ctypes.c_int
@@ -308,6 +328,111 @@ def basp_shard(rank: int, world: int, batch: int, seq_len: int) -> dict:
     g, k, s0, s1 = (x.value for x in i32)
     return {"group": g, "group_size": k, "seq_begin": s0, "seq_end": s1,
             "tok_begin": i64[0].value, "tok_end": i64[1].value}
+
+
+@dataclass
+class CostModel:
+    """Inputs of the NSP planner's per-GPU cost model (``vl_cost_model`` in
+    include/varlen.h).  bytes_per_token: fwd prologue, fwd epilogue, bwd
+    prologue, bwd epilogue."""
+    curve_len: Sequence[float]
+    fwd_tflops: Sequence[float]
+    bwd_tflops: Sequence[float]
+    fwd_flops_per_pair: float
+    bwd_flops_per_pair: float
+    bytes_per_token: Sequence[float]
+    a2a_gbs: float
+    a2a_alpha_us: float
+    dense_fwd_flops_per_token: float = 0.0
+    dense_bwd_flops_per_token: float = 0.0
+    dense_tflops: float = 1.0
+
+    def _c(self):
+        arrs = [np.ascontiguousarray(np.asarray(a, dtype=np.float64))
+                for a in (self.curve_len, self.fwd_tflops, self.bwd_tflops)]
+        if not (len(arrs[0]) == len(arrs[1]) == len(arrs[2])):
+            raise ValueError("curve arrays must have the same length")
+        pd = ctypes.POINTER(ctypes.c_double)
+        c = _CostModelC(len(arrs[0]), *(a.ctypes.data_as(pd) for a in arrs),
+                        float(self.fwd_flops_per_pair), float(self.bwd_flops_per_pair),
+                        (ctypes.c_double * 4)(*map(float, self.bytes_per_token)),
+                        float(self.a2a_gbs), float(self.a2a_alpha_us),
+                        float(self.dense_fwd_flops_per_token),
+                        float(self.dense_bwd_flops_per_token), float(self.dense_tflops))
+        return c, arrs   # keep the arrays alive while the struct is in use
+
+
+CURVE_PATH = os.path.join(_HERE, "attn_curve_mi355x.json")
+
+
+def ulysses_cost_model(n_heads_q: int, n_heads_kv: int, head_dim: int, sp_max: int,
+                       curve: Optional[dict] = None, a2a_gbs: float = 7 * 153.0,
+                       a2a_alpha_us: float = 10.0, elem_bytes: int = 2,
+                       dense_fwd_flops_per_token: float = 0.0,
+                       dense_bwd_flops_per_token: float = 0.0,
+                       dense_tflops: float = 1000.0) -> CostModel:
+    """Cost model of Ulysses attention with this library's kernels.
+
+    Useful FLOPs per visible pair: 4 d Hq forward, 10 d Hq backward.  Exchanged
+    bytes per token: forward prologue Q, K, V (kv heads counted once per rank
+    that reads them: max(Hkv, sp_max) when Hkv < sp_max), forward epilogue O,
+    backward prologue dO, backward epilogue dQ, dK, dV.  The throughput curve is
+    the measured one shipped with the library (``attn_curve_mi355x.json``,
+    written by ``measure_curve.py``) unless one is given; the all-to-all
+    defaults are an MI355X node's 7 xGMI links of about 153 GB/s each."""
+    import json
+    if curve is None:
+        with open(CURVE_PATH) as fh:
+            curve = json.load(fh)
+    kv = max(n_heads_kv, sp_max) if n_heads_kv < sp_max else n_heads_kv
+    row = head_dim * elem_bytes
+    return CostModel(curve["len"], curve["fwd_tflops"], curve["bwd_tflops"],
+                     4.0 * head_dim * n_heads_q, 10.0 * head_dim * n_heads_q,
+                     ((n_heads_q + 2 * kv) * row, n_heads_q * row, n_heads_q * row,
+                      (n_heads_q + 2 * kv) * row),
+                     a2a_gbs, a2a_alpha_us, dense_fwd_flops_per_token, dense_bwd_flops_per_token,
+                     dense_tflops)
+
+
+def _lengths(lengths) -> np.ndarray:
+    return np.ascontiguousarray(np.asarray(lengths, dtype=np.int64).reshape(-1))
+
+
+def nsp_route(lengths, n_gpus: int, sp_max: int, cost: CostModel, token_budget: float,
+              prefix: int = 8, beam: int = 16, monotone: bool = False, level_mask: int = -1) -> dict:
+    """Host-only: NSP routing of a batch onto the SP tree.  Returns the node
+    (depth, index) of each sample, per-GPU stage times, token loads, the load
+    proxy max fwd + max bwd and whether the token budget holds."""
+    L = _lengths(lengths)
+    n = len(L)
+    depth, index = np.zeros(max(n, 1), np.int32), np.zeros(max(n, 1), np.int32)
+    f, b, t = (np.zeros(n_gpus, np.float64) for _ in range(3))
+    ok = ctypes.c_int32(0)
+    c, keep = cost._c()
+    pd = ctypes.POINTER(ctypes.c_double)
+    _check(lib().nsp_route(L.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)), n, n_gpus, sp_max,
+                           ctypes.byref(c), float(token_budget), prefix, beam, int(monotone),
+                           level_mask, _iptr(depth), _iptr(index), f.ctypes.data_as(pd),
+                           b.ctypes.data_as(pd), t.ctypes.data_as(pd), ctypes.byref(ok)))
+    return {"plan": [(int(depth[j]), int(index[j])) for j in range(n)], "gpu_fwd": f,
+            "gpu_bwd": b, "gpu_cost": f + b, "gpu_tokens": t,
+            "load": float(f.max() + b.max()) if n_gpus else 0.0, "within_budget": bool(ok.value)}
+
+
+def nsp_plan_cost(lengths, plan, n_gpus: int, sp_max: int, cost: CostModel) -> dict:
+    """Host-only: per-GPU stage times and token loads of a given plan."""
+    L = _lengths(lengths)
+    n = len(L)
+    depth = np.ascontiguousarray(np.array([d for d, _ in plan] or [0], np.int32))
+    index = np.ascontiguousarray(np.array([i for _, i in plan] or [0], np.int32))
+    f, b, t = (np.zeros(n_gpus, np.float64) for _ in range(3))
+    c, keep = cost._c()
+    pd = ctypes.POINTER(ctypes.c_double)
+    _check(lib().nsp_plan_cost(L.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)), n, n_gpus,
+                               sp_max, ctypes.byref(c), _iptr(depth), _iptr(index),
+                               f.ctypes.data_as(pd), b.ctypes.data_as(pd), t.ctypes.data_as(pd)))
+    return {"gpu_fwd": f, "gpu_bwd": b, "gpu_cost": f + b, "gpu_tokens": t,
+            "load": float(f.max() + b.max())}
 
 
 def varlen_schedule_export(cu_q, cu_k, causal: bool, pass_: int, head_dim: int) -> dict:

@@ -18,7 +18,7 @@ CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libvarlen.so")
 
-SOURCES = ["scheduler.cpp", "api.cpp", "profiler.cpp", "sp_permute.hip", "lse_merge.hip", "attn_fwd.hip",
+SOURCES = ["scheduler.cpp", "router.cpp", "api.cpp", "profiler.cpp", "sp_permute.hip", "lse_merge.hip", "attn_fwd.hip",
            "attn_bwd.hip"]
 
 ARCH = "gfx950"
@@ -40,6 +40,10 @@ def _compile(src: str, verbose: bool) -> str:
     cmd = [hipcc(), *COMMON, "-I", os.path.join(ROOT, "include")]
     if src.endswith(".hip"):
         cmd += ["-x", "hip", *DEVICE]
+    else:
+        # host code: no contraction into fused multiply-adds, so the planner's
+        # floating-point decisions follow the written order of operations
+        cmd += ["-ffp-contract=off"]
     cmd += ["-c", os.path.join(CSRC, src), "-o", obj]
     if verbose:
         print(" ".join(cmd), file=sys.stderr)

@@ -11,6 +11,7 @@
 
 #include "varlen.h"
 #include "launch.h"
+#include "router.h"
 #include "scheduler.h"
 
 namespace {
@@ -436,6 +437,128 @@ int basp_shard(int32_t rank, int32_t world, int32_t batch, int64_t seq_len, int3
     return VL_OK;
   } catch (...) {
     return fail(VL_EINVAL, "internal error");
+  }
+}
+
+static bool finite_nonneg(double x) { return std::isfinite(x) && x >= 0.0; }
+
+static int cost_params(const vl_cost_model* c, vl::CostParams& cm) {
+  if (!c) return fail(VL_EINVAL, "cost model is null");
+  if (c->n_points < 1 || !c->curve_len || !c->fwd_tflops || !c->bwd_tflops)
+    return fail(VL_EINVAL, "cost model needs a throughput curve of >= 1 point");
+  for (int32_t i = 0; i < c->n_points; ++i) {
+    if (!(std::isfinite(c->curve_len[i]) && c->curve_len[i] > 0) ||
+        (i > 0 && !(c->curve_len[i] > c->curve_len[i - 1])))
+      return fail(VL_EINVAL, "curve lengths must be positive and strictly increasing");
+    if (!(std::isfinite(c->fwd_tflops[i]) && c->fwd_tflops[i] > 0) ||
+        !(std::isfinite(c->bwd_tflops[i]) && c->bwd_tflops[i] > 0))
+      return fail(VL_EINVAL, "curve throughputs must be positive");
+  }
+  const double scalars[] = {c->fwd_flops_per_pair, c->bwd_flops_per_pair, c->bytes_per_token[0],
+                            c->bytes_per_token[1], c->bytes_per_token[2], c->bytes_per_token[3],
+                            c->a2a_alpha_us, c->dense_fwd_flops_per_token,
+                            c->dense_bwd_flops_per_token};
+  for (double x : scalars)
+    if (!finite_nonneg(x)) return fail(VL_EINVAL, "cost model terms must be finite and >= 0");
+  if (!(std::isfinite(c->a2a_gbs) && c->a2a_gbs > 0) ||
+      !(std::isfinite(c->dense_tflops) && c->dense_tflops > 0))
+    return fail(VL_EINVAL, "bandwidth and dense throughput must be positive");
+  cm.curve_len.assign(c->curve_len, c->curve_len + c->n_points);
+  cm.fwd_tflops.assign(c->fwd_tflops, c->fwd_tflops + c->n_points);
+  cm.bwd_tflops.assign(c->bwd_tflops, c->bwd_tflops + c->n_points);
+  cm.fwd_flops_per_pair = c->fwd_flops_per_pair;
+  cm.bwd_flops_per_pair = c->bwd_flops_per_pair;
+  for (int i = 0; i < 4; ++i) cm.bytes_per_token[i] = c->bytes_per_token[i];
+  cm.a2a_gbs = c->a2a_gbs;
+  cm.a2a_alpha_us = c->a2a_alpha_us;
+  cm.dense_fwd_flops_per_token = c->dense_fwd_flops_per_token;
+  cm.dense_bwd_flops_per_token = c->dense_bwd_flops_per_token;
+  cm.dense_tflops = c->dense_tflops;
+  return VL_OK;
+}
+
+static int sample_lengths(const int64_t* lengths, int32_t n, std::vector<double>& L) {
+  if (n < 0) return fail(VL_EINVAL, "n_samples must be >= 0");
+  if (n > 0 && !lengths) return fail(VL_EINVAL, "lengths is null");
+  L.resize(size_t(n));
+  for (int32_t j = 0; j < n; ++j) {
+    if (lengths[j] < 0) return fail(VL_EINVAL, "lengths must be >= 0");
+    L[j] = double(lengths[j]);
+  }
+  return VL_OK;
+}
+
+static void copy_out(const std::vector<double>& v, double* dst) {
+  if (dst) std::memcpy(dst, v.data(), sizeof(double) * v.size());
+}
+
+int nsp_route(const int64_t* lengths, int32_t n_samples, int32_t n_gpus, int32_t sp_max,
+              const vl_cost_model* cost, double token_budget, int32_t prefix, int32_t beam,
+              int32_t monotone, int32_t level_mask, int32_t* node_depth, int32_t* node_index,
+              double* gpu_fwd, double* gpu_bwd, double* gpu_tokens, int32_t* within_budget) {
+  try {
+    g_err.clear();
+    std::vector<double> L;
+    vl::CostParams cm;
+    int rc = sample_lengths(lengths, n_samples, L);
+    if (rc) return rc;
+    if ((rc = cost_params(cost, cm))) return rc;
+    if (n_samples > 0 && (!node_depth || !node_index)) return fail(VL_EINVAL, "node outputs are null");
+    if (std::isnan(token_budget)) return fail(VL_EINVAL, "token_budget is NaN");
+    if (prefix < 0 || beam < 1) return fail(VL_EINVAL, "prefix must be >= 0 and beam >= 1");
+    std::vector<vl::TreeNode> nodes;
+    vl::RouteResult r;
+    std::string err;
+    if (!vl::sp_tree(n_gpus, sp_max, level_mask, nodes, err)) return fail(VL_ESHAPE, err);
+    if (!vl::nsp_route(L, n_gpus, sp_max, cm, token_budget, prefix, beam, monotone != 0,
+                       level_mask, nodes, r, err))
+      return fail(VL_EINVAL, err);
+    for (int32_t j = 0; j < n_samples; ++j) {
+      node_depth[j] = nodes[r.node[j]].depth;
+      node_index[j] = nodes[r.node[j]].index;
+    }
+    copy_out(r.dfwd, gpu_fwd);
+    copy_out(r.dbwd, gpu_bwd);
+    copy_out(r.tok, gpu_tokens);
+    if (within_budget) *within_budget = r.within_budget ? 1 : 0;
+    return VL_OK;
+  } catch (const std::exception& ex) {
+    return fail(VL_EINVAL, std::string("internal error: ") + ex.what());
+  }
+}
+
+int nsp_plan_cost(const int64_t* lengths, int32_t n_samples, int32_t n_gpus, int32_t sp_max,
+                  const vl_cost_model* cost, const int32_t* node_depth, const int32_t* node_index,
+                  double* gpu_fwd, double* gpu_bwd, double* gpu_tokens) {
+  try {
+    g_err.clear();
+    std::vector<double> L;
+    vl::CostParams cm;
+    int rc = sample_lengths(lengths, n_samples, L);
+    if (rc) return rc;
+    if ((rc = cost_params(cost, cm))) return rc;
+    if (n_samples > 0 && (!node_depth || !node_index)) return fail(VL_EINVAL, "plan is null");
+    std::vector<vl::TreeNode> nodes;
+    std::string err;
+    if (!vl::sp_tree(n_gpus, sp_max, -1, nodes, err)) return fail(VL_ESHAPE, err);
+    // node (d, i) sits at offset (trees (2^d - 1)) + i in the full node list
+    const int32_t trees = n_gpus / sp_max;
+    const int32_t K = nodes.back().depth;
+    std::vector<int32_t> node_of(static_cast<size_t>(n_samples));
+    for (int32_t j = 0; j < n_samples; ++j) {
+      const int32_t d = node_depth[j], i = node_index[j];
+      if (d < 0 || d > K || i < 0 || i >= (trees << d))
+        return fail(VL_ESHAPE, "a node lies outside the tree");
+      node_of[j] = trees * ((1 << d) - 1) + i;
+    }
+    std::vector<double> f, b, t;
+    vl::nsp_plan_cost(L, nodes, node_of, n_gpus, cm, f, b, t);
+    copy_out(f, gpu_fwd);
+    copy_out(b, gpu_bwd);
+    copy_out(t, gpu_tokens);
+    return VL_OK;
+  } catch (const std::exception& ex) {
+    return fail(VL_EINVAL, std::string("internal error: ") + ex.what());
   }
 }
 
