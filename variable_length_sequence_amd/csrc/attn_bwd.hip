@@ -584,7 +584,7 @@ hipError_t run_bwd(const AttnShape& s, const uint16_t* q, const uint16_t* k, con
   if (s.total_q > 0 || acc_n4 > 0) {
     constexpr int RPB = kThreads / (D / 8);
     const int64_t want = std::max((s.total_q * s.hq + RPB - 1) / RPB, (acc_n4 + kThreads - 1) / kThreads);
-    const int blocks = int(std::max<int64_t>(1, std::min<int64_t>(want, int64_t(n_cu) * 16)));
+    const int blocks = int(std::max<int64_t>(1, std::min<int64_t>(want, int64_t(1) << 30)));
     ProfScope prof("bwd_pre", stream);
     hipLaunchKernelGGL((bwd_pre_kernel<D>), dim3(blocks), dim3(kThreads), 0, stream, o, dout,
                        delta, s.total_q, s.hq, reinterpret_cast<f32x4*>(dkv_acc), acc_n4);

@@ -115,11 +115,9 @@ hipError_t dispatch(const PartPtrs& p, int n_parts, int64_t n_rows, int n_heads,
   const int lanes_per_row = head_dim / 4;
   const int rows_per_block = kThreads / lanes_per_row;
   const int64_t n_pairs = n_rows * n_heads;
-  int dev = 0, n_cu = 256;
-  (void)hipGetDevice(&dev);
-  (void)hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev);
   const int64_t want = (n_pairs + rows_per_block - 1) / rows_per_block;
-  const int blocks = int(std::max<int64_t>(1, std::min<int64_t>(want, int64_t(n_cu) * 16)));
+  // one pass of the grid-stride loop: more rows in flight than a capped grid
+  const int blocks = int(std::max<int64_t>(1, std::min<int64_t>(want, int64_t(1) << 30)));
   ProfScope prof("lse_merge", stream);
 #define VL_MERGE_CASE(N)                                                                     \
   case N:                                                                                    \
