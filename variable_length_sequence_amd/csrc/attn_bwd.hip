@@ -105,6 +105,28 @@ __device__ __forceinline__ void mfma_chain(Load load, Mac mac) {
   __builtin_amdgcn_sched_group_barrier(0x008, PF, SYNC);
 }
 
+// The same chain with every step fenced, so the LDS reads keep their distance
+// PF from the MFMA that uses them.  The group barriers above pin only the
+// kinds of instructions, and the scheduler may fill a chain's read slots with
+// other reads of the region and sink the chain's own reads to just before
+// their MFMA.  The dQ kernel runs 1-2 % faster with the fenced form; the
+// dK/dV kernel runs faster with the pinned-kinds form.
+template <int N, int PF, typename Load, typename Mac>
+__device__ __forceinline__ void mfma_chain_fenced(Load load, Mac mac) {
+  bf16x8 r[PF];
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int f = 0; f < PF; ++f) r[f] = load(f);
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int f = 0; f < N; ++f) {
+    const bf16x8 a = r[f % PF];
+    mac(f, a);
+    if (f + PF < N) r[f % PF] = load(f + PF);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+}
+
 // ---------------------------------------------------------------- dK, dV
 constexpr int KB_Q = kBwdBQ;   // 32 query rows per step
 constexpr int KB_K = kBwdBK;   // 128 keys per workgroup
@@ -502,7 +524,7 @@ attn_bwd_dq_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ 
       const int prow = kb * 32 + l32;
       // S^T and dP^T chains interleaved; fragment f = (st, K or V), read
       // four fragments ahead
-      mfma_chain<2 * NKS, 4, 0>(
+      mfma_chain_fenced<2 * NKS, 4>(
           [&](int f) {
             const uint16_t* t = (f & 1) ? vs : ks;
             return as_bf16x8(*reinterpret_cast<const u32x4*>(&t[SwzTile<D>::chunk(prow, 2 * (f >> 1) + half)]));
@@ -535,7 +557,7 @@ attn_bwd_dq_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ 
     }
 
     // dQ^T += K^T dS^T; fragment f = (cb, kb, hs), read transposed, two ahead
-    mfma_chain<4 * NCB, 2, 1, 2>(
+    mfma_chain_fenced<4 * NCB, 2>(
         [&](int f) { return tr_frag<D>(ks, lane, 16 * (f & 3), 32 * (f >> 2)); },
         [&](int f, const bf16x8& a) { acc[f >> 2] = mfma32(a, dsf[(f >> 1) & 1][f & 1], acc[f >> 2]); });
   };
