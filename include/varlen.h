@@ -16,7 +16,9 @@
  *   - Device work is enqueued on `stream` (a hipStream_t; NULL = the null
  *     stream) and the call returns without waiting, except the first call
  *     with a new cu_seqlens pattern, which uploads that pattern's work list
- *     synchronously and caches it (see varlen_cache_clear).
+ *     synchronously and caches it (see varlen_cache_clear).  Later calls
+ *     with that pattern only launch kernels (no allocation, copy or memset),
+ *     so they can be captured into a HIP graph.
  *   - bf16 values are IEEE binary32 truncated to the top 16 bits; results are
  *     rounded to nearest-even.  Scores, softmax and accumulation are fp32.
  */

@@ -201,15 +201,16 @@ def varlen_attn_fwd_acc(q, k, v, cu_q, cu_k, o_acc, lse_acc, causal: bool = True
 
 
 def varlen_attn_bwd(q, k, v, o, do, lse, cu_q, cu_k, causal: bool = True,
-                    scale: Optional[float] = None, workspace=None):
-    """Packed varlen attention backward -> (dq, dk, dv), bf16."""
+                    scale: Optional[float] = None, workspace=None, dq=None, dk=None, dv=None):
+    """Packed varlen attention backward -> (dq, dk, dv), bf16 (written into the
+    given tensors when passed)."""
     import torch
     cq, ck = _cu_host(cu_q), _cu_host(cu_k)
     tq, hq, d = q.shape
     tk, hkv, _ = k.shape
-    dq = torch.empty_like(q)
-    dk = torch.empty_like(k)
-    dv = torch.empty_like(v)
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
     need = lib().varlen_attn_bwd_workspace_size(tq, tk, hq, hkv, d)
     if workspace is None:
         workspace = torch.empty(max(int(need), 256), dtype=torch.uint8, device=q.device)
