@@ -101,15 +101,14 @@ def test_packing_invariance_and_determinism_bitwise():
     dev = require_gpu()
     rng = np.random.default_rng(21)
     lq, lk, q, k, v, do = random_case(rng, 5, 1, 400, 8, 2, 128, seed=21)
-    # O, LSE and dQ are bitwise deterministic and packing invariant.  dK/dV are
-    # summed over a kv group's q heads; when the library splits the group over
-    # several workgroups that sum runs in fp32 atomics, so only the tolerance holds.
+    # Every output is bitwise deterministic; O, LSE and dQ are also packing
+    # invariant.  dK/dV sum a kv group's q heads, and how the library splits
+    # that group over workgroups depends on the whole batch (the partial sums
+    # are added in split order), so a document alone matches to tolerance.
     a = _run(q, k, v, do, lq, lk, True, dev)
     b = _run(q, k, v, do, lq, lk, True, dev)
-    for n in ("o", "lse", "dq"):
+    for n in ("o", "lse", "dq", "dk", "dv"):
         assert torch.equal(a[n], b[n]), f"{n} not deterministic"
-    for n in ("dk", "dv"):
-        assert rel_fro(f64(a[n]), f64(b[n])) < 1e-2
     cu = workloads.cu_seqlens(lq)
     for i, L in enumerate(lq):
         s, e = int(cu[i]), int(cu[i + 1])

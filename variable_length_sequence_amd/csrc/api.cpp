@@ -136,6 +136,15 @@ float resolve_scale(float s, int d) { return s > 0.f ? s : 1.0f / std::sqrt(floa
 
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
+// The largest q-head split the backward may choose: a power of two dividing
+// the group size, at most vl::kMaxHeadSplit.
+int max_head_split(int32_t hq, int32_t hkv) {
+  const int grp = hkv > 0 ? hq / hkv : 1;
+  int split = 1;
+  while (split < grp && grp % (split * 2) == 0 && split * 2 <= vl::kMaxHeadSplit) split *= 2;
+  return split;
+}
+
 }  // namespace
 
 extern "C" {
@@ -211,7 +220,8 @@ size_t varlen_attn_bwd_workspace_size(int64_t total_q, int64_t total_k, int32_t 
                                       int32_t n_heads_kv, int32_t head_dim) {
   if (total_q < 0 || total_k < 0 || n_heads_q <= 0 || n_heads_kv <= 0 || head_dim <= 0) return 0;
   return align256(size_t(total_q) * size_t(n_heads_q) * 4) +
-         align256(2 * size_t(total_k) * size_t(n_heads_kv) * size_t(head_dim) * 4);
+         align256(size_t(max_head_split(n_heads_q, n_heads_kv)) * 2 * size_t(total_k) *
+                  size_t(n_heads_kv) * size_t(head_dim) * 4);
 }
 
 int varlen_attn_bwd(const void* q, const void* k, const void* v, const void* out, const void* dout,
@@ -253,7 +263,7 @@ int varlen_attn_bwd(const void* q, const void* k, const void* v, const void* out
     {
       const double total = double(pb.total_count) * grp * n_heads_kv;
       const double per_cu = total / double(n_cu);
-      while (split < grp && grp % (split * 2) == 0 &&
+      while (split < max_head_split(n_heads_q, n_heads_kv) &&
              double(pb.max_count) * grp / split > per_cu)
         split *= 2;
     }

@@ -7,9 +7,8 @@
 //   dS_ij = P_ij (dP_ij - D_i),
 //   dV_j = sum_i P_ij dO_i,  dK_j = scale sum_i dS_ij Q_i,  dQ_i = scale sum_j dS_ij K_j.
 //
-// Three kernels, no atomics on dQ:
-//   1. bwd_pre: D = rowsum(dO * O) in fp32, [Hq, T]; clears the fp32 dK/dV
-//      accumulator when kernel 2 uses it.
+// Three kernels (four with a q-head split), no atomics:
+//   1. bwd_pre: D = rowsum(dO * O) in fp32, [Hq, T].
 //   2. dkdv: one workgroup per (128-key tile of a document, kv head[, slice of
 //      its q heads]); each wave owns 32 keys and keeps their K, V operands and
 //      fp32 dK, dV accumulators in registers while 32-row query tiles of every
@@ -19,6 +18,10 @@
 //      in the A-operand layout of dV += P^T dO and dK += dS^T Q.
 //   3. dq: the forward's mapping (a lane owns one query): S^T = K Q^T and
 //      dP^T = V dO^T per 64-key tile, then dQ^T += K^T dS^T.
+//   With the q heads of a group split over workgroups, each split stores its
+//   fp32 dK/dV partial and a fourth kernel adds the partials in split order
+//   (plain stores run at several times the rate of fp32 atomic adds, and the
+//   sum is deterministic).
 // The extra two contractions of (3) replace a zeroed fp32 dQ accumulator, its
 // atomics and a conversion pass, and keep dQ deterministic.
 #include <hip/hip_runtime.h>
@@ -36,16 +39,10 @@ namespace {
 constexpr int kThreads = 256;
 
 // ---------------------------------------------------------------- D = rowsum(dO O)
-// It also clears the fp32 dK/dV accumulator (acc_n4 float4s; 0 when the
-// dK/dV kernel writes its results directly).
 template <int D>
 __global__ void __launch_bounds__(kThreads)
 bwd_pre_kernel(const uint16_t* __restrict__ o, const uint16_t* __restrict__ dout,
-               float* __restrict__ delta, int64_t total_q, int hq, f32x4* __restrict__ dkv_acc,
-               int64_t acc_n4) {
-  for (int64_t i = int64_t(blockIdx.x) * kThreads + threadIdx.x; i < acc_n4;
-       i += int64_t(gridDim.x) * kThreads)
-    dkv_acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+               float* __restrict__ delta, int64_t total_q, int hq) {
   constexpr int LPR = D / 8;                 // lanes per (row, head)
   constexpr int RPB = kThreads / LPR;        // rows per block
   const int sub = threadIdx.x / LPR;
@@ -71,13 +68,22 @@ bwd_pre_kernel(const uint16_t* __restrict__ o, const uint16_t* __restrict__ dout
   }
 }
 
-// fp32 [T, H, D] accumulator -> bf16
+// dK and dV of a split q-head group: the sum of the splits' fp32 partials
+// ([split][dK, dV][T, H, D]), added in split order (deterministic), -> bf16
 __global__ void __launch_bounds__(kThreads)
-f32_to_bf16_kernel(const f32x4* __restrict__ src, u32x2* __restrict__ dst, int64_t n4) {
-  for (int64_t i = int64_t(blockIdx.x) * kThreads + threadIdx.x; i < n4;
+f32_to_bf16_kernel(const f32x4* __restrict__ src, u32x2* __restrict__ dk, u32x2* __restrict__ dv,
+                   int64_t n4, int n_split) {
+  for (int64_t i = int64_t(blockIdx.x) * kThreads + threadIdx.x; i < 2 * n4;
        i += int64_t(gridDim.x) * kThreads) {
-    const f32x4 x = src[i];
-    dst[i] = u32x2{pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3])};
+    const int t = i >= n4;
+    const int64_t j = i - t * n4;
+    f32x4 x = src[int64_t(t) * n4 + j];
+    for (int sp = 1; sp < n_split; ++sp) {
+      const f32x4 y = src[(int64_t(sp) * 2 + t) * n4 + j];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) x[e] += y[e];
+    }
+    (t ? dv : dk)[j] = u32x2{pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3])};
   }
 }
 
@@ -398,7 +404,7 @@ attn_bwd_dkdv_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
 
   // epilogue: lane holds column c = 32 cb + l32 of keys 32 w + 8 (v/4) + 4 half + v%4
   uint16_t* outp = role == 0 ? dv : dk;
-  float* accp = dkv_acc + (role == 0 ? total_k * kv_tok : 0);
+  float* accp = dkv_acc + (int64_t(split) * 2 + (role == 0 ? 1 : 0)) * total_k * kv_tok;
 #pragma unroll
   for (int cb = 0; cb < NCB; ++cb) {
 #pragma unroll
@@ -409,7 +415,7 @@ attn_bwd_dkdv_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
         if (head_split == 1)
           outp[idx] = __builtin_bit_cast(uint16_t, (__bf16)acc[cb][i]);
         else
-          atomicAdd(accp + idx, acc[cb][i]);
+          accp[idx] = acc[cb][i];
       }
     }
   }
@@ -587,29 +593,20 @@ attn_bwd_dq_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ 
   }
 }
 
-int device_cus() {
-  int dev = 0, n = 256;
-  (void)hipGetDevice(&dev);
-  (void)hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev);
-  return n;
-}
-
 template <int D>
 hipError_t run_bwd(const AttnShape& s, const uint16_t* q, const uint16_t* k, const uint16_t* v,
                    const uint16_t* o, const uint16_t* dout, const float* lse,
                    const ItemMap& fwd_map, const ItemMap& bwd_map, int32_t head_split,
                    uint16_t* dq, uint16_t* dk, uint16_t* dv, float* delta, float* dkv_acc,
                    hipStream_t stream) {
-  const int n_cu = device_cus();
   const int64_t kv_elems = s.total_k * s.hkv * D;
-  const int64_t acc_n4 = head_split > 1 ? 2 * kv_elems / 4 : 0;
-  if (s.total_q > 0 || acc_n4 > 0) {
+  if (s.total_q > 0) {
     constexpr int RPB = kThreads / (D / 8);
-    const int64_t want = std::max((s.total_q * s.hq + RPB - 1) / RPB, (acc_n4 + kThreads - 1) / kThreads);
+    const int64_t want = (s.total_q * s.hq + RPB - 1) / RPB;
     const int blocks = int(std::max<int64_t>(1, std::min<int64_t>(want, int64_t(1) << 30)));
     ProfScope prof("bwd_pre", stream);
     hipLaunchKernelGGL((bwd_pre_kernel<D>), dim3(blocks), dim3(kThreads), 0, stream, o, dout,
-                       delta, s.total_q, s.hq, reinterpret_cast<f32x4*>(dkv_acc), acc_n4);
+                       delta, s.total_q, s.hq);
   }
   if (bwd_map.rows > 0) {
     const dim3 grid(unsigned(bwd_map.rows) * unsigned(kXcds) * unsigned(s.hkv * head_split));
@@ -620,13 +617,11 @@ hipError_t run_bwd(const AttnShape& s, const uint16_t* q, const uint16_t* k, con
   }
   if (head_split > 1 && kv_elems > 0) {
     const int64_t n4 = kv_elems / 4;
-    const int blocks = int(std::min<int64_t>((n4 + kThreads - 1) / kThreads, int64_t(n_cu) * 16));
+    const int blocks = int(std::max<int64_t>(1, (2 * n4 + kThreads - 1) / kThreads));
     ProfScope prof("bwd_dkv_convert", stream);
     hipLaunchKernelGGL(f32_to_bf16_kernel, dim3(blocks), dim3(kThreads), 0, stream,
-                       reinterpret_cast<const f32x4*>(dkv_acc), reinterpret_cast<u32x2*>(dk), n4);
-    hipLaunchKernelGGL(f32_to_bf16_kernel, dim3(blocks), dim3(kThreads), 0, stream,
-                       reinterpret_cast<const f32x4*>(dkv_acc + kv_elems),
-                       reinterpret_cast<u32x2*>(dv), n4);
+                       reinterpret_cast<const f32x4*>(dkv_acc), reinterpret_cast<u32x2*>(dk),
+                       reinterpret_cast<u32x2*>(dv), n4, int(head_split));
   }
   if (fwd_map.rows > 0) {
     const dim3 grid(unsigned(fwd_map.rows) * unsigned(kXcds) * unsigned(s.hq));

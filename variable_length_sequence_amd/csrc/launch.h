@@ -67,8 +67,10 @@ hipError_t launch_attn_fwd(const AttnShape& s, const void* q, const void* k, con
                            hipStream_t stream);
 
 // Backward: D_i = dO_i . O_i, then dK/dV over the kv-tile list, then dQ over
-// the query-tile list.  dkv_acc is fp32 [2, total_k, hkv, d] scratch used when
-// q heads of one group are split over several workgroups (head_split > 1).
+// the query-tile list.  When the q heads of one group are split over
+// head_split > 1 workgroups, dkv_acc holds their fp32 partials
+// [head_split][dK, dV][total_k, hkv, d], summed by a conversion kernel.
+constexpr int kMaxHeadSplit = 4;
 hipError_t launch_attn_bwd(const AttnShape& s, const void* q, const void* k, const void* v,
                            const void* o, const void* dout, const float* lse,
                            const ItemMap& fwd_map, const ItemMap& bwd_map,
