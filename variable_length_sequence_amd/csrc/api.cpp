@@ -30,13 +30,12 @@ int hip_fail(hipError_t e, const char* what) {
 
 // ------------------------------------------------------------ work-list cache
 struct Plan {
-  vl::DevItem* dev = nullptr;   // one allocation: the items, then their XCD slots
-  int32_t* slot = nullptr;
+  vl::DevItem* dev = nullptr;   // the items in XCD slot order (rows * kXcds entries)
   int32_t n = 0;
   int32_t rows = 0;             // items of the longest XCD list
   int32_t max_count = 0;
   int64_t total_count = 0;
-  vl::ItemMap map() const { return vl::ItemMap{dev, slot, rows}; }
+  vl::ItemMap map() const { return vl::ItemMap{dev, rows}; }
 };
 
 std::mutex g_mu;
@@ -92,18 +91,25 @@ int get_plan(int pass, int causal, const int32_t* cu_q, const int32_t* cu_k, int
       (void)hipDeviceSynchronize();
       clear_plans_locked();
     }
-    const size_t b_items = di.size() * sizeof(vl::DevItem);
-    std::vector<char> host(b_items + slots.size() * sizeof(int32_t));
-    std::memcpy(host.data(), di.data(), b_items);
-    std::memcpy(host.data() + b_items, slots.data(), slots.size() * sizeof(int32_t));
-    e = hipMalloc(&p.dev, host.size());
+    // items in slot order, so a workgroup reads its item with one load;
+    // an empty slot has doc = -1
+    std::vector<vl::DevItem> host(slots.size());
+    for (size_t j = 0; j < slots.size(); ++j) {
+      if (slots[j] >= 0) {
+        host[j] = di[size_t(slots[j])];
+      } else {
+        host[j] = vl::DevItem{};
+        host[j].doc = -1;
+      }
+    }
+    const size_t bytes = host.size() * sizeof(vl::DevItem);
+    e = hipMalloc(&p.dev, bytes);
     if (e != hipSuccess) return hip_fail(e, "hipMalloc(work list)");
-    e = hipMemcpy(p.dev, host.data(), host.size(), hipMemcpyHostToDevice);
+    e = hipMemcpy(p.dev, host.data(), bytes, hipMemcpyHostToDevice);
     if (e != hipSuccess) {
       (void)hipFree(p.dev);
       return hip_fail(e, "hipMemcpy(work list)");
     }
-    p.slot = reinterpret_cast<int32_t*>(reinterpret_cast<char*>(p.dev) + b_items);
   }
   g_plans.emplace(key, p);
   out = p;

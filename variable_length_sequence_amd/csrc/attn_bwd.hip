@@ -168,7 +168,7 @@ __global__ void __launch_bounds__(kKvThreads)
 attn_bwd_dkdv_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
                      const uint16_t* __restrict__ v, const uint16_t* __restrict__ dout,
                      const float* __restrict__ lse, const float* __restrict__ delta,
-                     const DevItem* __restrict__ items, const int32_t* __restrict__ slot,
+                     const DevItem* __restrict__ items,
                      int hq, int hkv, int head_split, float scale, int causal, int64_t total_q,
                      uint16_t* __restrict__ dk, uint16_t* __restrict__ dv,
                      float* __restrict__ dkv_acc, int64_t total_k) {
@@ -181,11 +181,10 @@ attn_bwd_dkdv_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
   const int xcd = b & (kXcds - 1);
   const int r = b / kXcds;
   const int per_item = hkv * head_split;
-  const int item_idx = slot[(r / per_item) * kXcds + xcd];
+  const DevItem it = items[(r / per_item) * kXcds + xcd];
   const int g = (r % per_item) / head_split;
   const int split = r % head_split;
-  if (item_idx < 0) return;
-  const DevItem it = items[item_idx];
+  if (it.doc < 0) return;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -439,7 +438,7 @@ __global__ void __launch_bounds__(kThreads, 2)
 attn_bwd_dq_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
                    const uint16_t* __restrict__ v, const uint16_t* __restrict__ dout,
                    const float* __restrict__ lse, const float* __restrict__ delta,
-                   const DevItem* __restrict__ items, const int32_t* __restrict__ slot, int hq,
+                   const DevItem* __restrict__ items, int hq,
                    int hkv, float scale, int causal, int64_t total_q, uint16_t* __restrict__ dq) {
   constexpr int NKS = D / 16;
   constexpr int NCB = D / 32;
@@ -448,10 +447,9 @@ attn_bwd_dq_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ 
   const int b = blockIdx.x;
   const int xcd = b & (kXcds - 1);
   const int r = b / kXcds;
-  const int item_idx = slot[(r / hq) * kXcds + xcd];
+  const DevItem it = items[(r / hq) * kXcds + xcd];
   const int h = r % hq;
-  if (item_idx < 0) return;
-  const DevItem it = items[item_idx];
+  if (it.doc < 0) return;
   const int g = h / (hq / hkv);
 
   const int tid = threadIdx.x;
@@ -612,7 +610,7 @@ hipError_t run_bwd(const AttnShape& s, const uint16_t* q, const uint16_t* k, con
     const dim3 grid(unsigned(bwd_map.rows) * unsigned(kXcds) * unsigned(s.hkv * head_split));
     ProfScope prof("bwd_dkdv", stream);
     hipLaunchKernelGGL((attn_bwd_dkdv_kernel<D>), grid, dim3(kKvThreads), 0, stream, q, k, v, dout,
-                       lse, delta, bwd_map.items, bwd_map.slot, s.hq, s.hkv, head_split, s.scale,
+                       lse, delta, bwd_map.items, s.hq, s.hkv, head_split, s.scale,
                        s.causal, s.total_q, dk, dv, dkv_acc, s.total_k);
   }
   if (head_split > 1 && kv_elems > 0) {
@@ -627,7 +625,7 @@ hipError_t run_bwd(const AttnShape& s, const uint16_t* q, const uint16_t* k, con
     const dim3 grid(unsigned(fwd_map.rows) * unsigned(kXcds) * unsigned(s.hq));
     ProfScope prof("bwd_dq", stream);
     hipLaunchKernelGGL((attn_bwd_dq_kernel<D>), grid, dim3(kThreads), 0, stream, q, k, v, dout, lse,
-                       delta, fwd_map.items, fwd_map.slot, s.hq, s.hkv, s.scale, s.causal,
+                       delta, fwd_map.items, s.hq, s.hkv, s.scale, s.causal,
                        s.total_q, dq);
   }
   return hipGetLastError();

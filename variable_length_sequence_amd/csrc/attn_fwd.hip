@@ -55,7 +55,7 @@ template <int D, int OUT>
 __global__ void __launch_bounds__(kThreads, 2)
 attn_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
                 const uint16_t* __restrict__ v, const DevItem* __restrict__ items,
-                const int32_t* __restrict__ slot, int hq, int hkv, float scale, int causal,
+                int hq, int hkv, float scale, int causal,
                 void* __restrict__ out,
                 float* __restrict__ lse, int64_t total_q) {
   constexpr int NKS = D / 16;  // k-steps over the head dim
@@ -67,10 +67,9 @@ attn_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
   const int b = blockIdx.x;
   const int xcd = b & (kXcds - 1);
   const int r = b / kXcds;
-  const int item_idx = slot[(r / hq) * kXcds + xcd];
+  const DevItem it = items[(r / hq) * kXcds + xcd];
   const int h = r % hq;
-  if (item_idx < 0) return;
-  const DevItem it = items[item_idx];
+  if (it.doc < 0) return;
   const int g = h / (hq / hkv);
 
   const int tid = threadIdx.x;
@@ -353,7 +352,7 @@ hipError_t launch_attn_fwd(const AttnShape& s, const void* q, const void* k, con
   ProfScope prof("attn_fwd", stream);
 #define VL_FWD(DD, OUTK)                                                                       \
   hipLaunchKernelGGL((attn_fwd_kernel<DD, OUTK>), grid, dim3(kThreads), 0, stream, qq, kk, vv,  \
-                     map.items, map.slot, s.hq, s.hkv, s.scale, s.causal, out, lse, s.total_q)
+                     map.items, s.hq, s.hkv, s.scale, s.causal, out, lse, s.total_q)
   if (s.d == 128) {
     if (out_kind == kOutAcc) VL_FWD(128, kOutAcc);
     else if (out_kind == kOutF32) VL_FWD(128, kOutF32);

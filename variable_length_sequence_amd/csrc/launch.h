@@ -40,15 +40,15 @@ constexpr int kFwdBK = 64;
 constexpr int kBwdBQ = 32;    // dK/dV kernel: query rows per step
 constexpr int kBwdBK = 128;   // dK/dV kernel: 4 waves x 32 keys
 
-// The work items of one pass and their assignment to the 8 XCDs: workgroup
-// b runs on XCD b % 8 (dispatch order), and the j-th item of XCD x is
-// items[slot[j * 8 + x]] (slot -1: none).  Every item is run for units_per_item
-// consecutive workgroups of its XCD (q heads, or kv heads x head slices).
+// The work items of one pass, laid out by their assignment to the 8 XCDs:
+// workgroup b runs on XCD b % 8 (dispatch order), and the j-th item of XCD x
+// is items[j * 8 + x] (doc < 0: none), so a workgroup finds its item with one
+// load.  Every item is run for units_per_item consecutive workgroups of its
+// XCD (q heads, or kv heads x head slices).
 constexpr int kXcds = 8;
 
 struct ItemMap {
-  const DevItem* items;
-  const int32_t* slot;   // [rows * kXcds]
+  const DevItem* items;  // [rows * kXcds]
   int32_t rows;          // items of the longest XCD list
 };
 
