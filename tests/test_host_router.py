@@ -148,3 +148,29 @@ def test_shipped_curve_routes_the_pareto_batch():
     # the longest document is spread over more GPUs than the shortest
     deg = [P >> d for d, _ in got["plan"]]
     assert deg[int(np.argmax(w.lengths))] > deg[int(np.argmin(w.lengths))]
+
+
+def test_ulysses_cost_model_terms_by_hand():
+    curve = {"len": [128.0, 65536.0], "fwd_tflops": [100.0, 1000.0], "bwd_tflops": [80.0, 700.0]}
+    # 32 q heads, 4 kv heads, d 128, bf16, 8-way groups: kv heads 4 < 8 are sent
+    # to two ranks each, so the exchange carries 8 kv heads' worth per tensor
+    cm = vl.ulysses_cost_model(32, 4, 128, sp_max=8, curve=curve, a2a_gbs=1000.0,
+                               a2a_alpha_us=5.0)
+    assert cm.fwd_flops_per_pair == 4 * 128 * 32 and cm.bwd_flops_per_pair == 10 * 128 * 32
+    row = 128 * 2
+    assert tuple(cm.bytes_per_token) == ((32 + 2 * 8) * row, 32 * row, 32 * row, (32 + 2 * 8) * row)
+    # with at least as many kv heads as ranks nothing is replicated
+    cm2 = vl.ulysses_cost_model(32, 8, 128, sp_max=8, curve=curve)
+    assert cm2.bytes_per_token[0] == (32 + 2 * 8) * row
+    cm3 = vl.ulysses_cost_model(32, 16, 64, sp_max=4, curve=curve)
+    assert cm3.bytes_per_token[0] == (32 + 2 * 16) * 64 * 2
+
+
+def test_shipped_curve_is_well_formed():
+    import json
+    c = json.load(open(vl.CURVE_PATH))
+    L = c["len"]
+    assert len(L) == len(c["fwd_tflops"]) == len(c["bwd_tflops"]) >= 2
+    assert all(b > a for a, b in zip(L, L[1:]))
+    assert all(x > 0 for x in c["fwd_tflops"] + c["bwd_tflops"])
+    assert (c["heads_q"], c["heads_kv"], c["head_dim"]) == (32, 4, 128)
