@@ -44,6 +44,9 @@ def _args():
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="first copy this many MiB device-to-device (a plain copy of known "
                          "size, to calibrate hardware byte counters against)")
+    ap.add_argument("--copy-kernels", action="store_true",
+                    help="run only the bandwidth-bound kernels (Ulysses permutes, fused Q/K/V "
+                         "pack, merge) and print their table (for hardware counter passes)")
     return ap.parse_args()
 
 
@@ -294,6 +297,25 @@ def bench_router(vl, reps=20):
             "within_budget": r["within_budget"]}
 
 
+def bench_merge(vl, torch, dev, steps):
+    """attn_lse_merge of 8 fp32 partials [32768, 8, 128] (the ring share's
+    merge) into bf16, alternating two input sets."""
+    n, H, d, P = 32768, 8, 128, 8
+    g = torch.Generator(device=dev).manual_seed(0)
+    parts = [[torch.randn(n, H, d, generator=g, device=dev) for _ in range(P)] for _ in range(2)]
+    lses = [[torch.randn(H, n, generator=g, device=dev) for _ in range(P)] for _ in range(2)]
+    for i in range(2):
+        vl.attn_lse_merge(parts[i], lses[i])
+    vl.profile_enable(True)
+    for i in range(steps):
+        vl.attn_lse_merge(parts[i % 2], lses[i % 2])
+    prof = vl.profile_read()
+    vl.profile_enable(False)
+    nbytes = P * (n * H * d * 4 + H * n * 4) + n * H * d * 2 + H * n * 4
+    del parts, lses
+    return prof, {"lse_merge": nbytes}
+
+
 def bench_ring(vl, torch, dev, steps):
     import numpy as np
     import workloads
@@ -371,6 +393,15 @@ def main():
         dst.copy_(src)
         torch.cuda.synchronize()
         del src, dst
+    if a.copy_kernels:
+        tabs = {}
+        for name, fn in (("ulysses_permute_49152x32x128_P8", bench_permute),
+                         ("ulysses_qkv_permute_49152_q32_kv4_d128_P8", bench_qkv_permute),
+                         ("lse_merge_8x32768x8x128_f32", bench_merge)):
+            prof, by = fn(vl, torch, dev, 10)
+            tabs[name] = kernel_table(prof, {}, by)
+        print(json.dumps({"copy_kernels": tabs}))
+        return
     w = workloads.longtail_16k()
     print(f"[bench] {w.name}: {len(w.lengths)} docs, {w.total} tokens, "
           f"{a.warmup} warmup + {a.steps} timed steps", file=sys.stderr, flush=True)
