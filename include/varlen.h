@@ -134,6 +134,8 @@ VL_API size_t varlen_attn_bwd_workspace_size(int64_t total_q, int64_t total_k,
  *   dk, dv       bf16 [total_k, n_heads_kv, head_dim]
  *   workspace    device memory of at least varlen_attn_bwd_workspace_size()
  *                bytes, 256-byte aligned; contents on entry are ignored
+ * No atomics: results are bitwise deterministic for given inputs (the dK/dV
+ * sums over a kv group's q heads run in a fixed order).
  * Errors: as the forward, plus VL_EWORKSPACE.
  */
 VL_API int varlen_attn_bwd(const void* q, const void* k, const void* v,
