@@ -386,6 +386,19 @@ VL_API int nsp_plan_cost(const int64_t* lengths, int32_t n_samples, int32_t n_gp
                   double* gpu_tokens);
 
 /*
+ * varlen_mfma_probe - measurement aid: a kernel of n_workgroups workgroups
+ * (4 waves each) whose waves issue iters rounds of 8 independent 32x32x16
+ * bf16 MFMAs from registers, with no memory traffic in the loop.  Timing it
+ * (events on `stream`) gives the matrix-core rate the chip sustains under
+ * full load, the reachable ceiling beside the spec peak.
+ *   sink     device float[n_workgroups] (one checksum per workgroup)
+ *   flops    output: the FLOPs the launch performs (may be NULL)
+ * Errors: VL_EINVAL, VL_EHIP.
+ */
+VL_API int varlen_mfma_probe(int32_t iters, int32_t n_workgroups, float* sink, int64_t* flops,
+                      void* stream);
+
+/*
  * varlen_profile_enable / varlen_profile_read - optional per-kernel timing.
  * While enabled, every kernel the library launches is bracketed by two HIP
  * events recorded on its launch stream.  Enabling clears earlier records.

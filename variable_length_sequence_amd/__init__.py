@@ -38,7 +38,7 @@ EXPORTS = ["varlen_attn_fwd", "varlen_attn_bwd_workspace_size", "varlen_attn_bwd
            "attn_lse_merge", "sp_seq2head", "sp_head2seq", "varlen_schedule_export",
            "varlen_last_error", "varlen_cache_clear", "varlen_version", "varlen_profile_enable",
            "varlen_profile_read", "varlen_ring_block", "varlen_attn_fwd_acc", "sp_qkv_seq2head",
-           "sp_qkv_head2seq", "basp_shard", "nsp_route", "nsp_plan_cost"]
+           "sp_qkv_head2seq", "basp_shard", "nsp_route", "nsp_plan_cost", "varlen_mfma_probe"]
 
 RING_CLASSES = ("N", "A1", "A2", "A3", "A4", "A5")
 
@@ -104,6 +104,8 @@ def lib():
     L.nsp_plan_cost.argtypes = [pi64, i32, i32, i32, ctypes.POINTER(_CostModelC), pi32, pi32, pd,
                                 pd, pd]
     L.nsp_plan_cost.restype = ctypes.c_int
+    L.varlen_mfma_probe.argtypes = [i32, i32, vp, pi64, vp]
+    L.varlen_mfma_probe.restype = ctypes.c_int
     L.varlen_schedule_export.argtypes = [pi32, pi32, i32, i32, i32, i32, pi32, i64, pi64, pi64,
                                          pi64, pi32, pi32]
     L.varlen_schedule_export.restype = ctypes.c_int
@@ -434,6 +436,17 @@ def nsp_plan_cost(lengths, plan, n_gpus: int, sp_max: int, cost: CostModel) -> d
                                f.ctypes.data_as(pd), b.ctypes.data_as(pd), t.ctypes.data_as(pd)))
     return {"gpu_fwd": f, "gpu_bwd": b, "gpu_cost": f + b, "gpu_tokens": t,
             "load": float(f.max() + b.max())}
+
+
+def varlen_mfma_probe(iters: int = 4096, n_workgroups: int = 8192, sink=None) -> int:
+    """Enqueue the matrix-core throughput probe on the current stream; returns
+    its FLOPs (time it with events around the call)."""
+    import torch
+    if sink is None:
+        sink = torch.empty(n_workgroups, dtype=torch.float32, device="cuda")
+    f = ctypes.c_int64(0)
+    _check(lib().varlen_mfma_probe(iters, n_workgroups, _dev_ptr(sink), ctypes.byref(f), _stream()))
+    return int(f.value)
 
 
 def varlen_schedule_export(cu_q, cu_k, causal: bool, pass_: int, head_dim: int) -> dict:

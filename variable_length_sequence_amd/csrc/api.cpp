@@ -578,6 +578,22 @@ int nsp_plan_cost(const int64_t* lengths, int32_t n_samples, int32_t n_gpus, int
   }
 }
 
+int varlen_mfma_probe(int32_t iters, int32_t n_workgroups, float* sink, int64_t* flops,
+                      void* stream) {
+  try {
+    g_err.clear();
+    if (iters <= 0 || n_workgroups <= 0) return fail(VL_EINVAL, "iters and n_workgroups must be positive");
+    if (!sink) return fail(VL_EINVAL, "sink must be non-null");
+    if (flops) *flops = vl::mfma_probe_flops(iters, n_workgroups);
+    hipError_t e = vl::launch_mfma_probe(iters, n_workgroups, sink,
+                                         reinterpret_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(e, "mfma_probe launch");
+    return VL_OK;
+  } catch (...) {
+    return fail(VL_EHIP, "internal error");
+  }
+}
+
 int varlen_ring_block(const int32_t* cu_seqlens, int32_t n_docs, int64_t q_begin, int64_t q_end,
                       int64_t k_begin, int64_t k_end, int32_t* cu_q_out, int32_t* cu_k_out,
                       int32_t* causal_out, int32_t* cls_out) {

@@ -27,6 +27,11 @@ hipError_t launch_sp_qkv(const QkvTensors& t, int64_t n_tokens, int32_t n_heads_
                          int32_t n_heads_kv, int32_t head_dim, int32_t sp_degree, int32_t dtype,
                          int dir, hipStream_t stream);
 
+// Matrix-core throughput probe (independent MFMA chains, no memory traffic);
+// n_wg workgroups of 4 waves, each writing one float to sink.
+hipError_t launch_mfma_probe(int32_t iters, int32_t n_wg, float* sink, hipStream_t stream);
+int64_t mfma_probe_flops(int32_t iters, int32_t n_wg);
+
 constexpr int kMaxMergeParts = 64;
 
 hipError_t launch_lse_merge(int32_t n_parts, const void* const* o_parts,
