@@ -1,9 +1,12 @@
 #!/usr/bin/env python3
 """Benchmark of packed variable-length causal attention on one MI355X.
 
-One step = the whole hot path over one synthetic packed batch: the cached
-work lists (cu_seqlens validation and scheduling; built once, then looked up),
-varlen_attn_fwd and varlen_attn_bwd (D = rowsum(dO*O), dK/dV, dQ).  The
+One step = the whole hot path over one synthetic packed batch:
+varlen_attn_fwd and varlen_attn_bwd, each validating the cu_seqlens,
+scheduling the work lists on the host and uploading them (the plan cache is
+off, as for a freshly packed batch every step), then the kernels (forward;
+D = rowsum(dO*O), dK/dV, dQ).  The same steps with cached work lists are
+reported beside it.  The
 headline workload is the 16384-token long-tail batch (lognormal lengths,
 median 512, sigma 1.2, clipped to [64, 8192]; 32 q heads, 4 kv heads,
 head_dim 128).  The metric is useful TFLOP/s: 4 d FLOPs per visible
@@ -103,22 +106,30 @@ def attn_step_fn(vl, torch, w, q, k, v, do, cu):
     return step
 
 
-def bench_attention(vl, torch, w, steps, warmup, dev, tensors=None, profile=True):
+def bench_attention(vl, torch, w, steps, warmup, dev, tensors=None, profile=True,
+                    plan_cache=False):
+    """Times fwd+bwd steps.  With plan_cache False (the default) every call
+    validates and schedules its cu_seqlens again and uploads the work lists,
+    as a step over a freshly packed batch would."""
     import workloads
     q, k, v, do = tensors if tensors is not None else workloads.make_tensors(w)
     q, k, v, do = (t.to(dev) for t in (q, k, v, do))
     cu = w.cu
     step = attn_step_fn(vl, torch, w, q, k, v, do, cu)
-    for _ in range(warmup):
-        step()
-    if profile:
-        vl.profile_enable(True)
-    ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
-    with Timer(torch) as tm:
-        ev[0].record()
-        for i in range(steps):
+    prev = vl.set_plan_cache(plan_cache)
+    try:
+        for _ in range(warmup):
             step()
-            ev[i + 1].record()
+        if profile:
+            vl.profile_enable(True)
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+        with Timer(torch) as tm:
+            ev[0].record()
+            for i in range(steps):
+                step()
+                ev[i + 1].record()
+    finally:
+        vl.set_plan_cache(prev)
     per_step = sorted(ev[i].elapsed_time(ev[i + 1]) for i in range(steps))
     prof = vl.profile_read() if profile else {}
     if profile:
@@ -402,6 +413,8 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
     vl.lib()
+    # every timed attention call schedules its own work lists (see bench_attention)
+    vl.set_plan_cache(False)
     dev = torch.device("cuda:0")
     if a.copy_mib > 0:
         n = a.copy_mib << 20
@@ -429,6 +442,7 @@ def main():
     dom = max((n for n in kflops if n in r["prof"]), key=lambda n: r["prof"][n][1])
     dom_avg = r["prof"][dom][1] / r["prof"][dom][0]
     achieved = kflops[dom] / (dom_avg * 1e-3) / 1e12
+    cached = bench_attention(vl, torch, w, a.steps, a.warmup, dev, profile=False, plan_cache=True)
     print("[bench] matrix-core probe", file=sys.stderr, flush=True)
     probe = measured_mfma_peak(vl, torch, dev)
     out = {
@@ -453,6 +467,8 @@ def main():
         "pct_measured_mfma_peak": round(100 * r["tflops"] / probe, 2),
         "step_ms_median": round(r["median_ms"], 4),
         "step_ms_min": round(r["min_ms"], 4),
+        "work_lists": "scheduled and uploaded by every call (plan cache off)",
+        "ms_per_step_plan_cached": round(cached["ms"], 4),
         "useful_tflop_per_step": round((r["flops_fwd"] + r["flops_bwd"]) / 1e12, 4),
         "roofline": {"bound": "mfma", "kernel": dom, "achieved": round(achieved, 2),
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",

@@ -282,3 +282,14 @@ def test_basp_shard_rejects(args):
     with pytest.raises(vl.VarlenError) as e:
         vl.basp_shard(*args)
     assert e.value.code == -2
+
+
+def test_plan_cache_switch_returns_previous_setting():
+    # the switch itself touches no device
+    prev = vl.set_plan_cache(False)
+    try:
+        assert vl.set_plan_cache(False) is False
+        assert vl.set_plan_cache(True) is False
+        assert vl.set_plan_cache(True) is True
+    finally:
+        vl.set_plan_cache(prev)

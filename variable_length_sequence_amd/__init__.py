@@ -36,8 +36,8 @@ STATUS = {0: "VL_OK", -1: "VL_EINVAL", -2: "VL_ESHAPE", -3: "VL_ESEQLENS",
 
 EXPORTS = ["varlen_attn_fwd", "varlen_attn_bwd_workspace_size", "varlen_attn_bwd",
            "attn_lse_merge", "sp_seq2head", "sp_head2seq", "varlen_schedule_export",
-           "varlen_last_error", "varlen_cache_clear", "varlen_version", "varlen_profile_enable",
-           "varlen_profile_read", "varlen_ring_block", "varlen_attn_fwd_acc", "sp_qkv_seq2head",
+           "varlen_last_error", "varlen_cache_clear", "varlen_set_plan_cache", "varlen_version",
+           "varlen_profile_enable", "varlen_profile_read", "varlen_ring_block", "varlen_attn_fwd_acc", "sp_qkv_seq2head",
            "sp_qkv_head2seq", "basp_shard", "nsp_route", "nsp_plan_cost", "varlen_mfma_probe"]
 
 RING_CLASSES = ("N", "A1", "A2", "A3", "A4", "A5")
@@ -115,6 +115,8 @@ def lib():
     L.varlen_last_error.restype = ctypes.c_char_p
     L.varlen_cache_clear.argtypes = []
     L.varlen_cache_clear.restype = None
+    L.varlen_set_plan_cache.argtypes = [ctypes.c_int32]
+    L.varlen_set_plan_cache.restype = ctypes.c_int
     L.varlen_version.argtypes = []
     L.varlen_version.restype = ctypes.c_int
     L.varlen_profile_enable.argtypes = [i32]
@@ -500,6 +502,13 @@ def profile_read() -> dict:
 
 def cache_clear():
     lib().varlen_cache_clear()
+
+
+def set_plan_cache(on: bool) -> bool:
+    """Switch the per-pattern work-list cache (default on); returns the
+    previous setting.  Off: every call schedules its cu_seqlens again and
+    enqueues the upload of its work lists on its stream."""
+    return bool(lib().varlen_set_plan_cache(1 if on else 0))
 
 
 def version() -> int:

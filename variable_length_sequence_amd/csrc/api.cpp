@@ -2,8 +2,10 @@
 // cached device work lists, and dispatch to the HIP kernels.
 #include <hip/hip_runtime.h>
 
+#include <atomic>
 #include <cmath>
 #include <cstring>
+#include <deque>
 #include <map>
 #include <mutex>
 #include <string>
@@ -52,13 +54,43 @@ std::string plan_key(int dev, int pass, int causal, const int32_t* cu_q, const i
   return key;
 }
 
+size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
 void clear_plans_locked() {
   for (auto& kv : g_plans)
     if (kv.second.dev) (void)hipFree(kv.second.dev);
   g_plans.clear();
 }
 
-// pass 0: forward / dQ list (query tiles); pass 1: dK/dV list (key tiles)
+// pass 0: forward / dQ list (query tiles); pass 1: dK/dV list (key tiles).
+// Builds the list on the host in XCD slot order (a workgroup reads its item
+// with one load; an empty slot has doc = -1) and fills the plan's counts.
+void build_list(int pass, int causal, const int32_t* cu_q, const int32_t* cu_k, int32_t n_docs,
+                std::vector<vl::DevItem>& host, Plan& p) {
+  const std::vector<vl::Doc> docs = vl::doc_table(cu_q, cu_k, n_docs);
+  const std::vector<vl::Item> items =
+      pass == 0 ? vl::fwd_items(docs, causal != 0, vl::kFwdBQ, vl::kFwdBK)
+                : vl::bwd_items(docs, causal != 0, vl::kBwdBQ, vl::kBwdBK);
+  const std::vector<vl::DevItem> di = vl::device_items(docs, items);
+  int32_t rows = 0;
+  const std::vector<int32_t> slots = vl::xcd_slots(items, vl::kXcds, rows);
+  p = Plan{};
+  p.n = int32_t(di.size());
+  p.rows = rows;
+  for (const auto& it : items) {
+    p.max_count = std::max(p.max_count, it.count);
+    p.total_count += it.count;
+  }
+  host.assign(di.empty() ? 0 : slots.size(), vl::DevItem{});
+  for (size_t j = 0; j < host.size(); ++j) {
+    if (slots[j] >= 0) {
+      host[j] = di[size_t(slots[j])];
+    } else {
+      host[j].doc = -1;
+    }
+  }
+}
+
 int get_plan(int pass, int causal, const int32_t* cu_q, const int32_t* cu_k, int32_t n_docs,
              Plan& out) {
   int dev = 0;
@@ -71,36 +103,14 @@ int get_plan(int pass, int causal, const int32_t* cu_q, const int32_t* cu_k, int
     out = itp->second;
     return VL_OK;
   }
-  const std::vector<vl::Doc> docs = vl::doc_table(cu_q, cu_k, n_docs);
-  const std::vector<vl::Item> items =
-      pass == 0 ? vl::fwd_items(docs, causal != 0, vl::kFwdBQ, vl::kFwdBK)
-                : vl::bwd_items(docs, causal != 0, vl::kBwdBQ, vl::kBwdBK);
-  const std::vector<vl::DevItem> di = vl::device_items(docs, items);
-  int32_t rows = 0;
-  const std::vector<int32_t> slots = vl::xcd_slots(items, vl::kXcds, rows);
+  std::vector<vl::DevItem> host;
   Plan p;
-  p.n = int32_t(di.size());
-  p.rows = rows;
-  for (const auto& it : items) {
-    p.max_count = std::max(p.max_count, it.count);
-    p.total_count += it.count;
-  }
-  if (!di.empty()) {
+  build_list(pass, causal, cu_q, cu_k, n_docs, host, p);
+  if (!host.empty()) {
     // a new pattern: drain the device before touching the allocator when the cache is full
     if (g_plans.size() >= kMaxPlans) {
       (void)hipDeviceSynchronize();
       clear_plans_locked();
-    }
-    // items in slot order, so a workgroup reads its item with one load;
-    // an empty slot has doc = -1
-    std::vector<vl::DevItem> host(slots.size());
-    for (size_t j = 0; j < slots.size(); ++j) {
-      if (slots[j] >= 0) {
-        host[j] = di[size_t(slots[j])];
-      } else {
-        host[j] = vl::DevItem{};
-        host[j].doc = -1;
-      }
     }
     const size_t bytes = host.size() * sizeof(vl::DevItem);
     e = hipMalloc(&p.dev, bytes);
@@ -115,6 +125,155 @@ int get_plan(int pass, int causal, const int32_t* cu_q, const int32_t* cu_k, int
   out = p;
   return VL_OK;
 }
+
+// ------------------------------------------------------------ per-call work lists
+// With the plan cache off, every call builds its work lists on the host and
+// enqueues their upload on its own stream: the lists go into pinned host
+// staging and from there, by one asynchronous copy, into a per-device ring
+// of device memory.  A region is handed out again only after the event
+// recorded behind the last kernel that read it has completed, so a call
+// allocates nothing and waits for nothing unless the host runs a whole ring
+// ahead of the device, or its lists outgrow half the ring (which then grows
+// once, after its in-flight regions have drained).
+struct Ring {
+  struct Use {
+    size_t off, size;
+    hipEvent_t ev;
+  };
+  char* dev = nullptr;
+  char* host = nullptr;   // pinned staging, same offsets as dev
+  size_t cap = 0, head = 0;
+  std::deque<Use> live;   // in reservation order
+  std::vector<hipEvent_t> spare;
+};
+
+std::atomic<int> g_cache_on{1};
+std::mutex g_ring_mu;
+std::map<int, Ring> g_rings;
+constexpr size_t kRingMin = size_t(1) << 20;
+
+int ring_retire(Ring& r, std::deque<Ring::Use>::iterator it, bool wait) {
+  if (wait) {
+    const hipError_t e = hipEventSynchronize(it->ev);
+    if (e != hipSuccess) return hip_fail(e, "hipEventSynchronize(work-list ring)");
+  }
+  r.spare.push_back(it->ev);
+  r.live.erase(it);
+  return VL_OK;
+}
+
+int ring_reserve(Ring& r, size_t bytes, size_t& off) {
+  // regions whose readers have finished go back first, oldest first
+  while (!r.live.empty() && hipEventQuery(r.live.front().ev) == hipSuccess)
+    (void)ring_retire(r, r.live.begin(), false);
+  if (bytes > r.cap / 2) {
+    while (!r.live.empty()) {
+      const int rc = ring_retire(r, r.live.begin(), true);
+      if (rc) return rc;
+    }
+    if (r.dev) (void)hipFree(r.dev);
+    if (r.host) (void)hipHostFree(r.host);
+    r.dev = r.host = nullptr;
+    r.cap = r.head = 0;
+    size_t cap = kRingMin;
+    while (cap < 4 * bytes) cap *= 2;
+    hipError_t e = hipMalloc(reinterpret_cast<void**>(&r.dev), cap);
+    if (e != hipSuccess) return hip_fail(e, "hipMalloc(work-list ring)");
+    e = hipHostMalloc(reinterpret_cast<void**>(&r.host), cap, hipHostMallocDefault);
+    if (e != hipSuccess) {
+      (void)hipFree(r.dev);
+      r.dev = nullptr;
+      return hip_fail(e, "hipHostMalloc(work-list staging)");
+    }
+    r.cap = cap;
+  }
+  off = r.head + bytes <= r.cap ? r.head : 0;
+  for (auto it = r.live.begin(); it != r.live.end();) {
+    if (it->off < off + bytes && off < it->off + it->size) {
+      const int rc = ring_retire(r, it, true);
+      if (rc) return rc;
+      it = r.live.begin();
+    } else {
+      ++it;
+    }
+  }
+  r.head = off + bytes;
+  return VL_OK;
+}
+
+// The work lists of one call: from the cache, or (cache off) built for this
+// call and uploaded into the ring.  With the ring, the lock is held until the
+// destructor has recorded the event behind the call's kernels.
+class CallPlans {
+ public:
+  ~CallPlans() {
+    if (!ring_) return;
+    hipEvent_t ev = nullptr;
+    if (!ring_->spare.empty()) {
+      ev = ring_->spare.back();
+      ring_->spare.pop_back();
+    } else if (hipEventCreateWithFlags(&ev, hipEventDisableTiming) != hipSuccess) {
+      ev = nullptr;
+    }
+    if (ev && hipEventRecord(ev, st_) == hipSuccess) {
+      ring_->live.push_back(Ring::Use{off_, size_, ev});
+    } else {
+      // no event: the region is free once the stream has drained
+      if (ev) ring_->spare.push_back(ev);
+      (void)hipStreamSynchronize(st_);
+    }
+  }
+
+  int get(int causal, const int32_t* cu_q, const int32_t* cu_k, int32_t n_docs,
+          hipStream_t st, int n_pass, const int* passes, Plan* out) {
+    if (g_cache_on.load()) {
+      for (int i = 0; i < n_pass; ++i) {
+        const int rc = get_plan(passes[i], causal, cu_q, cu_k, n_docs, out[i]);
+        if (rc) return rc;
+      }
+      return VL_OK;
+    }
+    hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+    if (hipStreamIsCapturing(st, &cs) == hipSuccess && cs != hipStreamCaptureStatusNone)
+      return fail(VL_EUNSUPPORTED,
+                  "with the plan cache off a call uploads its work lists and cannot be captured");
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+    std::vector<vl::DevItem> host[2];
+    size_t at[2] = {0, 0}, total = 0;
+    for (int i = 0; i < n_pass; ++i) {
+      build_list(passes[i], causal, cu_q, cu_k, n_docs, host[i], out[i]);
+      at[i] = total;
+      total += align256(host[i].size() * sizeof(vl::DevItem));
+    }
+    if (total == 0) return VL_OK;
+    lock_ = std::unique_lock<std::mutex>(g_ring_mu);
+    Ring& r = g_rings[dev];
+    size_t off = 0;
+    const int rc = ring_reserve(r, total, off);
+    if (rc) return rc;
+    for (int i = 0; i < n_pass; ++i) {
+      if (host[i].empty()) continue;
+      std::memcpy(r.host + off + at[i], host[i].data(), host[i].size() * sizeof(vl::DevItem));
+      out[i].dev = reinterpret_cast<vl::DevItem*>(r.dev + off + at[i]);
+    }
+    e = hipMemcpyAsync(r.dev + off, r.host + off, total, hipMemcpyHostToDevice, st);
+    // from here on the region is in flight: the destructor records its event
+    ring_ = &r;
+    off_ = off;
+    size_ = total;
+    st_ = st;
+    if (e != hipSuccess) return hip_fail(e, "hipMemcpyAsync(work list)");
+    return VL_OK;
+  }
+
+ private:
+  std::unique_lock<std::mutex> lock_;
+  Ring* ring_ = nullptr;
+  size_t off_ = 0, size_ = 0;
+  hipStream_t st_ = nullptr;
+};
 
 // ------------------------------------------------------------ validation
 int check_attn_common(const void* q, const void* k, const void* v, const int32_t* cu_q,
@@ -140,8 +299,6 @@ int check_attn_common(const void* q, const void* k, const void* v, const int32_t
 
 float resolve_scale(float s, int d) { return s > 0.f ? s : 1.0f / std::sqrt(float(d)); }
 
-size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
-
 // The largest q-head split the backward may choose: a power of two dividing
 // the group size, at most vl::kMaxHeadSplit.
 int max_head_split(int32_t hq, int32_t hkv) {
@@ -164,6 +321,8 @@ void varlen_cache_clear(void) {
   clear_plans_locked();
 }
 
+int varlen_set_plan_cache(int32_t on) { return g_cache_on.exchange(on != 0 ? 1 : 0); }
+
 int varlen_attn_fwd(const void* q, const void* k, const void* v, const int32_t* cu_seqlens_q,
                     const int32_t* cu_seqlens_k, int32_t n_docs, int64_t total_q, int64_t total_k,
                     int32_t n_heads_q, int32_t n_heads_kv, int32_t head_dim, float softmax_scale,
@@ -178,7 +337,10 @@ int varlen_attn_fwd(const void* q, const void* k, const void* v, const int32_t* 
     if (reinterpret_cast<uintptr_t>(out) % 16) return fail(VL_EINVAL, "out must be 16-byte aligned");
     if (total_q == 0) return VL_OK;
     Plan p;
-    rc = get_plan(0, causal != 0, cu_seqlens_q, cu_seqlens_k, n_docs, p);
+    CallPlans plans;
+    const int pass0 = 0;
+    rc = plans.get(causal != 0, cu_seqlens_q, cu_seqlens_k, n_docs,
+                   reinterpret_cast<hipStream_t>(stream), 1, &pass0, &p);
     if (rc) return rc;
     vl::AttnShape s{total_q, total_k, n_heads_q, n_heads_kv, head_dim,
                     resolve_scale(softmax_scale, head_dim), causal != 0};
@@ -207,7 +369,10 @@ int varlen_attn_fwd_acc(const void* q, const void* k, const void* v, const int32
     if (reinterpret_cast<uintptr_t>(o_acc) % 16) return fail(VL_EINVAL, "o_acc must be 16-byte aligned");
     if (total_q == 0) return VL_OK;
     Plan p;
-    rc = get_plan(0, causal != 0, cu_seqlens_q, cu_seqlens_k, n_docs, p);
+    CallPlans plans;
+    const int pass0 = 0;
+    rc = plans.get(causal != 0, cu_seqlens_q, cu_seqlens_k, n_docs,
+                   reinterpret_cast<hipStream_t>(stream), 1, &pass0, &p);
     if (rc) return rc;
     vl::AttnShape s{total_q, total_k, n_heads_q, n_heads_kv, head_dim,
                     resolve_scale(softmax_scale, head_dim), causal != 0};
@@ -252,12 +417,14 @@ int varlen_attn_bwd(const void* q, const void* k, const void* v, const void* out
       return fail(VL_EWORKSPACE, "workspace must hold at least " + std::to_string(need) + " bytes");
     if (reinterpret_cast<uintptr_t>(workspace) % 256) return fail(VL_EWORKSPACE, "workspace must be 256-byte aligned");
     if (total_q == 0 && total_k == 0) return VL_OK;
-    Plan pf, pb;
-    rc = get_plan(0, causal != 0, cu_seqlens_q, cu_seqlens_k, n_docs, pf);
-    if (rc) return rc;
-    rc = get_plan(1, causal != 0, cu_seqlens_q, cu_seqlens_k, n_docs, pb);
-    if (rc) return rc;
     hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+    Plan pp[2];
+    CallPlans plans;
+    const int passes[2] = {0, 1};
+    rc = plans.get(causal != 0, cu_seqlens_q, cu_seqlens_k, n_docs, st, 2, passes, pp);
+    if (rc) return rc;
+    const Plan& pf = pp[0];
+    const Plan& pb = pp[1];
     // dK/dV of kv tiles that no query tile reaches are zeros written by the kernel
     int dev = 0, n_cu = 256;
     (void)hipGetDevice(&dev);
