@@ -226,6 +226,7 @@ class CallPlans {
 
   int get(int causal, const int32_t* cu_q, const int32_t* cu_k, int32_t n_docs,
           hipStream_t st, int n_pass, const int* passes, Plan* out) {
+    if (n_pass < 1 || n_pass > 2) return fail(VL_EINVAL, "internal: one or two work lists per call");
     if (g_cache_on.load()) {
       for (int i = 0; i < n_pass; ++i) {
         const int rc = get_plan(passes[i], causal, cu_q, cu_k, n_docs, out[i]);
