@@ -95,3 +95,32 @@ def test_plan_cache_off_fresh_pattern_every_call():
         ref = _run(b, dev)
         for key, val in res.items():
             assert torch.equal(val, ref[key]), f"{b[0]}: {key} differs"
+
+
+def test_plan_cache_off_two_streams():
+    # calls alternate between two streams: each upload and its kernels run
+    # on the caller's stream, and each ring region waits for its own
+    # stream's event before it is handed out again
+    dev = require_gpu()
+    rng = np.random.default_rng(13)
+    batches = []
+    for i in range(8):
+        lq, lk, q, k, v, do = random_case(rng, int(rng.integers(1, 9)), 1, 500, 4, 2, 128,
+                                          seed=200 + i)
+        batches.append(("s%d" % i, lq, lk, q.to(dev), k.to(dev), v.to(dev), do.to(dev), True))
+    ref = [_run(b, dev) for b in batches]
+    torch.cuda.synchronize()
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    prev = vl.set_plan_cache(False)
+    try:
+        got = []
+        for rep in range(3):
+            for i, b in enumerate(batches):
+                with torch.cuda.stream(streams[(i + rep) % 2]):
+                    got.append((b[0], i, _run(b, dev)))
+        torch.cuda.synchronize()
+    finally:
+        vl.set_plan_cache(prev)
+    for name, i, res in got:
+        for key, val in res.items():
+            assert torch.equal(val, ref[i][key]), f"{name}: {key} differs"
