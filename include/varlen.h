@@ -14,13 +14,13 @@
  *     enqueued, a negative VL_E* code is returned and varlen_last_error()
  *     describes it.  No C++ exception leaves the library.
  *   - Device work is enqueued on `stream` (a hipStream_t; NULL = the null
- *     stream) and the call returns without waiting.  With the plan cache on
- *     (the default) the first call with a new cu_seqlens pattern uploads
- *     that pattern's work list synchronously and caches it (see
- *     varlen_cache_clear); later calls with that pattern only launch
- *     kernels (no allocation, copy or memset), so they can be captured into
- *     a HIP graph.  With it off, every call schedules its pattern again and
- *     enqueues the upload (see varlen_set_plan_cache).
+ *     stream) and the call returns without waiting.  By default every call
+ *     schedules its cu_seqlens pattern and enqueues the upload of its work
+ *     lists on `stream` (see varlen_set_plan_cache).  With the plan cache
+ *     switched on, the first call with a new pattern uploads its work list
+ *     synchronously and caches it (see varlen_cache_clear); later calls with
+ *     that pattern only launch kernels (no allocation, copy or memset), so
+ *     they can be captured into a HIP graph.
  *   - bf16 values are IEEE binary32 truncated to the top 16 bits; results are
  *     rounded to nearest-even.  Scores, softmax and accumulation are fp32.
  */
@@ -421,19 +421,20 @@ VL_API const char* varlen_last_error(void);
 VL_API void varlen_cache_clear(void);
 
 /* Plan cache switch, process-wide; returns the previous setting (1 = on).
- * On (the default): work lists are cached per cu_seqlens pattern as above.
- * Off: every attention call validates its cu_seqlens, builds its work lists
- * on the host (the scheduling of the HSAP page's Fig. 3 block classes with
- * the NSP page's longest-first order, Section 4.1.3) and enqueues their
- * upload on its own stream, as a training loop that packs a new batch every
- * step needs: the lists are copied into pinned host staging and by one
- * asynchronous copy into a per-device ring of device memory, whose regions
- * are handed out again once the kernels that read them have completed (an
- * event recorded behind them).  Such a call allocates nothing and does not
- * wait, unless the host is a whole ring ahead of the device or the call's
- * lists outgrow half the ring (1 MiB at first, then grown once, after the
- * regions in flight have drained).  With the cache off a call on a
- * capturing stream fails with VL_EUNSUPPORTED. */
+ * Off (the default): every attention call validates its cu_seqlens, builds
+ * its work lists on the host (the scheduling of the HSAP page's Fig. 3 block
+ * classes with the NSP page's longest-first order, Section 4.1.3) and
+ * enqueues their upload on its own stream, as a training loop that packs a
+ * new batch every step needs: the lists are copied into pinned host staging
+ * and by one asynchronous copy into a per-device ring of device memory,
+ * whose regions are handed out again once the kernels that read them have
+ * completed (an event recorded behind them).  Such a call allocates nothing
+ * and does not wait, unless the host is a whole ring ahead of the device or
+ * the call's lists outgrow half the ring (1 MiB at first, then grown once,
+ * after the regions in flight have drained).  A call on a capturing stream
+ * fails with VL_EUNSUPPORTED in this mode.
+ * On: work lists are cached per cu_seqlens pattern as above, for patterns
+ * that repeat and for graph capture (warm the pattern up before capturing). */
 VL_API int varlen_set_plan_cache(int32_t on);
 
 /* ABI version, currently 1. */

@@ -1,6 +1,7 @@
-"""The attention step captured in a HIP graph: after one eager call has built
-and cached the work lists for a cu_seqlens pattern, varlen_attn_fwd and
-varlen_attn_bwd only launch kernels, so a training step can capture them.
+"""The attention step captured in a HIP graph: with the plan cache on, after
+one eager call has built and cached the work lists for a cu_seqlens pattern,
+varlen_attn_fwd and varlen_attn_bwd only launch kernels, so a training step
+can capture them.
 Every replay (with eager work and synchronisations in between) must equal the
 eager result bit for bit."""
 import numpy as np
@@ -42,22 +43,26 @@ def test_graph_replay_equals_eager(name, lengths, hq, hkv, d):
         vl.varlen_attn_bwd(q, k, v, bufs["o"], do, bufs["lse"], cu, cu, workspace=ws,
                            dq=bufs["dq"], dk=bufs["dk"], dv=bufs["dv"])
 
-    s = torch.cuda.Stream()
-    s.wait_stream(torch.cuda.current_stream())
-    with torch.cuda.stream(s):
-        step()                                   # builds and caches the work lists
-    torch.cuda.current_stream().wait_stream(s)
-    torch.cuda.synchronize()
-    eager = {n: t.clone() for n, t in bufs.items()}
+    prev = vl.set_plan_cache(True)
+    try:
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s):
+            step()                               # builds and caches the work lists
+        torch.cuda.current_stream().wait_stream(s)
+        torch.cuda.synchronize()
+        eager = {n: t.clone() for n, t in bufs.items()}
 
-    g = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(g, stream=s):
-        step()
-    for r in range(3):
-        for t in bufs.values():
-            t.fill_(0)                          # eager work between replays
-        torch.cuda.synchronize()
-        g.replay()
-        torch.cuda.synchronize()
-        for n in bufs:
-            assert torch.equal(_bits(bufs[n]), _bits(eager[n])), (n, r)
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=s):
+            step()
+        for r in range(3):
+            for t in bufs.values():
+                t.fill_(0)                      # eager work between replays
+            torch.cuda.synchronize()
+            g.replay()
+            torch.cuda.synchronize()
+            for n in bufs:
+                assert torch.equal(_bits(bufs[n]), _bits(eager[n])), (n, r)
+    finally:
+        vl.set_plan_cache(prev)

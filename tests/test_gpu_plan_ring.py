@@ -54,12 +54,11 @@ def test_plan_cache_off_matches_cached_bitwise():
     for c in _cases():
         name, lq, lk, q, k, v, do, causal = c
         cases.append((name, lq, lk, q.to(dev), k.to(dev), v.to(dev), do.to(dev), causal))
-    vl.set_plan_cache(True)
-    ref = {c[0]: _run(c, dev) for c in cases}
-    torch.cuda.synchronize()
-    prev = vl.set_plan_cache(False)
+    prev = vl.set_plan_cache(True)
     try:
-        assert prev is True
+        ref = {c[0]: _run(c, dev) for c in cases}
+        torch.cuda.synchronize()
+        assert vl.set_plan_cache(False) is True
         got = []
         # interleaved, no synchronisation: the ring wraps and grows with
         # earlier uploads and kernels still in flight
@@ -68,7 +67,7 @@ def test_plan_cache_off_matches_cached_bitwise():
                 got.append((rep, c[0], _run(c, dev)))
         torch.cuda.synchronize()
     finally:
-        vl.set_plan_cache(True)
+        vl.set_plan_cache(prev)
     for rep, name, res in got:
         for key, val in res.items():
             assert torch.equal(val, ref[name][key]), f"{name} rep {rep}: {key} differs"
@@ -89,12 +88,13 @@ def test_plan_cache_off_fresh_pattern_every_call():
     try:
         got = [_run(b, dev) for b in batches]
         torch.cuda.synchronize()
+        vl.set_plan_cache(True)
+        ref = [_run(b, dev) for b in batches]
     finally:
         vl.set_plan_cache(prev)
-    for b, res in zip(batches, got):
-        ref = _run(b, dev)
+    for b, res, rf in zip(batches, got, ref):
         for key, val in res.items():
-            assert torch.equal(val, ref[key]), f"{b[0]}: {key} differs"
+            assert torch.equal(val, rf[key]), f"{b[0]}: {key} differs"
 
 
 def test_plan_cache_off_two_streams():
@@ -108,7 +108,11 @@ def test_plan_cache_off_two_streams():
         lq, lk, q, k, v, do = random_case(rng, int(rng.integers(1, 9)), 1, 500, 4, 2, 128,
                                           seed=200 + i)
         batches.append(("s%d" % i, lq, lk, q.to(dev), k.to(dev), v.to(dev), do.to(dev), True))
-    ref = [_run(b, dev) for b in batches]
+    prev = vl.set_plan_cache(True)
+    try:
+        ref = [_run(b, dev) for b in batches]
+    finally:
+        vl.set_plan_cache(prev)
     torch.cuda.synchronize()
     streams = [torch.cuda.Stream(), torch.cuda.Stream()]
     prev = vl.set_plan_cache(False)

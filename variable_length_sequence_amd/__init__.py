@@ -505,9 +505,10 @@ def cache_clear():
 
 
 def set_plan_cache(on: bool) -> bool:
-    """Switch the per-pattern work-list cache (default on); returns the
-    previous setting.  Off: every call schedules its cu_seqlens again and
-    enqueues the upload of its work lists on its stream."""
+    """Switch the per-pattern work-list cache (default off); returns the
+    previous setting.  Off: every call schedules its cu_seqlens and enqueues
+    the upload of its work lists on its stream.  On: a pattern's lists are
+    uploaded once and reused (needed for HIP graph capture)."""
     return bool(lib().varlen_set_plan_cache(1 if on else 0))
 
 

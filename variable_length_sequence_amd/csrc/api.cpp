@@ -147,7 +147,7 @@ struct Ring {
   std::vector<hipEvent_t> spare;
 };
 
-std::atomic<int> g_cache_on{1};
+std::atomic<int> g_cache_on{0};   // per-call work lists unless a caller opts in
 std::mutex g_ring_mu;
 std::map<int, Ring> g_rings;
 constexpr size_t kRingMin = size_t(1) << 20;
