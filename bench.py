@@ -144,10 +144,10 @@ def bench_attention(vl, torch, w, steps, warmup, dev, tensors=None, profile=True
 
 # kernel -> the sources its code comes from (a counter summary is valid only for
 # the sources it was taken with)
-KERNEL_SOURCES = {
-    "attn_fwd": ["attn_fwd.hip", "common.h", "launch.h"],
-    "bwd_dkdv": ["attn_bwd.hip", "common.h", "launch.h"],
-    "bwd_dq": ["attn_bwd.hip", "common.h", "launch.h"],
+KERNEL_SOURCES = {   # relative to csrc/; the build script holds the compile flags
+    "attn_fwd": ["attn_fwd.hip", "common.h", "launch.h", "../build.py"],
+    "bwd_dkdv": ["attn_bwd.hip", "common.h", "launch.h", "../build.py"],
+    "bwd_dq": ["attn_bwd.hip", "common.h", "launch.h", "../build.py"],
 }
 
 

@@ -26,6 +26,15 @@ COMMON = ["-O3", "-fPIC", "-std=c++17", "-fvisibility=hidden", "-Wall", "-Wno-un
           f"--offload-arch={ARCH}"]
 # gfx950 code is built without packed fp32 ALU ops (v_pk_*_f32)
 DEVICE = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
+# Machine-scheduler strategy per source (instruction order only; the kernels'
+# results are bitwise the same).  Measured on the attention kernels: the
+# ILP-first strategy makes the backward kernels 1-2.5 % faster, the
+# memory-clause one the forward about 1 %, against the occupancy-first default
+# (their register counts stay within two waves per SIMD either way).
+SCHED = {
+    "attn_bwd.hip": ["-mllvm", "-amdgpu-sched-strategy=max-ilp"],
+    "attn_fwd.hip": ["-mllvm", "-amdgpu-sched-strategy=max-memory-clause"],
+}
 
 
 def hipcc() -> str:
@@ -39,7 +48,7 @@ def _compile(src: str, verbose: bool) -> str:
     obj = os.path.join(BUILD, src + ".o")
     cmd = [hipcc(), *COMMON, "-I", os.path.join(ROOT, "include")]
     if src.endswith(".hip"):
-        cmd += ["-x", "hip", *DEVICE]
+        cmd += ["-x", "hip", *DEVICE, *SCHED.get(src, [])]
     else:
         # host code: no contraction into fused multiply-adds, so the planner's
         # floating-point decisions follow the written order of operations
