@@ -97,7 +97,7 @@ def kernel_table(prof, flops, bytes_):
 
 
 def attn_step_fn(vl, torch, w, q, k, v, do, cu):
-    ws = torch.empty(vl.bwd_workspace_bytes(q.shape[0], k.shape[0], w.hq, w.hkv, w.d),
+    ws = torch.empty(vl.bwd_workspace_bytes_cu(cu, cu, w.hq, w.hkv, w.d),
                      dtype=torch.uint8, device=q.device)
 
     def step():

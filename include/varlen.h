@@ -110,12 +110,29 @@ VL_API int varlen_attn_fwd_acc(const void* q, const void* k, const void* v,
                         void* stream);
 
 /*
- * varlen_attn_bwd_workspace_size - bytes of device workspace varlen_attn_bwd
- * needs for these sizes (fp32 per-row terms and kv-gradient accumulators).
+ * varlen_attn_bwd_workspace_size - an upper bound on the device workspace
+ * varlen_attn_bwd needs for any batch of these sizes: the fp32 per-row terms
+ * D [n_heads_q, total_q] plus the fp32 dK/dV partials of the largest q-head
+ * split the backward may choose (4 when the group size allows it).  0 for
+ * invalid sizes.
  */
 VL_API size_t varlen_attn_bwd_workspace_size(int64_t total_q, int64_t total_k,
                                       int32_t n_heads_q, int32_t n_heads_kv,
                                       int32_t head_dim);
+
+/*
+ * varlen_attn_bwd_workspace_size_cu - the device workspace varlen_attn_bwd
+ * needs for this batch on the current device: D plus the partials of the
+ * q-head split it will choose for these cu_seqlens (none when it does not
+ * split; the split depends on the batch's key-tile counts and the device's
+ * compute-unit count).  Host only.  Arguments as varlen_attn_bwd; 0 for
+ * invalid arguments.
+ */
+VL_API size_t varlen_attn_bwd_workspace_size_cu(const int32_t* cu_seqlens_q,
+                                         const int32_t* cu_seqlens_k, int32_t n_docs,
+                                         int64_t total_q, int64_t total_k,
+                                         int32_t n_heads_q, int32_t n_heads_kv,
+                                         int32_t head_dim, int32_t causal);
 
 /*
  * varlen_attn_bwd - exact gradients of the forward above for an upstream dO.
@@ -134,8 +151,10 @@ VL_API size_t varlen_attn_bwd_workspace_size(int64_t total_q, int64_t total_k,
  *   lse          fp32 [n_heads_q, total_q], the forward's LSE
  *   dq           bf16 [total_q, n_heads_q, head_dim]
  *   dk, dv       bf16 [total_k, n_heads_kv, head_dim]
- *   workspace    device memory of at least varlen_attn_bwd_workspace_size()
- *                bytes, 256-byte aligned; contents on entry are ignored
+ *   workspace    device memory of at least varlen_attn_bwd_workspace_size_cu()
+ *                bytes for this batch (varlen_attn_bwd_workspace_size() bounds
+ *                it for any batch), 256-byte aligned; contents on entry are
+ *                ignored
  * No atomics: results are bitwise deterministic for given inputs (the dK/dV
  * sums over a kv group's q heads run in a fixed order).
  * Errors: as the forward, plus VL_EWORKSPACE.

@@ -115,12 +115,46 @@ def test_fwd_rejects_bad_arguments(kw, code):
     assert rc == code and msg
 
 
+def _align256(x):
+    return (x + 255) // 256 * 256
+
+
+def test_bwd_workspace_sizes():
+    L = vl.lib()
+    # one short document: its only key tile outlasts the per-CU share of the
+    # pass, so the group of two q heads is split in two, which is also the bound
+    cu = np.array([0, 8], np.int32)
+    ip = cu.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))
+    two = _align256(8 * 4 * 4) + _align256(2 * 2 * 8 * 2 * 64 * 4)
+    assert L.varlen_attn_bwd_workspace_size_cu(ip, ip, 1, 8, 8, 4, 2, 64, 1) == two
+    assert L.varlen_attn_bwd_workspace_size(8, 8, 4, 2, 64) == two
+    # 120 equal short documents spread over the device: no split, D only
+    cu120 = np.arange(0, 121 * 200, 200, dtype=np.int32)
+    p120 = cu120.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))
+    assert L.varlen_attn_bwd_workspace_size_cu(p120, p120, 120, 24000, 24000, 32, 4, 128, 1) == _align256(24000 * 32 * 4)
+    # any batch: D plus 0, 2 or 4 fp32 dK/dV partials, never above the bound
+    for w in (workloads.longtail_16k(), workloads.mixed_128k(), workloads.ulysses_384k()):
+        cu = np.asarray(w.cu, np.int32)
+        ip = cu.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))
+        got = L.varlen_attn_bwd_workspace_size_cu(ip, ip, len(cu) - 1, w.total, w.total, w.hq, w.hkv, w.d, 1)
+        delta = _align256(w.total * w.hq * 4)
+        part = w.total * w.hkv * w.d * 4
+        assert got in {delta, delta + _align256(2 * 2 * part), delta + _align256(4 * 2 * part)}, w.name
+        assert got <= L.varlen_attn_bwd_workspace_size(w.total, w.total, w.hq, w.hkv, w.d)
+        assert vl.bwd_workspace_bytes_cu(w.cu, w.cu, w.hq, w.hkv, w.d) == got
+    # invalid arguments give 0
+    bad = np.array([0, 9], np.int32)
+    bp = bad.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))
+    assert L.varlen_attn_bwd_workspace_size_cu(bp, bp, 1, 8, 8, 4, 2, 64, 1) == 0
+    assert L.varlen_attn_bwd_workspace_size_cu(ip, ip, 1, 8, 8, 4, 3, 64, 1) == 0
+
+
 def test_bwd_rejects_small_workspace():
     L = vl.lib()
     cu = np.array([0, 8], np.int32)
     ip = cu.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))
     f = ctypes.c_void_p(FAKE)
-    need = L.varlen_attn_bwd_workspace_size(8, 8, 4, 2, 64)
+    need = L.varlen_attn_bwd_workspace_size_cu(ip, ip, 1, 8, 8, 4, 2, 64, 1)
     assert need > 0
     rc = L.varlen_attn_bwd(f, f, f, f, f, f, ip, ip, 1, 8, 8, 4, 2, 64, 0.0, 1, f, f, f, f, need - 1, None)
     assert rc == -6
@@ -293,3 +327,90 @@ def test_plan_cache_switch_returns_previous_setting():
         assert vl.set_plan_cache(True) is True
     finally:
         vl.set_plan_cache(prev)
+
+
+# ---------------------------------------------------------------- binding argument checks
+# The C ABI derives every size from q and k; the binding checks the other
+# tensors' shapes and dtypes before any pointer reaches the library.  CPU
+# tensors are enough: the checks fire before the GPU-placement check.
+def _bf(*shape):
+    import torch
+    return torch.zeros(shape, dtype=torch.bfloat16)
+
+
+def _f32(*shape):
+    import torch
+    return torch.zeros(shape, dtype=torch.float32)
+
+
+def test_fwd_binding_rejects_mismatched_tensors():
+    cu = np.array([0, 8], np.int32)
+    q, k, v = _bf(8, 4, 64), _bf(8, 2, 64), _bf(8, 2, 64)
+    with pytest.raises(ValueError, match="v must have shape"):
+        vl.varlen_attn_fwd(q, k, _bf(8, 1, 64), cu, cu)
+    with pytest.raises(TypeError, match="k must be bfloat16"):
+        vl.varlen_attn_fwd(q, k.float(), v, cu, cu)
+    with pytest.raises(ValueError, match="share head_dim"):
+        vl.varlen_attn_fwd(q, _bf(8, 2, 128), _bf(8, 2, 128), cu, cu)
+    with pytest.raises(ValueError, match="out must have shape"):
+        vl.varlen_attn_fwd(q, k, v, cu, cu, out=_bf(8, 4, 32))
+    with pytest.raises(ValueError, match="lse must have shape"):
+        vl.varlen_attn_fwd(q, k, v, cu, cu, lse=_f32(8, 4))
+    with pytest.raises(TypeError, match="lse must be float32"):
+        vl.varlen_attn_fwd(q, k, v, cu, cu, lse=_bf(4, 8))
+    with pytest.raises(TypeError, match="out_dtype"):
+        import torch
+        vl.varlen_attn_fwd(q, k, v, cu, cu, out_dtype=torch.float16)
+    with pytest.raises(ValueError, match="lse_acc must have shape"):
+        vl.varlen_attn_fwd_acc(q, k, v, cu, cu, _f32(8, 4, 64), _f32(8, 4))
+
+
+def test_bwd_binding_rejects_mismatched_tensors():
+    cu = np.array([0, 8], np.int32)
+    q, k, v = _bf(8, 4, 64), _bf(8, 2, 64), _bf(8, 2, 64)
+    o, do, lse = _bf(8, 4, 64), _bf(8, 4, 64), _f32(4, 8)
+    # an fp32 O (what out_dtype=float32 returns) would be read as bf16 pairs
+    with pytest.raises(TypeError, match="o must be bfloat16"):
+        vl.varlen_attn_bwd(q, k, v, o.float(), do, lse, cu, cu)
+    with pytest.raises(ValueError, match="do must have shape"):
+        vl.varlen_attn_bwd(q, k, v, o, _bf(8, 2, 64), lse, cu, cu)
+    with pytest.raises(ValueError, match="lse must have shape"):
+        vl.varlen_attn_bwd(q, k, v, o, do, _f32(2, 8), cu, cu)
+    with pytest.raises(ValueError, match="v must have shape"):
+        vl.varlen_attn_bwd(q, k, _bf(7, 2, 64), o, do, lse, cu, cu)
+    with pytest.raises(ValueError, match="dk must have shape"):
+        vl.varlen_attn_bwd(q, k, v, o, do, lse, cu, cu, dk=_bf(8, 4, 64))
+    with pytest.raises(TypeError, match="dv must be bfloat16"):
+        vl.varlen_attn_bwd(q, k, v, o, do, lse, cu, cu, dv=_f32(8, 2, 64))
+    with pytest.raises(ValueError, match="dq must have shape"):
+        vl.varlen_attn_bwd(q, k, v, o, do, lse, cu, cu, dq=_bf(8, 2, 64))
+    with pytest.raises(TypeError, match="workspace"):
+        vl.varlen_attn_bwd(q, k, v, o, do, lse, cu, cu, workspace=_f32(1 << 16))
+
+
+def test_merge_and_permute_bindings_reject_mismatched_tensors():
+    o1, o2 = _f32(8, 2, 16), _f32(8, 2, 16)
+    l1, l2 = _f32(2, 8), _f32(2, 8)
+    with pytest.raises(ValueError, match=r"lse_parts\[1\] must have shape"):
+        vl.attn_lse_merge([o1, o2], [l1, _f32(8, 2)])
+    with pytest.raises(TypeError, match=r"o_parts\[1\] must be float32"):
+        vl.attn_lse_merge([o1, o2.bfloat16()], [l1, l2])
+    with pytest.raises(ValueError, match="out must have shape"):
+        vl.attn_lse_merge([o1, o2], [l1, l2], out=_bf(8, 2, 8))
+    with pytest.raises(ValueError, match="lse_out must have shape"):
+        vl.attn_lse_merge([o1, o2], [l1, l2], lse_out=_f32(8, 2))
+    x = _bf(16, 8, 32)
+    with pytest.raises(ValueError, match="out must have shape"):
+        vl.sp_seq2head(x, 4, out=_bf(4, 16, 4, 32))
+    with pytest.raises(TypeError, match="out must be bfloat16"):
+        vl.sp_seq2head(x, 4, out=_f32(4, 16, 2, 32))
+    with pytest.raises(ValueError, match="out must have shape"):
+        vl.sp_head2seq(_bf(4, 16, 2, 32), out=_bf(16, 4, 32))
+    q, k, v = _bf(16, 8, 32), _bf(16, 2, 32), _bf(16, 2, 32)
+    with pytest.raises(ValueError, match=r"out\[1\] must have shape"):
+        vl.sp_qkv_seq2head(q, k, v, 4, out=(_bf(4, 16, 2, 32), _bf(4, 16, 2, 32), _bf(4, 16, 1, 32)))
+    yq, yk = _bf(4, 16, 2, 32), _bf(4, 16, 1, 32)
+    with pytest.raises(ValueError, match="yk must have shape"):
+        vl.sp_qkv_head2seq(yq, _bf(4, 16, 2, 32), _bf(4, 16, 2, 32), 2)
+    with pytest.raises(ValueError, match=r"out\[2\] must have shape"):
+        vl.sp_qkv_head2seq(yq, yk, yk, 2, out=(_bf(16, 8, 32), _bf(16, 2, 32), _bf(16, 4, 32)))

@@ -149,6 +149,52 @@ def test_schedule_covers_each_visible_pair_once(rng, causal, bq, bk):
         assert keys == sorted(keys)
 
 
+def _brute_issued_area(items, bq, bk, col):
+    """Cells of the issued tiles, enumerated one by one (tile cells past a
+    document's end included: the area the kernels compute)."""
+    n = 0
+    for it in items:
+        if col == "fwd":
+            tiles = [(int(it[1]), j) for j in range(int(it[2]), int(it[2]) + int(it[3]))]
+        else:
+            tiles = [(t, int(it[1])) for t in range(int(it[2]), int(it[2]) + int(it[3]))]
+        for t, j in tiles:
+            for _i in range(t * bq, (t + 1) * bq):
+                for _kk in range(j * bk, (j + 1) * bk):
+                    n += 1
+    return n
+
+
+@pytest.mark.parametrize("causal", [True, False])
+@pytest.mark.parametrize("bq,bk", [(4, 8), (8, 4), (3, 5)])
+def test_issued_pairs_equals_enumerated_tile_area(rng, causal, bq, bk):
+    for _ in range(4):
+        lq = rng.integers(0, 30, size=4)
+        lk = lq.copy() if rng.random() < 0.5 else rng.integers(0, 30, size=4)
+        cq = np.concatenate([[0], np.cumsum(lq)]).astype(np.int32)
+        ck = np.concatenate([[0], np.cumsum(lk)]).astype(np.int32)
+        f = schedule.fwd_items(cq, ck, causal, bq, bk)
+        bw = schedule.bwd_items(cq, ck, causal, bq, bk)
+        assert schedule.issued_pairs(f, bq, bk) == _brute_issued_area(f, bq, bk, "fwd")
+        assert schedule.issued_pairs(bw, bq, bk) == _brute_issued_area(bw, bq, bk, "bwd")
+        # the issued area covers every visible pair
+        assert schedule.issued_pairs(f, bq, bk) >= schedule.visible_pairs(cq, ck, causal)
+
+
+def test_issued_pairs_tiny_batch_by_hand():
+    # documents [17, 64, 128, 47], causal.  Forward tiles of 128 query rows x
+    # 64 keys: one query tile per document; the 128-token document needs two
+    # key tiles, the others one -> 5 tiles of 8192 cells.  dK/dV tiles of 32
+    # query rows x 128 keys: one key tile per document with 1, 2, 4 and 2
+    # query tiles -> 9 tiles of 4096 cells.
+    cu = np.array([0, 17, 81, 209, 256], dtype=np.int32)
+    f = schedule.fwd_items(cu, cu, True, 128, 64)
+    bw = schedule.bwd_items(cu, cu, True, 32, 128)
+    assert schedule.issued_pairs(f, 128, 64) == 5 * 128 * 64 == 40960
+    assert schedule.issued_pairs(bw, 32, 128) == 9 * 32 * 128 == 36864
+    assert round(schedule.visible_pairs(cu, cu, True) / 40960, 3) == 0.284
+
+
 def test_visible_pairs_closed_form():
     lengths = [17, 64, 128, 47]
     cu = np.concatenate([[0], np.cumsum(lengths)]).astype(np.int32)

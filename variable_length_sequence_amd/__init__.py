@@ -34,7 +34,8 @@ VL_BF16, VL_F32 = 0, 1
 STATUS = {0: "VL_OK", -1: "VL_EINVAL", -2: "VL_ESHAPE", -3: "VL_ESEQLENS",
           -4: "VL_EUNSUPPORTED", -5: "VL_EHIP", -6: "VL_EWORKSPACE"}
 
-EXPORTS = ["varlen_attn_fwd", "varlen_attn_bwd_workspace_size", "varlen_attn_bwd",
+EXPORTS = ["varlen_attn_fwd", "varlen_attn_bwd_workspace_size", "varlen_attn_bwd_workspace_size_cu",
+           "varlen_attn_bwd",
            "attn_lse_merge", "sp_seq2head", "sp_head2seq", "varlen_schedule_export",
            "varlen_last_error", "varlen_cache_clear", "varlen_set_plan_cache", "varlen_version",
            "varlen_profile_enable", "varlen_profile_read", "varlen_ring_block", "varlen_attn_fwd_acc", "sp_qkv_seq2head",
@@ -83,6 +84,8 @@ def lib():
     L.varlen_attn_fwd_acc.restype = ctypes.c_int
     L.varlen_attn_bwd_workspace_size.argtypes = [i64, i64, i32, i32, i32]
     L.varlen_attn_bwd_workspace_size.restype = ctypes.c_size_t
+    L.varlen_attn_bwd_workspace_size_cu.argtypes = [pi32, pi32, i32, i64, i64, i32, i32, i32, i32]
+    L.varlen_attn_bwd_workspace_size_cu.restype = ctypes.c_size_t
     L.varlen_attn_bwd.argtypes = [vp, vp, vp, vp, vp, vp, pi32, pi32, i32, i64, i64, i32, i32, i32,
                                   f32, i32, vp, vp, vp, vp, ctypes.c_size_t, vp]
     L.varlen_attn_bwd.restype = ctypes.c_int
@@ -153,6 +156,35 @@ def _stream():
     return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
 
 
+def _want(t, name: str, shape, dtypes, device=None):
+    """Check a tensor argument before any pointer reaches the library: the C
+    ABI derives every size from q and k, so a mismatched second input or
+    output buffer would be read or written out of bounds."""
+    if tuple(t.shape) != tuple(int(x) for x in shape):
+        raise ValueError(f"{name} must have shape {tuple(int(x) for x in shape)}, got {tuple(t.shape)}")
+    if t.dtype not in dtypes:
+        names = " or ".join(str(d).replace("torch.", "") for d in dtypes)
+        raise TypeError(f"{name} must be {names}, got {str(t.dtype).replace('torch.', '')}")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} must be on {device}, got {t.device}")
+
+
+def _qkv_shapes(q, k, v):
+    """(tq, hq, d, tk, hkv) of bf16 q [Tq,Hq,d] and k, v [Tk,Hkv,d]."""
+    import torch
+    if q.dim() != 3 or k.dim() != 3:
+        raise ValueError("q must be [Tq, Hq, d] and k, v [Tk, Hkv, d]")
+    tq, hq, d = q.shape
+    tk, hkv, dk = k.shape
+    if dk != d:
+        raise ValueError(f"q and k must share head_dim, got {d} and {dk}")
+    bf = (torch.bfloat16,)
+    _want(q, "q", (tq, hq, d), bf)
+    _want(k, "k", (tk, hkv, d), bf, q.device)
+    _want(v, "v", (tk, hkv, d), bf, q.device)
+    return tq, hq, d, tk, hkv
+
+
 def _dev_ptr(t) -> ctypes.c_void_p:
     if not t.is_cuda:
         raise ValueError("tensors must live on the GPU")
@@ -166,16 +198,16 @@ def varlen_attn_fwd(q, k, v, cu_q, cu_k, causal: bool = True, scale: Optional[fl
     """Packed varlen attention forward.  q [Tq,Hq,d], k/v [Tk,Hkv,d] bf16 -> (o, lse[Hq,Tq])."""
     import torch
     out_dtype = torch.bfloat16 if out_dtype is None else out_dtype
+    if out_dtype not in (torch.bfloat16, torch.float32):
+        raise TypeError("out_dtype must be bfloat16 or float32")
     cq, ck = _cu_host(cu_q), _cu_host(cu_k)
-    tq, hq, d = q.shape
-    tk, hkv, _ = k.shape
-    for t in (q, k, v):
-        if t.dtype != torch.bfloat16:
-            raise TypeError("q, k and v must be bfloat16")
+    tq, hq, d, tk, hkv = _qkv_shapes(q, k, v)
     if out is None:
         out = torch.empty((tq, hq, d), dtype=out_dtype, device=q.device)
     if lse is None:
         lse = torch.empty((hq, tq), dtype=torch.float32, device=q.device)
+    _want(out, "out", (tq, hq, d), (torch.bfloat16, torch.float32), q.device)
+    _want(lse, "lse", (hq, tq), (torch.float32,), q.device)
     od = VL_F32 if out.dtype == torch.float32 else VL_BF16
     _check(lib().varlen_attn_fwd(_dev_ptr(q), _dev_ptr(k), _dev_ptr(v), _iptr(cq), _iptr(ck),
                                  len(cq) - 1, tq, tk, hq, hkv, d, float(scale or 0.0), int(causal),
@@ -189,15 +221,9 @@ def varlen_attn_fwd_acc(q, k, v, cu_q, cu_k, o_acc, lse_acc, causal: bool = True
     [Tq,Hq,d] and lse_acc [Hq,Tq] (in place; start from 0 and -inf)."""
     import torch
     cq, ck = _cu_host(cu_q), _cu_host(cu_k)
-    tq, hq, d = q.shape
-    tk, hkv, _ = k.shape
-    for t in (q, k, v):
-        if t.dtype != torch.bfloat16:
-            raise TypeError("q, k and v must be bfloat16")
-    if o_acc.dtype != torch.float32 or lse_acc.dtype != torch.float32:
-        raise TypeError("o_acc and lse_acc must be float32")
-    if tuple(o_acc.shape) != (tq, hq, d) or tuple(lse_acc.shape) != (hq, tq):
-        raise ValueError("o_acc must be [Tq, Hq, d] and lse_acc [Hq, Tq]")
+    tq, hq, d, tk, hkv = _qkv_shapes(q, k, v)
+    _want(o_acc, "o_acc", (tq, hq, d), (torch.float32,), q.device)
+    _want(lse_acc, "lse_acc", (hq, tq), (torch.float32,), q.device)
     _check(lib().varlen_attn_fwd_acc(_dev_ptr(q), _dev_ptr(k), _dev_ptr(v), _iptr(cq), _iptr(ck),
                                      len(cq) - 1, tq, tk, hq, hkv, d, float(scale or 0.0),
                                      int(causal), _dev_ptr(o_acc), _dev_ptr(lse_acc), _stream()))
@@ -210,14 +236,23 @@ def varlen_attn_bwd(q, k, v, o, do, lse, cu_q, cu_k, causal: bool = True,
     given tensors when passed)."""
     import torch
     cq, ck = _cu_host(cu_q), _cu_host(cu_k)
-    tq, hq, d = q.shape
-    tk, hkv, _ = k.shape
+    tq, hq, d, tk, hkv = _qkv_shapes(q, k, v)
+    bf = (torch.bfloat16,)
+    _want(o, "o", (tq, hq, d), bf, q.device)
+    _want(do, "do", (tq, hq, d), bf, q.device)
+    _want(lse, "lse", (hq, tq), (torch.float32,), q.device)
     dq = torch.empty_like(q) if dq is None else dq
     dk = torch.empty_like(k) if dk is None else dk
     dv = torch.empty_like(v) if dv is None else dv
-    need = lib().varlen_attn_bwd_workspace_size(tq, tk, hq, hkv, d)
+    _want(dq, "dq", (tq, hq, d), bf, q.device)
+    _want(dk, "dk", (tk, hkv, d), bf, q.device)
+    _want(dv, "dv", (tk, hkv, d), bf, q.device)
+    need = lib().varlen_attn_bwd_workspace_size_cu(_iptr(cq), _iptr(ck), len(cq) - 1, tq, tk, hq,
+                                                   hkv, d, int(causal))
     if workspace is None:
         workspace = torch.empty(max(int(need), 256), dtype=torch.uint8, device=q.device)
+    if workspace.dtype != torch.uint8 or workspace.dim() != 1:
+        raise TypeError("workspace must be a 1-D uint8 tensor")
     _check(lib().varlen_attn_bwd(_dev_ptr(q), _dev_ptr(k), _dev_ptr(v), _dev_ptr(o), _dev_ptr(do),
                                  _dev_ptr(lse), _iptr(cq), _iptr(ck), len(cq) - 1, tq, tk, hq, hkv,
                                  d, float(scale or 0.0), int(causal), _dev_ptr(dq), _dev_ptr(dk),
@@ -226,7 +261,16 @@ def varlen_attn_bwd(q, k, v, o, do, lse, cu_q, cu_k, causal: bool = True,
 
 
 def bwd_workspace_bytes(tq: int, tk: int, hq: int, hkv: int, d: int) -> int:
+    """Workspace bound for any batch of these sizes."""
     return int(lib().varlen_attn_bwd_workspace_size(tq, tk, hq, hkv, d))
+
+
+def bwd_workspace_bytes_cu(cu_q, cu_k, hq: int, hkv: int, d: int, causal: bool = True) -> int:
+    """Workspace this batch needs on the current device."""
+    cq, ck = _cu_host(cu_q), _cu_host(cu_k)
+    return int(lib().varlen_attn_bwd_workspace_size_cu(_iptr(cq), _iptr(ck), len(cq) - 1,
+                                                       int(cq[-1]), int(ck[-1]), hq, hkv, d,
+                                                       int(causal)))
 
 
 def attn_lse_merge(o_parts: Sequence, lse_parts: Sequence, out_dtype=None, out=None, lse_out=None):
@@ -236,15 +280,22 @@ def attn_lse_merge(o_parts: Sequence, lse_parts: Sequence, out_dtype=None, out=N
     n = len(o_parts)
     if n == 0 or n != len(lse_parts):
         raise ValueError("need the same positive number of O and LSE partials")
+    if o_parts[0].dim() != 3:
+        raise ValueError("partial O must be [T, H, d]")
     t, h, d = o_parts[0].shape
     in_dt = o_parts[0].dtype
-    for o, l in zip(o_parts, lse_parts):
-        if o.shape != (t, h, d) or o.dtype != in_dt or l.shape != (h, t) or l.dtype != torch.float32:
-            raise ValueError("partials must share shape and dtype; LSE is fp32 [H, T]")
+    if in_dt not in (torch.bfloat16, torch.float32):
+        raise TypeError("partial O must be bfloat16 or float32")
+    dev = o_parts[0].device
+    for i, (o, l) in enumerate(zip(o_parts, lse_parts)):
+        _want(o, f"o_parts[{i}]", (t, h, d), (in_dt,), dev)
+        _want(l, f"lse_parts[{i}]", (h, t), (torch.float32,), dev)
     if out is None:
-        out = torch.empty((t, h, d), dtype=out_dtype, device=o_parts[0].device)
+        out = torch.empty((t, h, d), dtype=out_dtype, device=dev)
     if lse_out is None:
-        lse_out = torch.empty((h, t), dtype=torch.float32, device=o_parts[0].device)
+        lse_out = torch.empty((h, t), dtype=torch.float32, device=dev)
+    _want(out, "out", (t, h, d), (torch.bfloat16, torch.float32), dev)
+    _want(lse_out, "lse_out", (h, t), (torch.float32,), dev)
     op = (ctypes.c_void_p * n)(*[_dev_ptr(o).value for o in o_parts])
     lp = (ctypes.c_void_p * n)(*[_dev_ptr(l).value for l in lse_parts])
     idt = VL_F32 if in_dt == torch.float32 else VL_BF16
@@ -257,11 +308,16 @@ def attn_lse_merge(o_parts: Sequence, lse_parts: Sequence, out_dtype=None, out=N
 def sp_seq2head(x, sp_degree: int, out=None):
     """[n, H, d] -> [P, n, H/P, d] (chunk p = heads p*H/P .. (p+1)*H/P - 1)."""
     import torch
+    if x.dim() != 3:
+        raise ValueError("x must be [n, H, d]")
     n, H, d = x.shape
-    if H % sp_degree:
+    if sp_degree <= 0 or H % sp_degree:
         raise ValueError("sp_degree must divide the head count")
+    if x.element_size() not in (2, 4):
+        raise TypeError("elements must be 2 or 4 bytes")
     if out is None:
         out = torch.empty((sp_degree, n, H // sp_degree, d), dtype=x.dtype, device=x.device)
+    _want(out, "out", (sp_degree, n, H // sp_degree, d), (x.dtype,), x.device)
     _check(lib().sp_seq2head(_dev_ptr(x), _dev_ptr(out), n, H, d, sp_degree, x.element_size(),
                              _stream()))
     return out
@@ -270,9 +326,14 @@ def sp_seq2head(x, sp_degree: int, out=None):
 def sp_head2seq(y, out=None):
     """[P, n, h, d] -> [n, P*h, d], the inverse of sp_seq2head."""
     import torch
+    if y.dim() != 4:
+        raise ValueError("y must be [P, n, h, d]")
     P, n, h, d = y.shape
+    if y.element_size() not in (2, 4):
+        raise TypeError("elements must be 2 or 4 bytes")
     if out is None:
         out = torch.empty((n, P * h, d), dtype=y.dtype, device=y.device)
+    _want(out, "out", (n, P * h, d), (y.dtype,), y.device)
     _check(lib().sp_head2seq(_dev_ptr(y), _dev_ptr(out), n, P * h, d, P, y.element_size(),
                              _stream()))
     return out
@@ -292,16 +353,26 @@ def sp_qkv_seq2head(q, k, v, sp_degree: int, out=None):
     Returns (yq [P,n,Hq/P,d], yk, yv [P,n,hk,d]) with hk = Hkv/P, or 1 with each
     kv head replicated to the P/Hkv ranks that read it when Hkv < P."""
     import torch
+    if q.dim() != 3 or k.dim() != 3:
+        raise ValueError("q must be [n, Hq, d] and k, v [n, Hkv, d]")
     n, hq, d = q.shape
     hkv = k.shape[1]
     if k.shape != v.shape or k.shape[0] != n or k.shape[2] != d:
         raise ValueError("k and v must be [n, Hkv, d] with q's n and d")
+    if sp_degree <= 0 or hq % sp_degree:
+        raise ValueError("sp_degree must divide n_heads_q")
     hk = hkv // sp_degree if hkv >= sp_degree else 1
     if out is None:
         out = (torch.empty((sp_degree, n, hq // sp_degree, d), dtype=q.dtype, device=q.device),
                torch.empty((sp_degree, n, hk, d), dtype=q.dtype, device=q.device),
                torch.empty((sp_degree, n, hk, d), dtype=q.dtype, device=q.device))
     dt = _qkv_dtype(q, k, v, *out)
+    _want(out[0], "out[0]", (sp_degree, n, hq // sp_degree, d), (q.dtype,), q.device)
+    _want(out[1], "out[1]", (sp_degree, n, hk, d), (q.dtype,), q.device)
+    _want(out[2], "out[2]", (sp_degree, n, hk, d), (q.dtype,), q.device)
+    for name, t in (("k", k), ("v", v)):
+        if t.device != q.device:
+            raise ValueError(f"{name} must be on {q.device}")
     _check(lib().sp_qkv_seq2head(_dev_ptr(q), _dev_ptr(k), _dev_ptr(v), *map(_dev_ptr, out), n, hq,
                                  hkv, d, sp_degree, dt, _stream()))
     return out
@@ -311,14 +382,22 @@ def sp_qkv_head2seq(yq, yk, yv, n_heads_kv: int, out=None):
     """Unpack (dq, dk, dv) after the gradient exchange in one launch; the
     adjoint of sp_qkv_seq2head (replicated kv heads are summed in fp32)."""
     import torch
+    if yq.dim() != 4:
+        raise ValueError("yq must be [P, n, Hq/P, d]")
     P, n, hq, d = yq.shape
-    if yk.shape != yv.shape:
-        raise ValueError("yk and yv must have the same shape")
+    if n_heads_kv <= 0:
+        raise ValueError("n_heads_kv must be positive")
+    hk = n_heads_kv // P if n_heads_kv >= P else 1
+    _want(yk, "yk", (P, n, hk, d), (yq.dtype,), yq.device)
+    _want(yv, "yv", (P, n, hk, d), (yq.dtype,), yq.device)
     if out is None:
         out = (torch.empty((n, P * hq, d), dtype=yq.dtype, device=yq.device),
                torch.empty((n, n_heads_kv, d), dtype=yq.dtype, device=yq.device),
                torch.empty((n, n_heads_kv, d), dtype=yq.dtype, device=yq.device))
     dt = _qkv_dtype(yq, yk, yv, *out)
+    _want(out[0], "out[0]", (n, P * hq, d), (yq.dtype,), yq.device)
+    _want(out[1], "out[1]", (n, n_heads_kv, d), (yq.dtype,), yq.device)
+    _want(out[2], "out[2]", (n, n_heads_kv, d), (yq.dtype,), yq.device)
     _check(lib().sp_qkv_head2seq(_dev_ptr(yq), _dev_ptr(yk), _dev_ptr(yv), *map(_dev_ptr, out), n,
                                  P * hq, n_heads_kv, d, P, dt, _stream()))
     return out

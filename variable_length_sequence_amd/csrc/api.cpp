@@ -309,6 +309,52 @@ int max_head_split(int32_t hq, int32_t hkv) {
   return split;
 }
 
+// Compute units of the current device (cached per device).
+int device_cus() {
+  static std::mutex mu;
+  static std::map<int, int> cache;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 256;
+  std::lock_guard<std::mutex> lock(mu);
+  auto it = cache.find(dev);
+  if (it != cache.end()) return it->second;
+  int n_cu = 0;
+  if (hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+      n_cu <= 0)
+    n_cu = 256;
+  cache[dev] = n_cu;
+  return n_cu;
+}
+
+// The q-head split of the dK/dV pass: the q heads of a group go to 2-4
+// workgroups when one item would otherwise outlast the average per-CU share
+// of the whole pass (only the item counts of the dK/dV list matter).
+int choose_split(const int32_t* cu_q, const int32_t* cu_k, int32_t n_docs, int causal,
+                 int32_t hq, int32_t hkv, int n_cu) {
+  const std::vector<vl::Doc> docs = vl::doc_table(cu_q, cu_k, n_docs);
+  const std::vector<vl::Item> items = vl::bwd_items(docs, causal != 0, vl::kBwdBQ, vl::kBwdBK);
+  int64_t total_count = 0;
+  int32_t max_count = 0;
+  for (const auto& it : items) {
+    total_count += it.count;
+    max_count = std::max(max_count, it.count);
+  }
+  const int grp = hq / hkv;
+  const double per_cu = double(total_count) * grp * hkv / double(std::max(n_cu, 1));
+  int split = 1;
+  while (split < max_head_split(hq, hkv) && double(max_count) * grp / split > per_cu) split *= 2;
+  return split;
+}
+
+// Workspace of one backward call: D [Hq, Tq] fp32, then the fp32 dK/dV
+// partials of the q-head slices when the group is split.
+size_t bwd_workspace_bytes(int64_t total_q, int64_t total_k, int32_t hq, int32_t hkv, int32_t d,
+                           int split) {
+  return align256(size_t(total_q) * size_t(hq) * 4) +
+         (split > 1 ? align256(size_t(split) * 2 * size_t(total_k) * size_t(hkv) * size_t(d) * 4)
+                    : 0);
+}
+
 }  // namespace
 
 extern "C" {
@@ -391,9 +437,30 @@ int varlen_attn_fwd_acc(const void* q, const void* k, const void* v, const int32
 size_t varlen_attn_bwd_workspace_size(int64_t total_q, int64_t total_k, int32_t n_heads_q,
                                       int32_t n_heads_kv, int32_t head_dim) {
   if (total_q < 0 || total_k < 0 || n_heads_q <= 0 || n_heads_kv <= 0 || head_dim <= 0) return 0;
-  return align256(size_t(total_q) * size_t(n_heads_q) * 4) +
-         align256(size_t(max_head_split(n_heads_q, n_heads_kv)) * 2 * size_t(total_k) *
-                  size_t(n_heads_kv) * size_t(head_dim) * 4);
+  if (n_heads_q % n_heads_kv) return 0;
+  return bwd_workspace_bytes(total_q, total_k, n_heads_q, n_heads_kv, head_dim,
+                             max_head_split(n_heads_q, n_heads_kv));
+}
+
+size_t varlen_attn_bwd_workspace_size_cu(const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
+                                         int32_t n_docs, int64_t total_q, int64_t total_k,
+                                         int32_t n_heads_q, int32_t n_heads_kv, int32_t head_dim,
+                                         int32_t causal) {
+  try {
+    g_err.clear();
+    if (!cu_seqlens_q || !cu_seqlens_k || n_docs < 0 || total_q < 0 || total_k < 0 ||
+        n_heads_q <= 0 || n_heads_kv <= 0 || head_dim <= 0 || n_heads_q % n_heads_kv)
+      return 0;
+    std::string err;
+    if (!vl::validate_cu(cu_seqlens_q, n_docs, total_q, err) ||
+        !vl::validate_cu(cu_seqlens_k, n_docs, total_k, err))
+      return 0;
+    const int split = choose_split(cu_seqlens_q, cu_seqlens_k, n_docs, causal, n_heads_q,
+                                   n_heads_kv, device_cus());
+    return bwd_workspace_bytes(total_q, total_k, n_heads_q, n_heads_kv, head_dim, split);
+  } catch (...) {
+    return 0;
+  }
 }
 
 int varlen_attn_bwd(const void* q, const void* k, const void* v, const void* out, const void* dout,
@@ -413,7 +480,10 @@ int varlen_attn_bwd(const void* q, const void* k, const void* v, const void* out
                          reinterpret_cast<uintptr_t>(dq) | reinterpret_cast<uintptr_t>(dk) |
                          reinterpret_cast<uintptr_t>(dv);
     if (al % 16) return fail(VL_EINVAL, "out, dout, dq, dk and dv must be 16-byte aligned");
-    const size_t need = varlen_attn_bwd_workspace_size(total_q, total_k, n_heads_q, n_heads_kv, head_dim);
+    const int n_cu = device_cus();
+    const int split = choose_split(cu_seqlens_q, cu_seqlens_k, n_docs, causal, n_heads_q,
+                                   n_heads_kv, n_cu);
+    const size_t need = bwd_workspace_bytes(total_q, total_k, n_heads_q, n_heads_kv, head_dim, split);
     if (!workspace || workspace_bytes < need)
       return fail(VL_EWORKSPACE, "workspace must hold at least " + std::to_string(need) + " bytes");
     if (reinterpret_cast<uintptr_t>(workspace) % 256) return fail(VL_EWORKSPACE, "workspace must be 256-byte aligned");
@@ -427,20 +497,6 @@ int varlen_attn_bwd(const void* q, const void* k, const void* v, const void* out
     const Plan& pf = pp[0];
     const Plan& pb = pp[1];
     // dK/dV of kv tiles that no query tile reaches are zeros written by the kernel
-    int dev = 0, n_cu = 256;
-    (void)hipGetDevice(&dev);
-    (void)hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev);
-    // split the q heads of a group over workgroups when one item would
-    // otherwise outlast the average per-CU share of the whole pass
-    const int grp = n_heads_q / n_heads_kv;
-    int split = 1;
-    {
-      const double total = double(pb.total_count) * grp * n_heads_kv;
-      const double per_cu = total / double(n_cu);
-      while (split < max_head_split(n_heads_q, n_heads_kv) &&
-             double(pb.max_count) * grp / split > per_cu)
-        split *= 2;
-    }
     float* delta = reinterpret_cast<float*>(workspace);
     float* dkv_acc = reinterpret_cast<float*>(reinterpret_cast<char*>(workspace) +
                                               align256(size_t(total_q) * size_t(n_heads_q) * 4));
