@@ -213,6 +213,49 @@ def cpu_baseline(w):
                       f"(O, LSE, dQ, dK, dV) of all {len(w.lengths)} documents x {w.hq} heads"}
 
 
+def cpu_sampled_checks(full_rate_tflops):
+    """The sampled oracle checks of the large workloads, timed on the host: the
+    forward and dQ of 64 sampled query rows per q head (what the GPU parity
+    tests compute per row), and the full oracle's time for each workload
+    extrapolated from the full-oracle rate measured on the headline batch."""
+    import numpy as np
+    import oracle
+    import workloads
+    res = {}
+    for wf in (workloads.ulysses_384k, workloads.ring_256k, workloads.mixed_128k):
+        w = wf()
+        q, k, v, do = workloads.make_tensors(w)
+        f = lambda t: t.float().numpy()
+        qn, kn, vn, don = f(q), f(k), f(v), f(do)
+        del q, k, v, do
+        cu = np.asarray(w.cu, np.int64)
+        if w.name == "ring_256k":   # query chunk 7 of the sequence
+            n, c, qc = w.extra["n_chunks"], w.extra["chunk"], w.extra["q_chunk"]
+            base, span = qc * c, c
+            pairs_full = 7 * c * c + c * (c + 1) // 2
+        else:
+            base, span = 0, w.total
+            pairs_full = oracle.schedule.visible_pairs(cu, cu, True)
+        rows = workloads.sample_rows(span, 64, seed=1) + base
+        rows = np.concatenate([rows] * w.hq)
+        heads = np.repeat(np.arange(w.hq), 64)
+        t0 = time.perf_counter()
+        oracle.attn_bwd_dq_rows(qn, kn, vn, don, cu, cu, rows, heads)
+        sec = time.perf_counter() - t0
+        doc = np.searchsorted(cu, rows, side="right") - 1
+        vis = int(np.sum(rows - cu[doc] + 1))   # causal: a row sees its document's keys up to itself
+        sflops = 8 * w.d * vis                  # per visible pair: S, PV, dP, dS K
+        full_flops = 14 * w.d * pairs_full * w.hq
+        res[w.name] = {"value": round(sflops / sec / 1e12, 5), "unit": "TFLOP/s",
+                       "kind": "oracle", "seconds": round(sec, 2),
+                       "sample": f"forward and dQ of 64 sampled query rows x {w.hq} q heads"
+                                 + (" of query chunk 7" if w.name == "ring_256k" else ""),
+                       "full_oracle_seconds_extrapolated": round(full_flops / (full_rate_tflops * 1e12), 1),
+                       "extrapolated_from": "the full-oracle TFLOP/s of the longtail_16k batch in this run"}
+        del qn, kn, vn, don
+    return res
+
+
 def measured_gemm_peak(torch, dev, n=8192, reps=20):
     """bf16 GEMM throughput of the vendor library (hipBLASLt via torch.matmul) on
     one n x n x n product: a measured stand-in for the reachable MFMA peak."""
@@ -349,10 +392,11 @@ def bench_ring(vl, torch, dev, steps):
     import workloads
     w = workloads.ring_256k()
     n, c, qc = w.extra["n_chunks"], w.extra["chunk"], w.extra["q_chunk"]
-    q, k, v, _ = workloads.make_tensors(w, with_do=False)
+    q, k, v, do = workloads.make_tensors(w)
     qd = q[qc * c:(qc + 1) * c].contiguous().to(dev)
+    dod = do[qc * c:(qc + 1) * c].contiguous().to(dev)
     kd, vd = k.to(dev), v.to(dev)
-    del q, k, v
+    del q, k, v, do
     one = np.array([0, c], np.int32)
     parts_o = [torch.empty(c, w.hq, w.d, dtype=torch.float32, device=dev) for _ in range(n)]
     parts_l = [torch.empty(w.hq, c, dtype=torch.float32, device=dev) for _ in range(n)]
@@ -389,12 +433,45 @@ def bench_ring(vl, torch, dev, steps):
         for _ in range(steps):
             step_acc()
     ms2 = tm2.wall_ms / steps
+
+    # the blockwise backward of the share: block j's backward with the merged
+    # O and LSE gives its share of dQ (summed in fp32) and chunk j's dK, dV
+    om, lm = step()
+    dq = torch.empty(c, w.hq, w.d, dtype=torch.float32, device=dev)
+    dk, dv = torch.empty_like(kd), torch.empty_like(vd)
+    dq_j = torch.empty_like(qd)
+    ws = torch.empty(max(vl.bwd_workspace_bytes_cu(one, one, w.hq, w.hkv, w.d, c), 256),
+                     dtype=torch.uint8, device=dev)
+
+    def step_bwd():
+        dq.zero_()
+        for j in range(n):
+            vl.varlen_attn_bwd(qd, kd[j * c:(j + 1) * c], vd[j * c:(j + 1) * c], om, dod, lm, one,
+                               one, causal=(j == qc), workspace=ws, dq=dq_j,
+                               dk=dk[j * c:(j + 1) * c], dv=dv[j * c:(j + 1) * c])
+            dq.add_(dq_j)
+    step_bwd()
+    vl.profile_enable(True)
+    with Timer(torch) as tm3:
+        for _ in range(steps):
+            step_bwd()
+    prof3 = vl.profile_read()
+    vl.profile_enable(False)
+    ms3 = tm3.wall_ms / steps
+    bflops = 10 * w.d * pairs * w.hq
     return {"workload": w.name, "ms_per_step": round(ms, 3),
             "tflops": round(flops / (ms * 1e-3) / 1e12, 2), "useful_tflop": round(flops / 1e12, 3),
             "kernels": kernel_table(prof, {}, {"lse_merge": merge_bytes}),
             "attn_fwd_avg_ms": round(prof["attn_fwd"][1] / prof["attn_fwd"][0], 4),
             "fused_merge": {"ms_per_step": round(ms2, 3),
-                            "tflops": round(flops / (ms2 * 1e-3) / 1e12, 2)}}
+                            "tflops": round(flops / (ms2 * 1e-3) / 1e12, 2)},
+            "backward": {"what": "8 block backwards with the merged O/LSE (dQ summed in fp32)",
+                         "ms_per_step": round(ms3, 3),
+                         "tflops": round(bflops / (ms3 * 1e-3) / 1e12, 2),
+                         "useful_tflop": round(bflops / 1e12, 3),
+                         "kernels": kernel_table(prof3, {}, {})},
+            "fwd_merge_bwd": {"ms_per_step": round(ms + ms3, 3),
+                              "tflops": round((flops + bflops) / ((ms + ms3) * 1e-3) / 1e12, 2)}}
 
 
 def main():
@@ -435,12 +512,16 @@ def main():
     w = workloads.longtail_16k()
     print(f"[bench] {w.name}: {len(w.lengths)} docs, {w.total} tokens, "
           f"{a.warmup} warmup + {a.steps} timed steps", file=sys.stderr, flush=True)
-    r = bench_attention(vl, torch, w, a.steps, a.warmup, dev)
+    # the headline: no timing events inside the step
+    r = bench_attention(vl, torch, w, a.steps, a.warmup, dev, profile=False)
+    # the same steps again with every kernel bracketed by HIP events on its
+    # launch stream: the per-kernel table and the roofline
+    rp = bench_attention(vl, torch, w, a.steps, a.warmup, dev, profile=True)
     kflops = attn_kernel_flops(r["pairs"], w.hq, w.d)
     bpre = 2 * w.total * w.hq * w.d * 2 + w.total * w.hq * 4
-    ktab = kernel_table(r["prof"], kflops, {"bwd_pre": bpre})
-    dom = max((n for n in kflops if n in r["prof"]), key=lambda n: r["prof"][n][1])
-    dom_avg = r["prof"][dom][1] / r["prof"][dom][0]
+    ktab = kernel_table(rp["prof"], kflops, {"bwd_pre": bpre})
+    dom = max((n for n in kflops if n in rp["prof"]), key=lambda n: rp["prof"][n][1])
+    dom_avg = rp["prof"][dom][1] / rp["prof"][dom][0]
     achieved = kflops[dom] / (dom_avg * 1e-3) / 1e12
     cached = bench_attention(vl, torch, w, a.steps, a.warmup, dev, profile=False, plan_cache=True)
     print("[bench] matrix-core probe", file=sys.stderr, flush=True)
@@ -469,6 +550,7 @@ def main():
         "step_ms_min": round(r["min_ms"], 4),
         "work_lists": "scheduled and uploaded by every call (plan cache off)",
         "ms_per_step_plan_cached": round(cached["ms"], 4),
+        "ms_per_step_profiled": round(rp["ms"], 4),
         "useful_tflop_per_step": round((r["flops_fwd"] + r["flops_bwd"]) / 1e12, 4),
         "roofline": {"bound": "mfma", "kernel": dom, "achieved": round(achieved, 2),
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
@@ -529,6 +611,9 @@ def main():
     if not a.no_cpu_baseline:
         print("[bench] cpu baseline (fp64 oracle)", file=sys.stderr, flush=True)
         out["cpu_baseline"] = cpu_baseline(w)
+        if not a.no_extra:
+            print("[bench] cpu baseline: sampled oracle checks", file=sys.stderr, flush=True)
+            out["cpu_baseline"]["other_workloads"] = cpu_sampled_checks(out["cpu_baseline"]["value"])
     print(json.dumps(out), flush=True)
 
 

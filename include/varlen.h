@@ -435,8 +435,10 @@ VL_API int varlen_profile_read(int32_t idx, char* name, int32_t name_cap,
 /* Message of the last failed call on this thread ("" if none). */
 VL_API const char* varlen_last_error(void);
 
-/* Free the cached device work lists.  The caller guarantees no launched
- * kernel still reads them (e.g. after a device or stream synchronize). */
+/* Free the cached device work lists, those pinned by captured graphs
+ * included.  The caller guarantees no launched kernel and no graph that may
+ * still be replayed reads them (e.g. after a device synchronize, once the
+ * graphs captured with the plan cache on are destroyed). */
 VL_API void varlen_cache_clear(void);
 
 /* Plan cache switch, process-wide; returns the previous setting (1 = on).
@@ -453,7 +455,12 @@ VL_API void varlen_cache_clear(void);
  * after the regions in flight have drained).  A call on a capturing stream
  * fails with VL_EUNSUPPORTED in this mode.
  * On: work lists are cached per cu_seqlens pattern as above, for patterns
- * that repeat and for graph capture (warm the pattern up before capturing). */
+ * that repeat and for graph capture.  Warm a pattern up before capturing: a
+ * new pattern on a capturing stream fails with VL_EUNSUPPORTED.  A plan used
+ * under capture is pinned (the graph holds its device address).  The cache
+ * keeps up to 4096 plans; a call with a new pattern on a full cache waits for
+ * the device and frees every plan that is not pinned, or fails with
+ * VL_EUNSUPPORTED when all 4096 are pinned (varlen_cache_clear frees them). */
 VL_API int varlen_set_plan_cache(int32_t on);
 
 /* ABI version, currently 1. */

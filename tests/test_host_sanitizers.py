@@ -8,6 +8,9 @@ launchers replaced by stand-ins that report failure
 (tests/host_asan/launch_stubs.cpp).  The CPU tests of the C ABI and the
 planner then run against that library in a child process with the
 sanitizer runtime preloaded; any report ends the child with an error.
+The plan cache's eviction rule (plan_cache.h) has a unit test of its own
+(tests/host_asan/plan_cache_test.cpp), built and run with the same
+sanitizers.
 """
 import os
 import shutil
@@ -75,3 +78,19 @@ def test_host_code_under_address_and_ub_sanitizers():
     tail = res.stdout[-2000:] + res.stderr[-2000:] + "".join(reports)
     assert res.returncode == 0 and not reports, tail
     assert "passed" in res.stdout, tail
+
+
+def test_plan_cache_eviction_rule_under_sanitizers():
+    if not _tool("g++"):
+        pytest.skip("needs g++")
+    os.makedirs(OUT, exist_ok=True)
+    exe = os.path.join(OUT, "plan_cache_test")
+    src = os.path.join(ROOT, "tests", "host_asan", "plan_cache_test.cpp")
+    res = subprocess.run(["g++", "-std=c++17", "-O1", "-g", "-fsanitize=address,undefined",
+                          "-fno-sanitize-recover=all", "-I" + CSRC, src, "-o", exe],
+                         capture_output=True, text=True)
+    assert res.returncode == 0, res.stderr[-3000:]
+    run = subprocess.run([exe], capture_output=True, text=True,
+                         env=dict(os.environ, ASAN_OPTIONS="detect_leaks=1"))
+    assert run.returncode == 0, run.stdout + run.stderr
+    assert "all checks passed" in run.stdout

@@ -13,6 +13,7 @@
 
 #include "varlen.h"
 #include "launch.h"
+#include "plan_cache.h"
 #include "router.h"
 #include "scheduler.h"
 
@@ -41,8 +42,8 @@ struct Plan {
 };
 
 std::mutex g_mu;
-std::map<std::string, Plan> g_plans;
 constexpr size_t kMaxPlans = 4096;
+vl::PlanCache<Plan> g_plans(kMaxPlans);
 
 std::string plan_key(int dev, int pass, int causal, const int32_t* cu_q, const int32_t* cu_k,
                      int32_t n_docs) {
@@ -56,11 +57,12 @@ std::string plan_key(int dev, int pass, int causal, const int32_t* cu_q, const i
 
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
-void clear_plans_locked() {
-  for (auto& kv : g_plans)
-    if (kv.second.dev) (void)hipFree(kv.second.dev);
-  g_plans.clear();
+void release_plan(Plan& p) {
+  if (p.dev) (void)hipFree(p.dev);
+  p.dev = nullptr;
 }
+
+void clear_plans_locked() { g_plans.clear(release_plan); }
 
 // pass 0: forward / dQ list (query tiles); pass 1: dK/dV list (key tiles).
 // Builds the list on the host in XCD slot order (a workgroup reads its item
@@ -91,26 +93,33 @@ void build_list(int pass, int causal, const int32_t* cu_q, const int32_t* cu_k, 
   }
 }
 
+// capturing: the caller's stream is being captured (the plan gets pinned).
 int get_plan(int pass, int causal, const int32_t* cu_q, const int32_t* cu_k, int32_t n_docs,
-             Plan& out) {
+             bool capturing, Plan& out) {
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
   const std::string key = plan_key(dev, pass, causal, cu_q, cu_k, n_docs);
   std::lock_guard<std::mutex> lock(g_mu);
-  auto itp = g_plans.find(key);
-  if (itp != g_plans.end()) {
-    out = itp->second;
+  if (const Plan* hit = g_plans.find(key, capturing)) {
+    out = *hit;
     return VL_OK;
   }
+  if (capturing)
+    return fail(VL_EUNSUPPORTED,
+                "a new cu_seqlens pattern under stream capture: run the call once before capturing");
   std::vector<vl::DevItem> host;
   Plan p;
   build_list(pass, causal, cu_q, cu_k, n_docs, host, p);
   if (!host.empty()) {
-    // a new pattern: drain the device before touching the allocator when the cache is full
+    // a new pattern: when the cache is full, drain the device and release the
+    // plans no captured graph holds
     if (g_plans.size() >= kMaxPlans) {
       (void)hipDeviceSynchronize();
-      clear_plans_locked();
+      if (!g_plans.make_room(release_plan))
+        return fail(VL_EUNSUPPORTED,
+                    "the plan cache is full of plans captured graphs may use: call "
+                    "varlen_cache_clear once those graphs are destroyed");
     }
     const size_t bytes = host.size() * sizeof(vl::DevItem);
     e = hipMalloc(&p.dev, bytes);
@@ -121,7 +130,7 @@ int get_plan(int pass, int causal, const int32_t* cu_q, const int32_t* cu_k, int
       return hip_fail(e, "hipMemcpy(work list)");
     }
   }
-  g_plans.emplace(key, p);
+  g_plans.insert(key, p, false);
   out = p;
   return VL_OK;
 }
@@ -227,15 +236,17 @@ class CallPlans {
   int get(int causal, const int32_t* cu_q, const int32_t* cu_k, int32_t n_docs,
           hipStream_t st, int n_pass, const int* passes, Plan* out) {
     if (n_pass < 1 || n_pass > 2) return fail(VL_EINVAL, "internal: one or two work lists per call");
+    hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+    const bool capturing =
+        hipStreamIsCapturing(st, &cs) == hipSuccess && cs != hipStreamCaptureStatusNone;
     if (g_cache_on.load()) {
       for (int i = 0; i < n_pass; ++i) {
-        const int rc = get_plan(passes[i], causal, cu_q, cu_k, n_docs, out[i]);
+        const int rc = get_plan(passes[i], causal, cu_q, cu_k, n_docs, capturing, out[i]);
         if (rc) return rc;
       }
       return VL_OK;
     }
-    hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
-    if (hipStreamIsCapturing(st, &cs) == hipSuccess && cs != hipStreamCaptureStatusNone)
+    if (capturing)
       return fail(VL_EUNSUPPORTED,
                   "with the plan cache off a call uploads its work lists and cannot be captured");
     int dev = 0;
