@@ -169,6 +169,37 @@ VL_API int varlen_attn_bwd(const void* q, const void* k, const void* v,
                     void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * varlen_attn_bwd_noalloc - varlen_attn_bwd for callers that cannot allocate
+ * device memory (tight serving or training loops, harnesses that forbid
+ * allocation): the same arguments minus the workspace, the same kernels,
+ * split and results.  D, the dK/dV partials and the two work lists go into a
+ * 128 MiB device scratch array inside the library (one per device, held
+ * until the process ends; its address is looked up once per device, with the
+ * device current, on the first call there).  It allocates nothing: the work
+ * lists are built on the host and copied from pageable host memory with
+ * hipMemcpyAsync on `stream`, so a call on a capturing stream fails with
+ * VL_EUNSUPPORTED (a captured copy would read host memory the call has
+ * released).
+ *
+ * Limit: D [n_heads_q, total_q] fp32, plus the fp32 dK/dV partials of the
+ * q-head split when the batch is split (varlen_attn_bwd_workspace_size_cu
+ * gives both), plus the work lists, must fit the 128 MiB; a larger call
+ * returns VL_EWORKSPACE before any work is enqueued.
+ * Every call on one device shares that device's scratch, which keeps the last
+ * call's contents: calls that overlap on one device (other streams, other
+ * host threads) race and must be ordered by the caller.
+ * Errors: as varlen_attn_bwd; VL_EWORKSPACE when the scratch is too small;
+ * VL_EUNSUPPORTED on a capturing stream.
+ */
+VL_API int varlen_attn_bwd_noalloc(const void* q, const void* k, const void* v,
+                            const void* out, const void* dout, const float* lse,
+                            const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
+                            int32_t n_docs, int64_t total_q, int64_t total_k,
+                            int32_t n_heads_q, int32_t n_heads_kv, int32_t head_dim,
+                            float softmax_scale, int32_t causal,
+                            void* dq, void* dk, void* dv, void* stream);
+
+/*
  * attn_lse_merge - combine partial attention results computed over disjoint
  * key sets (the online combination of ring-style attention: HSAP page,
  * Section 2.2.1; its copy/rescale step, Section 3.1 Table 1; BASP page,

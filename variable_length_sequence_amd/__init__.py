@@ -35,7 +35,7 @@ STATUS = {0: "VL_OK", -1: "VL_EINVAL", -2: "VL_ESHAPE", -3: "VL_ESEQLENS",
           -4: "VL_EUNSUPPORTED", -5: "VL_EHIP", -6: "VL_EWORKSPACE"}
 
 EXPORTS = ["varlen_attn_fwd", "varlen_attn_bwd_workspace_size", "varlen_attn_bwd_workspace_size_cu",
-           "varlen_attn_bwd",
+           "varlen_attn_bwd", "varlen_attn_bwd_noalloc",
            "attn_lse_merge", "sp_seq2head", "sp_head2seq", "varlen_schedule_export",
            "varlen_last_error", "varlen_cache_clear", "varlen_set_plan_cache", "varlen_version",
            "varlen_profile_enable", "varlen_profile_read", "varlen_ring_block", "varlen_attn_fwd_acc", "sp_qkv_seq2head",
@@ -89,6 +89,9 @@ def lib():
     L.varlen_attn_bwd.argtypes = [vp, vp, vp, vp, vp, vp, pi32, pi32, i32, i64, i64, i32, i32, i32,
                                   f32, i32, vp, vp, vp, vp, ctypes.c_size_t, vp]
     L.varlen_attn_bwd.restype = ctypes.c_int
+    L.varlen_attn_bwd_noalloc.argtypes = [vp, vp, vp, vp, vp, vp, pi32, pi32, i32, i64, i64, i32,
+                                          i32, i32, f32, i32, vp, vp, vp, vp]
+    L.varlen_attn_bwd_noalloc.restype = ctypes.c_int
     L.attn_lse_merge.argtypes = [i32, ctypes.POINTER(vp), ctypes.POINTER(vp), i32, i64, i32, i32,
                                  vp, vp, i32, vp]
     L.attn_lse_merge.restype = ctypes.c_int

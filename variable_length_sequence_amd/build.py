@@ -19,7 +19,7 @@ BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libvarlen.so")
 
 SOURCES = ["scheduler.cpp", "router.cpp", "api.cpp", "profiler.cpp", "sp_permute.hip", "lse_merge.hip", "attn_fwd.hip",
-           "attn_bwd.hip", "mfma_probe.hip"]
+           "attn_bwd.hip", "mfma_probe.hip", "noalloc.hip"]
 
 ARCH = "gfx950"
 COMMON = ["-O3", "-fPIC", "-std=c++17", "-fvisibility=hidden", "-Wall", "-Wno-unused-function",

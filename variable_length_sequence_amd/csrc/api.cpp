@@ -524,6 +524,74 @@ int varlen_attn_bwd(const void* q, const void* k, const void* v, const void* out
   }
 }
 
+int varlen_attn_bwd_noalloc(const void* q, const void* k, const void* v, const void* out,
+                            const void* dout, const float* lse, const int32_t* cu_seqlens_q,
+                            const int32_t* cu_seqlens_k, int32_t n_docs, int64_t total_q,
+                            int64_t total_k, int32_t n_heads_q, int32_t n_heads_kv,
+                            int32_t head_dim, float softmax_scale, int32_t causal, void* dq,
+                            void* dk, void* dv, void* stream) {
+  try {
+    g_err.clear();
+    int rc = check_attn_common(q, k, v, cu_seqlens_q, cu_seqlens_k, n_docs, total_q, total_k,
+                               n_heads_q, n_heads_kv, head_dim);
+    if (rc) return rc;
+    if (!out || !dout || !lse || !dq || !dk || !dv)
+      return fail(VL_EINVAL, "out, dout, lse, dq, dk and dv must be non-null");
+    const uintptr_t al = reinterpret_cast<uintptr_t>(out) | reinterpret_cast<uintptr_t>(dout) |
+                         reinterpret_cast<uintptr_t>(dq) | reinterpret_cast<uintptr_t>(dk) |
+                         reinterpret_cast<uintptr_t>(dv);
+    if (al % 16) return fail(VL_EINVAL, "out, dout, dq, dk and dv must be 16-byte aligned");
+    // the same split and work lists as varlen_attn_bwd, laid out in the
+    // device scratch: D, the dK/dV partials, then the two work lists
+    const int split = choose_split(cu_seqlens_q, cu_seqlens_k, n_docs, causal, n_heads_q,
+                                   n_heads_kv, device_cus());
+    const size_t ws = bwd_workspace_bytes(total_q, total_k, n_heads_q, n_heads_kv, head_dim, split);
+    std::vector<vl::DevItem> host[2];
+    Plan pl[2];
+    for (int i = 0; i < 2; ++i)
+      build_list(i, causal != 0, cu_seqlens_q, cu_seqlens_k, n_docs, host[i], pl[i]);
+    const size_t off0 = ws;
+    const size_t off1 = off0 + align256(host[0].size() * sizeof(vl::DevItem));
+    const size_t need = off1 + align256(host[1].size() * sizeof(vl::DevItem));
+    if (need > vl::kNoallocScratchBytes)
+      return fail(VL_EWORKSPACE, "this call needs " + std::to_string(need) +
+                                     " bytes of device scratch; varlen_attn_bwd_noalloc has " +
+                                     std::to_string(vl::kNoallocScratchBytes) +
+                                     " (use varlen_attn_bwd with a workspace)");
+    if (total_q == 0 && total_k == 0) return VL_OK;
+    hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+    hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+    if (hipStreamIsCapturing(st, &cs) == hipSuccess && cs != hipStreamCaptureStatusNone)
+      return fail(VL_EUNSUPPORTED,
+                  "varlen_attn_bwd_noalloc copies its work lists from host memory and cannot be "
+                  "captured");
+    void* base = nullptr;
+    hipError_t e = vl::noalloc_scratch(&base);
+    if (e != hipSuccess) return hip_fail(e, "hipGetSymbolAddress(scratch)");
+    char* sc = reinterpret_cast<char*>(base);
+    for (int i = 0; i < 2; ++i) {
+      if (host[i].empty()) continue;
+      pl[i].dev = reinterpret_cast<vl::DevItem*>(sc + (i == 0 ? off0 : off1));
+      // the lists live in pageable host memory: the copy has read them when it returns
+      e = hipMemcpyAsync(pl[i].dev, host[i].data(), host[i].size() * sizeof(vl::DevItem),
+                         hipMemcpyHostToDevice, st);
+      if (e != hipSuccess) return hip_fail(e, "hipMemcpyAsync(work list)");
+    }
+    float* delta = reinterpret_cast<float*>(sc);
+    float* dkv_acc = reinterpret_cast<float*>(sc + align256(size_t(total_q) * size_t(n_heads_q) * 4));
+    vl::AttnShape s{total_q, total_k, n_heads_q, n_heads_kv, head_dim,
+                    resolve_scale(softmax_scale, head_dim), causal != 0};
+    e = vl::launch_attn_bwd(s, q, k, v, out, dout, lse, pl[0].map(), pl[1].map(), split, dq, dk,
+                            dv, delta, dkv_acc, st);
+    if (e != hipSuccess) return hip_fail(e, "attn_bwd launch");
+    return VL_OK;
+  } catch (const std::exception& ex) {
+    return fail(VL_EHIP, std::string("internal error: ") + ex.what());
+  } catch (...) {
+    return fail(VL_EHIP, "internal error");
+  }
+}
+
 int attn_lse_merge(int32_t n_parts, const void* const* o_parts, const float* const* lse_parts,
                    int32_t in_dtype, int64_t n_rows, int32_t n_heads, int32_t head_dim,
                    void* o_out, float* lse_out, int32_t out_dtype, void* stream) {

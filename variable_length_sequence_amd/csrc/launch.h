@@ -82,4 +82,10 @@ hipError_t launch_attn_bwd(const AttnShape& s, const void* q, const void* k, con
                            int32_t head_split, void* dq, void* dk, void* dv,
                            float* delta, float* dkv_acc, hipStream_t stream);
 
+// The device scratch of varlen_attn_bwd_noalloc (defined in noalloc.hip):
+// its size, and the address of the current device's copy (looked up once per
+// device).
+constexpr size_t kNoallocScratchBytes = size_t(128) << 20;
+hipError_t noalloc_scratch(void** ptr);
+
 }  // namespace vl
