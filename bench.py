@@ -550,7 +550,6 @@ def main():
         "step_ms_min": round(r["min_ms"], 4),
         "work_lists": "scheduled and uploaded by every call (plan cache off)",
         "ms_per_step_plan_cached": round(cached["ms"], 4),
-        "ms_per_step_profiled": round(rp["ms"], 4),
         "useful_tflop_per_step": round((r["flops_fwd"] + r["flops_bwd"]) / 1e12, 4),
         "roofline": {"bound": "mfma", "kernel": dom, "achieved": round(achieved, 2),
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",

@@ -141,7 +141,7 @@ constexpr int kKvThreads = 512;
 constexpr int kKvBufs = 3;      // steps in flight: t - 1 (dK role), t (dV role), t + 1 (loading)
 
 template <int D>
-struct KvSmem {
+struct KvSmemLoop {
   // Q and dO tiles, row-major with swizzled chunks; query row r is kept at
   // LDS row swap_bits23(r).  The transposed operands (dO for dV += P^T dO, Q
   // for dK += dS^T Q) are read from the same tiles with the transpose read.
@@ -152,6 +152,15 @@ struct KvSmem {
   // P of the last two steps, bf16, in the A-operand layout of each dV wave:
   // [step parity][key block][operand half][lane][8]
   alignas(16) uint16_t p[2][4][2][64 * 8];
+};
+
+// After the step loop the same LDS holds each wave's 32 x D block of dK or dV
+// (fp32 for a split partial, else bf16), row-major with 16-byte chunks
+// XOR-swizzled by row, so the block leaves in full rows of 16-byte stores.
+template <int D>
+union KvSmem {
+  KvSmemLoop<D> loop;
+  alignas(16) uint32_t stage[8][32 * D];   // [wave][32 rows x D fp32 (or 2 D bf16)]
 };
 
 // 8 waves per workgroup, 128 keys of one document and one kv head; waves
@@ -281,15 +290,15 @@ attn_bwd_dkdv_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
   };
   auto store_rows = [&](float x, int buf) {
     if (wave < 2 && lane < KB_Q) {
-      if (wave == 0) sm.lse2[buf][lane] = x * kLog2e;
-      else sm.delta[buf][lane] = x * scale;
+      if (wave == 0) sm.loop.lse2[buf][lane] = x * kLog2e;
+      else sm.loop.delta[buf][lane] = x * scale;
     }
   };
 
   int nxt_i0 = i_last, nxt_h = h_begin;        // step t + 1
   int cur_i0 = i_last;                         // step t (dV role)
   if (n_steps > 0) {
-    issue(nxt_i0, nxt_h, lds_addr(sm.q[0]), lds_addr(sm.dout[0]));
+    issue(nxt_i0, nxt_h, lds_addr(sm.loop.q[0]), lds_addr(sm.loop.dout[0]));
     store_rows(fetch_rows(nxt_i0, nxt_h), 0);
     advance(nxt_i0, nxt_h);
   }
@@ -302,16 +311,16 @@ attn_bwd_dkdv_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
     __syncthreads();
     float rows = 0.f;
     if (t + 1 < n_steps) {
-      issue(nxt_i0, nxt_h, lds_addr(sm.q[0]) + uint32_t(nxt) * (KB_Q * D * 2),
-            lds_addr(sm.dout[0]) + uint32_t(nxt) * (KB_Q * D * 2));
+      issue(nxt_i0, nxt_h, lds_addr(sm.loop.q[0]) + uint32_t(nxt) * (KB_Q * D * 2),
+            lds_addr(sm.loop.dout[0]) + uint32_t(nxt) * (KB_Q * D * 2));
       rows = fetch_rows(nxt_i0, nxt_h);
     }
     const int st = t - role;                   // this wave's step
     if (st >= 0 && st < n_steps) {
       const int sb = role == 0 ? cur : prv;    // its buffer
-      const uint16_t* tile1 = role == 0 ? sm.q[sb] : sm.dout[sb];
-      const uint16_t* tile2 = role == 0 ? sm.dout[sb] : sm.q[sb];
-      const float* rowv = role == 0 ? sm.lse2[sb] : sm.delta[sb];
+      const uint16_t* tile1 = role == 0 ? sm.loop.q[sb] : sm.loop.dout[sb];
+      const uint16_t* tile2 = role == 0 ? sm.loop.dout[sb] : sm.loop.q[sb];
+      const float* rowv = role == 0 ? sm.loop.lse2[sb] : sm.loop.delta[sb];
       // this lane's 16 queries 16s + 8 half + u: LSE log2(e) or D scale
       f32x4 rr[4];
 #pragma unroll
@@ -320,7 +329,7 @@ attn_bwd_dkdv_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
       // dK role: P of step t - 1 from the dV wave
       u32x4 pr[2];
       if (role == 1) {
-        const uint16_t* pp = &sm.p[(t - 1) & 1][w][0][lane * 8];
+        const uint16_t* pp = &sm.loop.p[(t - 1) & 1][w][0][lane * 8];
         pr[0] = *reinterpret_cast<const u32x4*>(pp);
         pr[1] = *reinterpret_cast<const u32x4*>(pp + 64 * 8);
       }
@@ -343,7 +352,7 @@ attn_bwd_dkdv_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
       // element i holds query i0 + 8 half + e, e = 16 (i / 8) + i % 8
       u32x4 au[2];
       if (role == 0) {
-        uint16_t* pp = &sm.p[t & 1][w][0][lane * 8];
+        uint16_t* pp = &sm.loop.p[t & 1][w][0][lane * 8];
 #pragma unroll
         for (int s2 = 0; s2 < 2; ++s2)
 #pragma unroll
@@ -390,10 +399,12 @@ attn_bwd_dkdv_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
           }
         }
       }
-      // dV += P^T dO or dK += dS^T Q
+        // dV^T += dO^T P or dK^T += Q^T dS: the transposed products, so a lane
+      // holds 4 consecutive head dims of its key (the operands are the same
+      // registers: a B fragment read as an A fragment is its transpose)
 #pragma unroll
       for (int f = 0; f < 2 * NCB; ++f)
-        acc[f >> 1] = mfma32(as_bf16x8(au[f & 1]), tb[f], acc[f >> 1]);
+        acc[f >> 1] = mfma32(tb[f], as_bf16x8(au[f & 1]), acc[f >> 1]);
     }
     if (t + 1 < n_steps) store_rows(rows, nxt);
     cur_i0 = nxt_i0;
@@ -401,21 +412,57 @@ attn_bwd_dkdv_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
     cur = nxt;
   }
 
-  // epilogue: lane holds column c = 32 cb + l32 of keys 32 w + 8 (v/4) + 4 half + v%4
-  uint16_t* outp = role == 0 ? dv : dk;
-  float* accp = dkv_acc + (int64_t(split) * 2 + (role == 0 ? 1 : 0)) * total_k * kv_tok;
+  // epilogue: lane holds key kw0 + l32, head dims 32 cb + 8 j + 4 half + 0..3
+  // in acc[cb][4 j .. 4 j + 3].  Each wave stages its 32 x D block in LDS
+  // (the step buffers are free once every wave is past the loop) and writes
+  // it out as whole rows of 16-byte chunks.
+  __syncthreads();
+  uint32_t* stg = sm.stage[wave];
+  const int64_t row0 = (int64_t(it.k_start) + kw0) * kv_tok + int64_t(g) * D;   // key kw0
+  if (head_split == 1) {
+    // bf16: a row is D / 8 chunks; chunk c of row r sits at chunk
+    // c ^ (r % (D / 8))
+    constexpr int RCH = D / 8;
 #pragma unroll
-  for (int cb = 0; cb < NCB; ++cb) {
+    for (int cb = 0; cb < NCB; ++cb)
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int kk = kw0 + 8 * (i >> 2) + 4 * half + (i & 3);
-      if (kk < lk) {
-        const int64_t idx = (int64_t(it.k_start) + kk) * kv_tok + int64_t(g) * D + cb * 32 + l32;
-        if (head_split == 1)
-          outp[idx] = __builtin_bit_cast(uint16_t, (__bf16)acc[cb][i]);
-        else
-          accp[idx] = acc[cb][i];
+      for (int j = 0; j < 4; ++j) {
+        const int c = 4 * cb + j;
+        const u32x2 v2{pack_bf16x2(acc[cb][4 * j], acc[cb][4 * j + 1]),
+                       pack_bf16x2(acc[cb][4 * j + 2], acc[cb][4 * j + 3])};
+        *reinterpret_cast<u32x2*>(&stg[l32 * (D / 2) + ((c ^ (l32 & (RCH - 1))) << 2) + 2 * half]) = v2;
       }
+    uint16_t* outp = role == 0 ? dv : dk;
+    constexpr int RPI = 64 / RCH;              // rows per read
+#pragma unroll
+    for (int t = 0; t < 32 / RPI; ++t) {
+      const int r = t * RPI + lane / RCH, c = lane % RCH;
+      const u32x4 x = *reinterpret_cast<const u32x4*>(&stg[r * (D / 2) + ((c ^ (r & (RCH - 1))) << 2)]);
+      if (kw0 + r < lk)
+        *reinterpret_cast<u32x4*>(outp + row0 + int64_t(r) * kv_tok + 8 * c) = x;
+    }
+  } else {
+    // fp32 partial: a row is D / 4 chunks; chunk c of row r sits at chunk
+    // c ^ (r % (D / 4))
+    constexpr int RCH = D / 4;
+#pragma unroll
+    for (int cb = 0; cb < NCB; ++cb)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int c = 8 * cb + 2 * j + half;
+        f32x4 v4;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v4[e] = acc[cb][4 * j + e];
+        *reinterpret_cast<f32x4*>(&stg[l32 * D + ((c ^ (l32 & (RCH - 1))) << 2)]) = v4;
+      }
+    float* accp = dkv_acc + (int64_t(split) * 2 + (role == 0 ? 1 : 0)) * total_k * kv_tok;
+    constexpr int RPI = 64 / RCH;
+#pragma unroll
+    for (int t = 0; t < 32 / RPI; ++t) {
+      const int r = t * RPI + lane / RCH, c = lane % RCH;
+      const f32x4 x = *reinterpret_cast<const f32x4*>(&stg[r * D + ((c ^ (r & (RCH - 1))) << 2)]);
+      if (kw0 + r < lk)
+        *reinterpret_cast<f32x4*>(accp + row0 + int64_t(r) * kv_tok + 4 * c) = x;
     }
   }
 }
