@@ -189,9 +189,12 @@ attn_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
       }
       return grow;
     };
+    // A lane that has seen no visible key yet holds O = 0 and l = 0, so its
+    // first reference max needs no rescale (the first tile of every item).
     auto commit_half = [&](bool grow) {
-      if (__ballot(grow)) {
-        const float alpha = grow ? __builtin_amdgcn_exp2f((m_run - m_use) * c) : 1.f;
+      const bool scale_acc = grow && m_run != -INFINITY;
+      if (__ballot(scale_acc)) {
+        const float alpha = scale_acc ? __builtin_amdgcn_exp2f((m_run - m_use) * c) : 1.f;
         l_run *= alpha;
 #pragma unroll
         for (int cb = 0; cb < NCB; ++cb)
