@@ -399,7 +399,7 @@ attn_bwd_dkdv_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
           }
         }
       }
-        // dV^T += dO^T P or dK^T += Q^T dS: the transposed products, so a lane
+      // dV^T += dO^T P or dK^T += Q^T dS: the transposed products, so a lane
       // holds 4 consecutive head dims of its key (the operands are the same
       // registers: a B fragment read as an A fragment is its transpose)
 #pragma unroll
