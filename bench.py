@@ -600,7 +600,13 @@ def main():
             sub = workloads.Workload(f"{mw.name}_{name}", [mw.lengths[i] for i in idx], hq=mw.hq,
                                      hkv=mw.hkv, d=mw.d)
             t = [x[rows].contiguous() for x in (q, k, v, do)]
-            rr = bench_attention(vl, torch, sub, 3, 1, dev, tensors=t, profile=False)
+            # short buckets get the headline's 5 warmup + 20 timed steps (a
+            # step of the < 2K bucket is about a millisecond, and the first
+            # steps after the long runs above are slower); the > 16K bucket
+            # (about 0.2 s a step) keeps 1 + 3
+            short = sub.total <= 32768
+            rr = bench_attention(vl, torch, sub, 20 if short else 3, 5 if short else 1, dev,
+                                 tensors=t, profile=False)
             buckets[name] = {"docs": len(idx), "tokens": sub.total, "ms_per_step": round(rr["ms"], 3),
                              "tflops": round(rr["tflops"], 2),
                              "useful_tflop": round((rr["flops_fwd"] + rr["flops_bwd"]) / 1e12, 3)}
