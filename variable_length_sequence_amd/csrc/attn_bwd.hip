@@ -17,7 +17,9 @@
 //      of the A operand are permuted so P and dS come out of the MFMA already
 //      in the A-operand layout of dV += P^T dO and dK += dS^T Q.
 //   3. dq: the forward's mapping (a lane owns one query): S^T = K Q^T and
-//      dP^T = V dO^T per 64-key tile, then dQ^T += K^T dS^T.
+//      dP^T = V dO^T per 64-key tile, then dQ^T += K^T dS^T; like the
+//      forward, the Q tile arrives in LDS by direct loads and dQ leaves
+//      through LDS in whole rows.
 //   With the q heads of a group split over workgroups, each split stores its
 //   fp32 dK/dV partial and a fourth kernel adds the partials in split order
 //   (plain stores run at several times the rate of fp32 atomic adds, and the
@@ -513,19 +515,18 @@ attn_bwd_dq_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ 
   const int64_t kv_tok = int64_t(hkv) * D;
   const float c = scale * kLog2e;
 
+  // the Q tile by direct loads into LDS buffer 1 (read back below), the dO
+  // fragments (B operand of dP^T = V dO^T) into registers
+  load_rows128_lds<D>(q + (int64_t(it.q_start) + q0) * q_tok + int64_t(h) * D,
+                      uint32_t(q_tok * 2), lq - q0, lds_addr(sm.k[1]), lds_addr(sm.v[1]), w, lane);
   bf16x8 qf[NKS], df[NKS];
   {
     const int64_t row = int64_t(it.q_start) + qrow;
-    const uint16_t* qp = q + row * q_tok + int64_t(h) * D + 8 * half;
     const uint16_t* dp = dout + row * q_tok + int64_t(h) * D + 8 * half;
 #pragma unroll
     for (int s = 0; s < NKS; ++s) {
-      u32x4 a = u32x4{0, 0, 0, 0}, bb = u32x4{0, 0, 0, 0};
-      if (qrow < lq) {
-        a = *reinterpret_cast<const u32x4*>(qp + 16 * s);
-        bb = *reinterpret_cast<const u32x4*>(dp + 16 * s);
-      }
-      qf[s] = as_bf16x8(a);
+      u32x4 bb = u32x4{0, 0, 0, 0};
+      if (qrow < lq) bb = *reinterpret_cast<const u32x4*>(dp + 16 * s);
       df[s] = as_bf16x8(bb);
     }
   }
@@ -616,6 +617,16 @@ attn_bwd_dq_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ 
   const int n_kv = it.count;
   if (n_kv > 0)
     loader.load(kbase, vbase, kv_tok, 0, lk, lds_addr(sm.k[0]), lds_addr(sm.v[0]), w, lane);
+  // Q fragments (B operand of S^T = K Q^T): query l32, dims 16s + 8 half .. +8
+  __builtin_amdgcn_s_waitcnt(kWaitAll);
+  __syncthreads();
+  {
+    const int row = w * 32 + l32;
+    const uint16_t* qs = row < 64 ? sm.k[1] : sm.v[1];
+#pragma unroll
+    for (int s = 0; s < NKS; ++s)
+      qf[s] = as_bf16x8(*reinterpret_cast<const u32x4*>(&qs[SwzTile<D>::chunk(row & 63, 2 * s + half)]));
+  }
   int kt = 0;
   for (; kt + 1 < n_kv; kt += 2) {
     tile(kt, IC<0>{});
@@ -623,18 +634,29 @@ attn_bwd_dq_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ 
   }
   if (kt < n_kv) tile(kt, IC<0>{});
 
-  if (qrow < lq) {
-    const int64_t orow = (int64_t(it.q_start) + qrow) * q_tok + int64_t(h) * D;
+  // each wave stages its 32 x D block of dQ in LDS (the K/V buffers are free
+  // once every wave is past its last tile) and writes whole rows of 16-byte
+  // chunks; chunk c of row r sits at chunk c ^ (r % (D / 8))
+  __syncthreads();
+  uint32_t* stg = reinterpret_cast<uint32_t*>(&sm.k[0][0]) + w * (32 * D / 2);
+  constexpr int RCH = D / 8;
 #pragma unroll
-    for (int cb = 0; cb < NCB; ++cb)
+  for (int cb = 0; cb < NCB; ++cb)
 #pragma unroll
-      for (int gq = 0; gq < 4; ++gq) {
-        const int cc = cb * 32 + 8 * gq + 4 * half;
-        u32x2 o2;
-        o2[0] = pack_bf16x2(acc[cb][4 * gq], acc[cb][4 * gq + 1]);
-        o2[1] = pack_bf16x2(acc[cb][4 * gq + 2], acc[cb][4 * gq + 3]);
-        *reinterpret_cast<u32x2*>(dq + orow + cc) = o2;
-      }
+    for (int gq = 0; gq < 4; ++gq) {
+      const int cc = 4 * cb + gq;
+      const u32x2 o2{pack_bf16x2(acc[cb][4 * gq], acc[cb][4 * gq + 1]),
+                     pack_bf16x2(acc[cb][4 * gq + 2], acc[cb][4 * gq + 3])};
+      *reinterpret_cast<u32x2*>(&stg[l32 * (D / 2) + ((cc ^ (l32 & (RCH - 1))) << 2) + 2 * half]) = o2;
+    }
+  constexpr int RPI = 64 / RCH;
+  const int64_t orow0 = (int64_t(it.q_start) + q0 + w * 32) * q_tok + int64_t(h) * D;
+#pragma unroll
+  for (int t = 0; t < 32 / RPI; ++t) {
+    const int r = t * RPI + lane / RCH, cc = lane % RCH;
+    const u32x4 x = *reinterpret_cast<const u32x4*>(&stg[r * (D / 2) + ((cc ^ (r & (RCH - 1))) << 2)]);
+    if (q0 + w * 32 + r < lq)
+      *reinterpret_cast<u32x4*>(dq + orow0 + int64_t(r) * q_tok + 8 * cc) = x;
   }
 }
 

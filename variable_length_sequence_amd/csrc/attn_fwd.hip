@@ -23,6 +23,11 @@
 //     double-buffered and filled by direct global->LDS loads issued one tile
 //     ahead (one barrier per tile, no staging registers); the tile loop is
 //     unrolled by two so both buffers have fixed addresses;
+//   * the Q tile also arrives by direct loads (whole rows, into the buffer
+//     the second key tile will use) and each wave reads its Q fragments from
+//     LDS; the epilogue stages each wave's 32 x D block of O in LDS and writes
+//     whole rows of 16-byte chunks (both replace scattered 16- and 8-byte
+//     accesses of 32 rows per instruction);
 //   * work items are ordered longest first and the workgroup id is remapped
 //     so all q heads of one item run on the same XCD (shared K/V in its L2).
 #include <hip/hip_runtime.h>
@@ -86,18 +91,13 @@ attn_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
   const int64_t kv_tok = int64_t(hkv) * D;
   const float c = scale * kLog2e;
 
-  // Q fragment (B operand of S^T = K Q^T): query l32, dims 16s + 8 half .. +8
-  bf16x8 qf[NKS];
-  {
-    const uint16_t* qp = q + (int64_t(it.q_start) + qrow) * q_tok + int64_t(h) * D + 8 * half;
-#pragma unroll
-    for (int s = 0; s < NKS; ++s) {
-      u32x4 u = u32x4{0, 0, 0, 0};
-      if (qrow < lq) u = *reinterpret_cast<const u32x4*>(qp + 16 * s);
-      qf[s] = as_bf16x8(u);
-    }
-  }
+  // The Q tile arrives by direct loads into LDS buffer 1 (free until the
+  // prefetch of key tile 1): rows 0-63 in its K half, rows 64-127 in its V
+  // half; rows past the document repeat its last row.
+  load_rows128_lds<D>(q + (int64_t(it.q_start) + q0) * q_tok + int64_t(h) * D,
+                      uint32_t(q_tok * 2), lq - q0, lds_addr(sm.k[1]), lds_addr(sm.v[1]), w, lane);
 
+  bf16x8 qf[NKS];
   f32x16 acc[NCB];
 #pragma unroll
   for (int cb = 0; cb < NCB; ++cb)
@@ -276,6 +276,16 @@ attn_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
   const int n_kv = it.count;
   if (n_kv > 0)
     loader.load(kbase, vbase, kv_tok, 0, lk, lds_addr(sm.k[0]), lds_addr(sm.v[0]), w, lane);
+  // Q fragments (B operand of S^T = K Q^T): query l32, dims 16s + 8 half .. +8
+  __builtin_amdgcn_s_waitcnt(kWaitAll);
+  __syncthreads();
+  {
+    const int row = w * 32 + l32;
+    const uint16_t* qs = row < 64 ? sm.k[1] : sm.v[1];
+#pragma unroll
+    for (int s = 0; s < NKS; ++s)
+      qf[s] = as_bf16x8(*reinterpret_cast<const u32x4*>(&qs[SwzTile<D>::chunk(row & 63, 2 * s + half)]));
+  }
   int kt = 0;
   for (; kt + 1 < n_kv; kt += 2) {
     tile(kt, IC<0>{});
@@ -286,7 +296,37 @@ attn_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
   // epilogue: O = acc / l, LSE = m scale + ln l
   const float l_tot = halves_sum(l_run);
   const float inv = (l_tot > 0.f) ? 1.f / l_tot : 0.f;
-  if (qrow < lq) {
+  if constexpr (OUT == kOutBf16) {
+    // each wave stages its 32 x D block of O in LDS (the K/V buffers are free
+    // once every wave is past its last tile) and writes whole rows of 16-byte
+    // chunks; chunk c of row r sits at chunk c ^ (r % (D / 8))
+    __syncthreads();
+    uint32_t* stg = reinterpret_cast<uint32_t*>(&sm.k[0][0]) + w * (32 * D / 2);
+    constexpr int RCH = D / 8;
+#pragma unroll
+    for (int cb = 0; cb < NCB; ++cb)
+#pragma unroll
+      for (int gq = 0; gq < 4; ++gq) {
+        const int cc = 4 * cb + gq;
+        const u32x2 o2{pack_bf16x2(acc[cb][4 * gq] * inv, acc[cb][4 * gq + 1] * inv),
+                       pack_bf16x2(acc[cb][4 * gq + 2] * inv, acc[cb][4 * gq + 3] * inv)};
+        *reinterpret_cast<u32x2*>(&stg[l32 * (D / 2) + ((cc ^ (l32 & (RCH - 1))) << 2) + 2 * half]) = o2;
+      }
+    constexpr int RPI = 64 / RCH;
+    const int64_t orow0 = (int64_t(it.q_start) + q0 + w * 32) * q_tok + int64_t(h) * D;
+    uint16_t* outp = reinterpret_cast<uint16_t*>(out);
+#pragma unroll
+    for (int t = 0; t < 32 / RPI; ++t) {
+      const int r = t * RPI + lane / RCH, cc = lane % RCH;
+      const u32x4 x = *reinterpret_cast<const u32x4*>(&stg[r * (D / 2) + ((cc ^ (r & (RCH - 1))) << 2)]);
+      if (q0 + w * 32 + r < lq)
+        *reinterpret_cast<u32x4*>(outp + orow0 + int64_t(r) * q_tok + 8 * cc) = x;
+    }
+    if (qrow < lq && half == 0) {
+      const int64_t lrow = int64_t(h) * total_q + it.q_start + qrow;
+      lse[lrow] = (l_tot > 0.f) ? (m_run * scale + __logf(l_tot)) : -INFINITY;
+    }
+  } else if (qrow < lq) {
     const int64_t orow = (int64_t(it.q_start) + qrow) * q_tok + int64_t(h) * D;
     const int64_t lrow = int64_t(h) * total_q + it.q_start + qrow;
     const float lv = (l_tot > 0.f) ? (m_run * scale + __logf(l_tot)) : -INFINITY;

@@ -193,6 +193,29 @@ struct PairLoader {
   }
 };
 
+// Direct loads of a 128-row x D bf16 tile (rows of one [T, H, D] tensor,
+// base = its first row) into two 64-row SwzTile halves at LDS byte addresses
+// lo (rows 0-63) and hi (rows 64-127), spread over 4 waves: lane i of 1 KB
+// block j fills local row j * RPL + i / NCH.  Rows at or past n_valid (>= 1)
+// repeat row n_valid - 1.
+template <int D>
+__device__ __forceinline__ void load_rows128_lds(const uint16_t* base, uint32_t row_bytes,
+                                                 int n_valid, uint32_t lo, uint32_t hi, int wave,
+                                                 int lane) {
+  constexpr int NCH = D / 8;            // 16-byte chunks per row
+  constexpr int RPL = 64 / NCH;         // rows per 1 KB block
+  constexpr int NBLK = 128 / RPL;       // blocks of the tile
+#pragma unroll
+  for (int u = 0; u < NBLK / 4; ++u) {
+    const int j = u * 4 + wave;
+    const int row = j * RPL + lane / NCH;
+    const int p = row & 63;
+    const uint32_t pc = uint32_t((lane % NCH) ^ SwzTile<D>::swz(p));
+    const uint32_t off = uint32_t(min(row, n_valid - 1)) * row_bytes + (pc << 4);
+    load_lds16(base, off, (row < 64 ? lo : hi) + uint32_t((j % (64 / RPL)) * 1024));
+  }
+}
+
 // s_waitcnt immediates (gfx9 encoding: vmcnt in bits 3:0 and 15:14, expcnt
 // in 6:4, lgkmcnt in 11:8)
 constexpr int kWaitAll = 0;           // every counter at zero
