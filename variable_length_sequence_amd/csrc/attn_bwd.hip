@@ -17,9 +17,9 @@
 //      of the A operand are permuted so P and dS come out of the MFMA already
 //      in the A-operand layout of dV += P^T dO and dK += dS^T Q.
 //   3. dq: the forward's mapping (a lane owns one query): S^T = K Q^T and
-//      dP^T = V dO^T per 64-key tile, then dQ^T += K^T dS^T; like the
-//      forward, the Q tile arrives in LDS by direct loads and dQ leaves
-//      through LDS in whole rows.
+//      dP^T = V dO^T per 64-key tile, then dQ^T += K^T dS^T; the Q and dO
+//      tiles arrive in LDS by direct loads and dQ leaves through LDS, all in
+//      whole rows.
 //   With the q heads of a group split over workgroups, each split stores its
 //   fp32 dK/dV partial and a fourth kernel adds the partials in split order
 //   (plain stores run at several times the rate of fp32 atomic adds, and the
@@ -515,21 +515,15 @@ attn_bwd_dq_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ 
   const int64_t kv_tok = int64_t(hkv) * D;
   const float c = scale * kLog2e;
 
-  // the Q tile by direct loads into LDS buffer 1 (read back below), the dO
-  // fragments (B operand of dP^T = V dO^T) into registers
+  // The Q and dO tiles arrive by direct loads in whole rows (Q into buffer 1,
+  // dO into buffer 0; rows past the document repeat its last row, whose P is
+  // zero) and are read back as fragments below; the first K/V tile follows
+  // once buffer 0 is free again.
   load_rows128_lds<D>(q + (int64_t(it.q_start) + q0) * q_tok + int64_t(h) * D,
                       uint32_t(q_tok * 2), lq - q0, lds_addr(sm.k[1]), lds_addr(sm.v[1]), w, lane);
+  load_rows128_lds<D>(dout + (int64_t(it.q_start) + q0) * q_tok + int64_t(h) * D,
+                      uint32_t(q_tok * 2), lq - q0, lds_addr(sm.k[0]), lds_addr(sm.v[0]), w, lane);
   bf16x8 qf[NKS], df[NKS];
-  {
-    const int64_t row = int64_t(it.q_start) + qrow;
-    const uint16_t* dp = dout + row * q_tok + int64_t(h) * D + 8 * half;
-#pragma unroll
-    for (int s = 0; s < NKS; ++s) {
-      u32x4 bb = u32x4{0, 0, 0, 0};
-      if (qrow < lq) bb = *reinterpret_cast<const u32x4*>(dp + 16 * s);
-      df[s] = as_bf16x8(bb);
-    }
-  }
   float lse2 = INFINITY, dl = 0.f;
   if (qrow < lq) {
     const float l = lse[int64_t(h) * total_q + it.q_start + qrow];
@@ -615,18 +609,24 @@ attn_bwd_dq_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ 
   };
 
   const int n_kv = it.count;
-  if (n_kv > 0)
-    loader.load(kbase, vbase, kv_tok, 0, lk, lds_addr(sm.k[0]), lds_addr(sm.v[0]), w, lane);
-  // Q fragments (B operand of S^T = K Q^T): query l32, dims 16s + 8 half .. +8
+  // Q and dO fragments (B operands of S^T = K Q^T and dP^T = V dO^T): query
+  // l32, dims 16s + 8 half .. +8
   __builtin_amdgcn_s_waitcnt(kWaitAll);
   __syncthreads();
   {
     const int row = w * 32 + l32;
     const uint16_t* qs = row < 64 ? sm.k[1] : sm.v[1];
+    const uint16_t* ds = row < 64 ? sm.k[0] : sm.v[0];
 #pragma unroll
-    for (int s = 0; s < NKS; ++s)
+    for (int s = 0; s < NKS; ++s) {
       qf[s] = as_bf16x8(*reinterpret_cast<const u32x4*>(&qs[SwzTile<D>::chunk(row & 63, 2 * s + half)]));
+      df[s] = as_bf16x8(*reinterpret_cast<const u32x4*>(&ds[SwzTile<D>::chunk(row & 63, 2 * s + half)]));
+    }
   }
+  __builtin_amdgcn_s_waitcnt(kWaitAll);
+  __syncthreads();
+  if (n_kv > 0)
+    loader.load(kbase, vbase, kv_tok, 0, lk, lds_addr(sm.k[0]), lds_addr(sm.v[0]), w, lane);
   int kt = 0;
   for (; kt + 1 < n_kv; kt += 2) {
     tile(kt, IC<0>{});
