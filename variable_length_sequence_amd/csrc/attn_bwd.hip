@@ -634,11 +634,13 @@ attn_bwd_dq_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ 
   }
   if (kt < n_kv) tile(kt, IC<0>{});
 
-  // each wave stages its 32 x D block of dQ in LDS (the K/V buffers are free
-  // once every wave is past its last tile) and writes whole rows of 16-byte
-  // chunks; chunk c of row r sits at chunk c ^ (r % (D / 8))
-  __syncthreads();
-  uint32_t* stg = reinterpret_cast<uint32_t*>(&sm.k[0][0]) + w * (32 * D / 2);
+  // each wave stages its 32 x D block of dQ in LDS and writes whole rows of
+  // 16-byte chunks (chunk c of row r sits at chunk c ^ (r % (D / 8))), in the
+  // K/V buffer the last key tile did not use (free since that tile's barrier;
+  // no load went into it), so no wave waits for the others here
+  const int fb = n_kv & 1;
+  uint32_t* stg = reinterpret_cast<uint32_t*>(w < 2 ? &sm.k[fb][0] : &sm.v[fb][0]) +
+                  (w & 1) * (32 * D / 2);
   constexpr int RCH = D / 8;
 #pragma unroll
   for (int cb = 0; cb < NCB; ++cb)
