@@ -580,9 +580,15 @@ attn_bwd_dq_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ 
             if (f & 1) da = mfma32(a, df[st], st == 0 ? f32x16{} : da);
             else sa = mfma32(a, qf[st], st == 0 ? f32x16{} : sa);
           });
-      // key kv0 + 32 kb + 8 half + e (e = 16 hs + 2 j + e2) is visible iff
-      // e <= thr
-      const int thr = need_mask ? lim - kv0 - 32 * kb - 8 * half : 64;
+      // on tiles crossing the diagonal or the document's end: key kv0 + 32 kb
+      // + 8 half + e (e = 16 (i / 8) + i % 8) is visible iff e <= thr; a
+      // hidden score becomes -inf, so its P is exactly zero
+      if (need_mask) {
+        const int thr = lim - kv0 - 32 * kb - 8 * half;
+#pragma unroll
+        for (int i = 0; i < 16; ++i)
+          if (16 * (i >> 3) + (i & 7) > thr) sa[i] = -INFINITY;
+      }
 #pragma unroll
       for (int hs = 0; hs < 2; ++hs) {
         u32x4 u;
@@ -592,14 +598,16 @@ attn_bwd_dq_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ 
 #pragma unroll
           for (int e = 0; e < 2; ++e) {
             const int i = 8 * hs + 2 * j + e;
-            float pv_ = __builtin_amdgcn_exp2f(fmaf(sa[i], c, -lse2));
-            if (need_mask && 16 * hs + 2 * j + e > thr) pv_ = 0.f;
-            dsv[e] = pv_ * fmaf(da[i], scale, -dls);
+            dsv[e] = __builtin_amdgcn_exp2f(fmaf(sa[i], c, -lse2)) * fmaf(da[i], scale, -dls);
           }
           u[j] = pack_bf16x2(dsv[0], dsv[1]);
         }
         dsf[kb][hs] = as_bf16x8(u);
       }
+      // dS of this half is complete before the next half's chains start (the
+      // mask branch would otherwise let the compiler sink it below them and
+      // keep both halves' accumulators live)
+      asm volatile("" ::"v"(as_u32x4(dsf[kb][0])), "v"(as_u32x4(dsf[kb][1])));
     }
 
     // dQ^T += K^T dS^T; fragment f = (cb, kb, hs), read transposed, two ahead
