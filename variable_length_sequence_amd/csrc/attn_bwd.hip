@@ -151,9 +151,9 @@ struct KvSmemLoop {
   uint16_t dout[kKvBufs][KB_Q * D];
   alignas(16) float lse2[kKvBufs][KB_Q];   // LSE log2(e)
   alignas(16) float delta[kKvBufs][KB_Q];  // D scale
-  // P of the last two steps, bf16, in the A-operand layout of each dV wave:
-  // [step parity][key block][operand half][lane][8]
-  alignas(16) uint16_t p[2][4][2][64 * 8];
+  // P of recent steps, bf16, in the A-operand layout of each dV wave:
+  // [step buffer][key block][operand half][lane][8]
+  alignas(16) uint16_t p[kKvBufs][4][2][64 * 8];
 };
 
 // After the step loop the same LDS holds each wave's 32 x D block of dK or dV
@@ -172,8 +172,8 @@ union KvSmem {
 //  * waves 4-7 (dK role) take step t - 1: dP = dO V^T, P from LDS,
 //    dS = P (dP - D) scale, dK += dS^T Q.
 // Both roles run the same two MFMA chains on role-dependent LDS tiles (only
-// the elementwise middle differs), so the accumulators have one home; the
-// two waves of a SIMD work on different steps and overlap freely.
+// the elementwise middle differs); the two waves of a SIMD work on different
+// steps and overlap freely.
 template <int D>
 __global__ void __launch_bounds__(kKvThreads)
 attn_bwd_dkdv_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
@@ -304,10 +304,16 @@ attn_bwd_dkdv_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
     store_rows(fetch_rows(nxt_i0, nxt_h), 0);
     advance(nxt_i0, nxt_h);
   }
-  int cur = 0;                                 // buffer of step t
-  for (int t = 0; t <= n_steps; ++t) {
-    const int nxt = cur == kKvBufs - 1 ? 0 : cur + 1;
-    const int prv = cur == 0 ? kKvBufs - 1 : cur - 1;
+  // One loop iteration t.  The loop is unrolled by three and compiled once
+  // per role, so the step buffer (t % 3) and the role are compile-time
+  // constants and every LDS address is a loop-invariant register plus an
+  // immediate offset (a runtime buffer index and role select cost about a
+  // fifth of the vector instructions of a step).
+  auto iteration = [&](int t, auto cc, auto rc) {
+    constexpr int cur = decltype(cc)::value;
+    constexpr int role = decltype(rc)::value;   // this wave's role
+    constexpr int nxt = (cur + 1) % kKvBufs;
+    constexpr int prv = (cur + kKvBufs - 1) % kKvBufs;
     // step t has landed; nobody reads buffer nxt any more (step t - 2)
     __builtin_amdgcn_s_waitcnt(kWaitAll);
     __syncthreads();
@@ -331,7 +337,7 @@ attn_bwd_dkdv_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
       // dK role: P of step t - 1 from the dV wave
       u32x4 pr[2];
       if (role == 1) {
-        const uint16_t* pp = &sm.loop.p[(t - 1) & 1][w][0][lane * 8];
+        const uint16_t* pp = &sm.loop.p[prv][w][0][lane * 8];
         pr[0] = *reinterpret_cast<const u32x4*>(pp);
         pr[1] = *reinterpret_cast<const u32x4*>(pp + 64 * 8);
       }
@@ -354,7 +360,7 @@ attn_bwd_dkdv_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
       // element i holds query i0 + 8 half + e, e = 16 (i / 8) + i % 8
       u32x4 au[2];
       if (role == 0) {
-        uint16_t* pp = &sm.loop.p[t & 1][w][0][lane * 8];
+        uint16_t* pp = &sm.loop.p[cur][w][0][lane * 8];
 #pragma unroll
         for (int s2 = 0; s2 < 2; ++s2)
 #pragma unroll
@@ -411,8 +417,19 @@ attn_bwd_dkdv_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
     if (t + 1 < n_steps) store_rows(rows, nxt);
     cur_i0 = nxt_i0;
     advance(nxt_i0, nxt_h);
-    cur = nxt;
-  }
+  };
+  auto run = [&](auto rc) {
+    int t = 0;
+    for (; t + 2 <= n_steps; t += 3) {
+      iteration(t, IC<0>{}, rc);
+      iteration(t + 1, IC<1>{}, rc);
+      iteration(t + 2, IC<2>{}, rc);
+    }
+    if (t <= n_steps) iteration(t, IC<0>{}, rc);
+    if (t + 1 <= n_steps) iteration(t + 1, IC<1>{}, rc);
+  };
+  if (role == 0) run(IC<0>{});
+  else run(IC<1>{});
 
   // epilogue: lane holds key kw0 + l32, head dims 32 cb + 8 j + 4 half + 0..3
   // in acc[cb][4 j .. 4 j + 3].  Each wave stages its 32 x D block in LDS
