@@ -193,8 +193,8 @@ attn_bwd_dkdv_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
   const int r = b / kXcds;
   const int per_item = hkv * head_split;
   const DevItem it = items[(r / per_item) * kXcds + xcd];
-  const int g = (r % per_item) / head_split;
-  const int split = r % head_split;
+  const int g = __builtin_amdgcn_readfirstlane((r % per_item) / head_split);
+  const int split = __builtin_amdgcn_readfirstlane(r % head_split);
   if (it.doc < 0) return;
 
   const int tid = threadIdx.x;
@@ -212,8 +212,8 @@ attn_bwd_dkdv_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
   const int key = kw0 + l32;                   // this lane's key
   const int64_t q_tok = int64_t(hq) * D;
   const int64_t kv_tok = int64_t(hkv) * D;
-  const int grp = hq / hkv;
-  const int hpg = grp / head_split;            // q heads handled here
+  const int grp = __builtin_amdgcn_readfirstlane(hq / hkv);
+  const int hpg = __builtin_amdgcn_readfirstlane(grp / head_split);   // q heads handled here
   const int h_begin = g * grp + split * hpg;
   // the first chain's result x becomes fma(x, alpha, -row)
   const float alpha = role == 0 ? scale * kLog2e : scale;
@@ -514,9 +514,9 @@ attn_bwd_dq_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ 
   const int xcd = b & (kXcds - 1);
   const int r = b / kXcds;
   const DevItem it = items[(r / hq) * kXcds + xcd];
-  const int h = r % hq;
+  const int h = __builtin_amdgcn_readfirstlane(r % hq);
   if (it.doc < 0) return;
-  const int g = h / (hq / hkv);
+  const int g = __builtin_amdgcn_readfirstlane(h / (hq / hkv));
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;

@@ -73,9 +73,9 @@ attn_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
   const int xcd = b & (kXcds - 1);
   const int r = b / kXcds;
   const DevItem it = items[(r / hq) * kXcds + xcd];
-  const int h = r % hq;
+  const int h = __builtin_amdgcn_readfirstlane(r % hq);
   if (it.doc < 0) return;
-  const int g = h / (hq / hkv);
+  const int g = __builtin_amdgcn_readfirstlane(h / (hq / hkv));
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
