@@ -90,35 +90,13 @@ f32_to_bf16_kernel(const f32x4* __restrict__ src, u32x2* __restrict__ dk, u32x2*
 }
 
 // A chain of N dependent-accumulator MFMAs whose LDS operand fragment f is
-// read PF fragments ahead of its use; the schedule is pinned to (MFMA, LDS
-// read) pairs so the read latency hides behind the matrix pipe.
-// RPF is the number of LDS read instructions per fragment.
-template <int N, int PF, int SYNC, int RPF = 1, typename Load, typename Mac>
-__device__ __forceinline__ void mfma_chain(Load load, Mac mac) {
-  bf16x8 r[PF];
-#pragma unroll
-  for (int f = 0; f < PF; ++f) r[f] = load(f);
-#pragma unroll
-  for (int f = 0; f < N; ++f) {
-    const bf16x8 a = r[f % PF];
-    if (f + PF < N) r[f % PF] = load(f + PF);
-    mac(f, a);
-  }
-  __builtin_amdgcn_sched_group_barrier(0x100, PF * RPF, SYNC);
-#pragma unroll
-  for (int f = 0; f < N - PF; ++f) {
-    __builtin_amdgcn_sched_group_barrier(0x008, 1, SYNC);
-    __builtin_amdgcn_sched_group_barrier(0x100, RPF, SYNC);
-  }
-  __builtin_amdgcn_sched_group_barrier(0x008, PF, SYNC);
-}
-
-// The same chain with every step fenced, so the LDS reads keep their distance
-// PF from the MFMA that uses them.  The group barriers above pin only the
-// kinds of instructions, and the scheduler may fill a chain's read slots with
+// read PF fragments ahead of its use, with every step fenced so the reads
+// keep that distance.  Pinning only the kinds of instructions
+// (sched_group_barrier) let the scheduler fill a chain's read slots with
 // other reads of the region and sink the chain's own reads to just before
-// their MFMA.  The dQ kernel runs 1-2 % faster with the fenced form; the
-// dK/dV kernel runs faster with the pinned-kinds form.
+// their MFMA: the fenced form is 1-2 % faster in dQ and 1-3.5 % in dK/dV
+// (there the second chain's transpose reads had taken the first chain's read
+// slots, leaving three of its MFMAs each waiting for a fresh read).
 template <int N, int PF, typename Load, typename Mac>
 __device__ __forceinline__ void mfma_chain_fenced(Load load, Mac mac) {
   bf16x8 r[PF];
@@ -343,7 +321,7 @@ attn_bwd_dkdv_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
       }
       // S = Q K^T or dP = dO V^T (rows: queries 16s + 8 half + u; cols: keys)
       f32x16 x;
-      mfma_chain<NKS, 4, 0>(
+      mfma_chain_fenced<NKS, 4>(
           [&](int f) { return as_bf16x8(*reinterpret_cast<const u32x4*>(tile1 + a_off[f])); },
           [&](int f, const bf16x8& a) { x = mfma32(a, bf[f], f == 0 ? f32x16{} : x); });
       // B fragments of the second chain (transposed reads), issued now so
