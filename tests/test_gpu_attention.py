@@ -88,6 +88,23 @@ def test_fp32_output_and_softmax_range():
     _compare(res, q, k, v, do, lq, lk, True, "fp32-out", bwd=False)
 
 
+@pytest.mark.parametrize("d,hq,hkv", [(64, 8, 2), (128, 8, 2)])
+def test_head_split_batches(d, hq, hkv):
+    """One long document among short ones: the dK/dV pass splits each q-head
+    group over workgroups (fp32 partials summed by the convert kernel), for
+    both head dims; full tensors against the oracle."""
+    dev = require_gpu()
+    lens = [3000, 257, 131, 64, 500, 1]
+    cu = workloads.cu_seqlens(lens)
+    d_only = (sum(lens) * hq * 4 + 255) // 256 * 256
+    assert vl.bwd_workspace_bytes_cu(cu, cu, hq, hkv, d) > d_only   # the split path runs
+    w = workloads.Workload(f"split_d{d}", lens, hq=hq, hkv=hkv, d=d, seed=11)
+    q, k, v, do = workloads.make_tensors(w)
+    say(f"case lens={lens} hq={hq} hkv={hkv} d={d}")
+    res = _run(q, k, v, do, lens, lens, True, dev)
+    _compare(res, q, k, v, do, lens, lens, True, f"split_d{d}")
+
+
 def test_longtail_16k_full():
     dev = require_gpu()
     w = workloads.longtail_16k()
