@@ -5,7 +5,7 @@ One step = the whole hot path over one synthetic packed batch:
 varlen_attn_fwd and varlen_attn_bwd, each validating the cu_seqlens,
 scheduling the work lists on the host and uploading them (the plan cache is
 off, as for a freshly packed batch every step), then the kernels (forward;
-D = rowsum(dO*O), dK/dV, dQ).  The same steps with cached work lists are
+dQ, which also stores D = rowsum(dO*O); dK/dV).  The same steps with cached work lists are
 reported beside it.  The
 headline workload is the 16384-token long-tail batch (lognormal lengths,
 median 512, sigma 1.2, clipped to [64, 8192]; 32 q heads, 4 kv heads,
@@ -518,8 +518,7 @@ def main():
     # launch stream: the per-kernel table and the roofline
     rp = bench_attention(vl, torch, w, a.steps, a.warmup, dev, profile=True)
     kflops = attn_kernel_flops(r["pairs"], w.hq, w.d)
-    bpre = 2 * w.total * w.hq * w.d * 2 + w.total * w.hq * 4
-    ktab = kernel_table(rp["prof"], kflops, {"bwd_pre": bpre})
+    ktab = kernel_table(rp["prof"], kflops, {})
     dom = max((n for n in kflops if n in rp["prof"]), key=lambda n: rp["prof"][n][1])
     dom_avg = rp["prof"][dom][1] / rp["prof"][dom][0]
     achieved = kflops[dom] / (dom_avg * 1e-3) / 1e12

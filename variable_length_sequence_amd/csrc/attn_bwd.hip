@@ -7,8 +7,13 @@
 //   dS_ij = P_ij (dP_ij - D_i),
 //   dV_j = sum_i P_ij dO_i,  dK_j = scale sum_i dS_ij Q_i,  dQ_i = scale sum_j dS_ij K_j.
 //
-// Three kernels (four with a q-head split), no atomics:
-//   1. bwd_pre: D = rowsum(dO * O) in fp32, [Hq, T].
+// Two kernels (three with a q-head split), no atomics:
+//   1. dq: the forward's mapping (a lane owns one query): S^T = K Q^T and
+//      dP^T = V dO^T per 64-key tile, then dQ^T += K^T dS^T; the Q, dO and O
+//      tiles arrive in LDS by direct loads and dQ leaves through LDS, all in
+//      whole rows.  D = rowsum(dO * O) of its rows is computed in the
+//      prologue (the O tile rides beside the first K/V tile) and also stored,
+//      fp32 [Hq, T], for (2): no separate pass over O and dO.
 //   2. dkdv: one workgroup per (128-key tile of a document, kv head[, slice of
 //      its q heads]); each wave owns 32 keys and keeps their K, V operands and
 //      fp32 dK, dV accumulators in registers while 32-row query tiles of every
@@ -16,15 +21,11 @@
 //      Scores are computed as S = Q K^T so a lane owns one key; the query rows
 //      of the A operand are permuted so P and dS come out of the MFMA already
 //      in the A-operand layout of dV += P^T dO and dK += dS^T Q.
-//   3. dq: the forward's mapping (a lane owns one query): S^T = K Q^T and
-//      dP^T = V dO^T per 64-key tile, then dQ^T += K^T dS^T; the Q and dO
-//      tiles arrive in LDS by direct loads and dQ leaves through LDS, all in
-//      whole rows.
 //   With the q heads of a group split over workgroups, each split stores its
-//   fp32 dK/dV partial and a fourth kernel adds the partials in split order
+//   fp32 dK/dV partial and a third kernel adds the partials in split order
 //   (plain stores run at several times the rate of fp32 atomic adds, and the
 //   sum is deterministic).
-// The extra two contractions of (3) replace a zeroed fp32 dQ accumulator, its
+// The extra two contractions of (1) replace a zeroed fp32 dQ accumulator, its
 // atomics and a conversion pass, and keep dQ deterministic.
 #include <hip/hip_runtime.h>
 
@@ -39,36 +40,6 @@ namespace vl {
 namespace {
 
 constexpr int kThreads = 256;
-
-// ---------------------------------------------------------------- D = rowsum(dO O)
-template <int D>
-__global__ void __launch_bounds__(kThreads)
-bwd_pre_kernel(const uint16_t* __restrict__ o, const uint16_t* __restrict__ dout,
-               float* __restrict__ delta, int64_t total_q, int hq) {
-  constexpr int LPR = D / 8;                 // lanes per (row, head)
-  constexpr int RPB = kThreads / LPR;        // rows per block
-  const int sub = threadIdx.x / LPR;
-  const int c8 = threadIdx.x % LPR;
-  const int64_t n_pairs = total_q * hq;
-  for (int64_t pr = int64_t(blockIdx.x) * RPB + sub; pr < n_pairs;
-       pr += int64_t(gridDim.x) * RPB) {
-    const u32x4 a = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(o + pr * D + c8 * 8));
-    const u32x4 b = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(dout + pr * D + c8 * 8));
-    float acc = 0.f;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      acc = fmaf(bf16_lo(a[j]), bf16_lo(b[j]), acc);
-      acc = fmaf(bf16_hi(a[j]), bf16_hi(b[j]), acc);
-    }
-#pragma unroll
-    for (int m = LPR / 2; m >= 1; m >>= 1) acc += __shfl_xor(acc, m, 64);
-    if (c8 == 0) {
-      const int64_t t = pr / hq;
-      const int h = int(pr - t * hq);
-      delta[int64_t(h) * total_q + t] = acc;
-    }
-  }
-}
 
 // dK and dV of a split q-head group: the sum of the splits' fp32 partials
 // ([split][dK, dV][T, H, D]), added in split order (deterministic), -> bf16
@@ -481,8 +452,8 @@ template <int D>
 __global__ void __launch_bounds__(kThreads, 2)
 attn_bwd_dq_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
                    const uint16_t* __restrict__ v, const uint16_t* __restrict__ dout,
-                   const float* __restrict__ lse, const float* __restrict__ delta,
-                   const DevItem* __restrict__ items, int hq,
+                   const uint16_t* __restrict__ o, const float* __restrict__ lse,
+                   float* __restrict__ delta, const DevItem* __restrict__ items, int hq,
                    int hkv, float scale, int causal, int64_t total_q, uint16_t* __restrict__ dq) {
   constexpr int NKS = D / 16;
   constexpr int NCB = D / 32;
@@ -519,13 +490,12 @@ attn_bwd_dq_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ 
   load_rows128_lds<D>(dout + (int64_t(it.q_start) + q0) * q_tok + int64_t(h) * D,
                       uint32_t(q_tok * 2), lq - q0, lds_addr(sm.k[0]), lds_addr(sm.v[0]), w, lane);
   bf16x8 qf[NKS], df[NKS];
-  float lse2 = INFINITY, dl = 0.f;
+  float lse2 = INFINITY;
   if (qrow < lq) {
     const float l = lse[int64_t(h) * total_q + it.q_start + qrow];
     lse2 = (l == -INFINITY) ? INFINITY : l * kLog2e;
-    dl = delta[int64_t(h) * total_q + it.q_start + qrow];
   }
-  const float dls = dl * scale;
+  float dls;   // D scale, computed once the O tile has landed
 
   f32x16 acc[NCB];
 #pragma unroll
@@ -630,6 +600,39 @@ attn_bwd_dq_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ 
   __syncthreads();
   if (n_kv > 0)
     loader.load(kbase, vbase, kv_tok, 0, lk, lds_addr(sm.k[0]), lds_addr(sm.v[0]), w, lane);
+  // the O tile lands in buffer 1 beside the first K/V tile
+  load_rows128_lds<D>(o + (int64_t(it.q_start) + q0) * q_tok + int64_t(h) * D,
+                      uint32_t(q_tok * 2), lq - q0, lds_addr(sm.k[1]), lds_addr(sm.v[1]), w, lane);
+  __builtin_amdgcn_s_waitcnt(kWaitAll);
+  __syncthreads();
+  // D = dO . O of this lane's query row: each lane sums its 16-byte chunks
+  // (2s + half) one by one, the chunks pairwise in a fixed tree, then the two
+  // halves of the row; the row's D is stored for the dK/dV kernel
+  float dl;
+  {
+    const int row = w * 32 + l32;
+    const uint16_t* os = row < 64 ? sm.k[1] : sm.v[1];
+    float part[NKS];
+#pragma unroll
+    for (int s2 = 0; s2 < NKS; ++s2) {
+      const u32x4 a = *reinterpret_cast<const u32x4*>(&os[SwzTile<D>::chunk(row & 63, 2 * s2 + half)]);
+      const u32x4 b = as_u32x4(df[s2]);
+      float x = 0.f;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        x = fmaf(bf16_lo(a[j]), bf16_lo(b[j]), x);
+        x = fmaf(bf16_hi(a[j]), bf16_hi(b[j]), x);
+      }
+      part[s2] = x;
+    }
+#pragma unroll
+    for (int m = NKS / 2; m >= 1; m >>= 1)
+#pragma unroll
+      for (int s2 = 0; s2 < m; ++s2) part[s2] += part[s2 + m];
+    dl = halves_sum(part[0]);
+    if (half == 0 && qrow < lq) delta[int64_t(h) * total_q + it.q_start + qrow] = dl;
+  }
+  dls = dl * scale;
   int kt = 0;
   for (; kt + 1 < n_kv; kt += 2) {
     tile(kt, IC<0>{});
@@ -672,13 +675,12 @@ hipError_t run_bwd(const AttnShape& s, const uint16_t* q, const uint16_t* k, con
                    uint16_t* dq, uint16_t* dk, uint16_t* dv, float* delta, float* dkv_acc,
                    hipStream_t stream) {
   const int64_t kv_elems = s.total_k * s.hkv * D;
-  if (s.total_q > 0) {
-    constexpr int RPB = kThreads / (D / 8);
-    const int64_t want = (s.total_q * s.hq + RPB - 1) / RPB;
-    const int blocks = int(std::max<int64_t>(1, std::min<int64_t>(want, int64_t(1) << 30)));
-    ProfScope prof("bwd_pre", stream);
-    hipLaunchKernelGGL((bwd_pre_kernel<D>), dim3(blocks), dim3(kThreads), 0, stream, o, dout,
-                       delta, s.total_q, s.hq);
+  if (fwd_map.rows > 0) {
+    const dim3 grid(unsigned(fwd_map.rows) * unsigned(kXcds) * unsigned(s.hq));
+    ProfScope prof("bwd_dq", stream);
+    hipLaunchKernelGGL((attn_bwd_dq_kernel<D>), grid, dim3(kThreads), 0, stream, q, k, v, dout, o,
+                       lse, delta, fwd_map.items, s.hq, s.hkv, s.scale, s.causal,
+                       s.total_q, dq);
   }
   if (bwd_map.rows > 0) {
     const dim3 grid(unsigned(bwd_map.rows) * unsigned(kXcds) * unsigned(s.hkv * head_split));
@@ -694,13 +696,6 @@ hipError_t run_bwd(const AttnShape& s, const uint16_t* q, const uint16_t* k, con
     hipLaunchKernelGGL(f32_to_bf16_kernel, dim3(blocks), dim3(kThreads), 0, stream,
                        reinterpret_cast<const f32x4*>(dkv_acc), reinterpret_cast<u32x2*>(dk),
                        reinterpret_cast<u32x2*>(dv), n4, int(head_split));
-  }
-  if (fwd_map.rows > 0) {
-    const dim3 grid(unsigned(fwd_map.rows) * unsigned(kXcds) * unsigned(s.hq));
-    ProfScope prof("bwd_dq", stream);
-    hipLaunchKernelGGL((attn_bwd_dq_kernel<D>), grid, dim3(kThreads), 0, stream, q, k, v, dout, lse,
-                       delta, fwd_map.items, s.hq, s.hkv, s.scale, s.causal,
-                       s.total_q, dq);
   }
   return hipGetLastError();
 }

@@ -71,8 +71,8 @@ hipError_t launch_attn_fwd(const AttnShape& s, const void* q, const void* k, con
                            const ItemMap& map, int32_t out_kind, void* out, float* lse,
                            hipStream_t stream);
 
-// Backward: D_i = dO_i . O_i, then dK/dV over the kv-tile list, then dQ over
-// the query-tile list.  When the q heads of one group are split over
+// Backward: dQ over the query-tile list, which also stores D_i = dO_i . O_i
+// in delta ([hq, total_q] fp32), then dK/dV over the kv-tile list.  When the q heads of one group are split over
 // head_split > 1 workgroups, dkv_acc holds their fp32 partials
 // [head_split][dK, dV][total_k, hkv, d], summed by a conversion kernel.
 constexpr int kMaxHeadSplit = 4;
