@@ -506,6 +506,10 @@ attn_bwd_dq_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ 
   const uint16_t* kbase = k + int64_t(it.k_start) * kv_tok + int64_t(g) * D;
   const uint16_t* vbase = v + int64_t(it.k_start) * kv_tok + int64_t(g) * D;
   const PairLoader<D, QB_K, kThreads / 64> loader(w, lane, uint32_t(kv_tok * 2));
+  // the next key tile to load, advanced by one tile per tile
+  const int64_t kv_step = int64_t(QB_K) * kv_tok;
+  const uint16_t* knext = kbase + kv_step;
+  const uint16_t* vnext = vbase + kv_step;
   const int wq_first = q0 + w * 32;
   const int wq_last = min(q0 + w * 32 + 31, lq - 1);
   const int lim = causal ? min(lk - 1, qrow + off) : lk - 1;
@@ -516,9 +520,12 @@ attn_bwd_dq_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ 
     const int kv0 = kt * QB_K;
     __builtin_amdgcn_s_waitcnt(kWaitAll);
     __syncthreads();
-    if (kt + 1 < it.count)
-      loader.load(kbase, vbase, kv_tok, kv0 + QB_K, lk, lds_addr(sm.k[buf ^ 1]),
-                  lds_addr(sm.v[buf ^ 1]), w, lane);
+    if (kt + 1 < it.count) {
+      loader.load_from(knext, vnext, lk - kv0 - QB_K, uint32_t(kv_tok * 2),
+                       lds_addr(sm.k[buf ^ 1]), lds_addr(sm.v[buf ^ 1]), w, lane);
+      knext += kv_step;
+      vnext += kv_step;
+    }
     const uint16_t* ks = sm.k[buf];
     const uint16_t* vs = sm.v[buf];
 

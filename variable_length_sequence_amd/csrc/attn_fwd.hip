@@ -109,6 +109,10 @@ attn_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
   const uint16_t* kbase = k + int64_t(it.k_start) * kv_tok + int64_t(g) * D;
   const uint16_t* vbase = v + int64_t(it.k_start) * kv_tok + int64_t(g) * D;
   const PairLoader<D, BK, kThreads / 64> loader(w, lane, uint32_t(kv_tok * 2));
+  // the next key tile to load, advanced by one tile per tile
+  const int64_t kv_step = int64_t(BK) * kv_tok;
+  const uint16_t* knext = kbase + kv_step;
+  const uint16_t* vnext = vbase + kv_step;
 
   // first and last query rows of this wave (for skipping / masking)
   const int wq_first = q0 + w * 32;
@@ -123,9 +127,12 @@ attn_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     // is done with the other buffer (read during tile kt - 1)
     __builtin_amdgcn_s_waitcnt(kWaitAll);
     __syncthreads();
-    if (kt + 1 < it.count)
-      loader.load(kbase, vbase, kv_tok, kv0 + BK, lk, lds_addr(sm.k[buf ^ 1]),
-                  lds_addr(sm.v[buf ^ 1]), w, lane);
+    if (kt + 1 < it.count) {
+      loader.load_from(knext, vnext, lk - kv0 - BK, uint32_t(kv_tok * 2), lds_addr(sm.k[buf ^ 1]),
+                       lds_addr(sm.v[buf ^ 1]), w, lane);
+      knext += kv_step;
+      vnext += kv_step;
+    }
     const uint16_t* ks = sm.k[buf];
     const uint16_t* vs = sm.v[buf];
 

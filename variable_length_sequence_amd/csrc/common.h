@@ -125,10 +125,45 @@ __device__ __forceinline__ void load_lds16(const void* sbase, uint32_t voff, uin
                : "memory", "m0");
 }
 
+// N direct loads of 16 bytes per lane into N consecutive 1 KB LDS blocks
+// ending at byte address lds_top (wave-uniform): load u lands at lds_top -
+// 1024 (N - 1 - u) + 16 lane and reads sbase + voff[u] - 1024 (N - 1 - u).
+// The hardware adds an instruction's immediate offset to both its global and
+// its LDS address, so one M0 value serves all N loads; callers raise voff[u]
+// by 1024 (N - 1 - u) to read where they mean.
+template <int N>
+__device__ __forceinline__ void load_lds16_group(const void* sbase, const uint32_t (&voff)[N],
+                                                 uint32_t lds_top) {
+  const uint64_t a = reinterpret_cast<uint64_t>(sbase);
+  const uint32_t lo = uint32_t(__builtin_amdgcn_readfirstlane(int(uint32_t(a))));
+  const uint32_t hi = uint32_t(__builtin_amdgcn_readfirstlane(int(uint32_t(a >> 32))));
+  sbase = reinterpret_cast<const void*>(uint64_t(lo) | (uint64_t(hi) << 32));
+  const uint32_t m0 = uint32_t(__builtin_amdgcn_readfirstlane(int(lds_top)));
+  static_assert(N == 2 || N == 4, "grouped direct loads come in twos or fours");
+  if constexpr (N == 2)
+    asm volatile("s_mov_b32 m0, %3\n\ts_nop 0\n\t"
+                 "global_load_lds_dwordx4 %0, %2 offset:-1024\n\t"
+                 "global_load_lds_dwordx4 %1, %2"
+                 :
+                 : "v"(voff[0]), "v"(voff[1]), "s"(sbase), "s"(m0)
+                 : "memory", "m0");
+  else
+    asm volatile("s_mov_b32 m0, %5\n\ts_nop 0\n\t"
+                 "global_load_lds_dwordx4 %0, %4 offset:-3072\n\t"
+                 "global_load_lds_dwordx4 %1, %4 offset:-2048\n\t"
+                 "global_load_lds_dwordx4 %2, %4 offset:-1024\n\t"
+                 "global_load_lds_dwordx4 %3, %4"
+                 :
+                 : "v"(voff[0]), "v"(voff[1]), "v"(voff[2]), "v"(voff[3]), "s"(sbase), "s"(m0)
+                 : "memory", "m0");
+}
+
 // The direct loads of a pair of ROWS x D bf16 tiles (the same rows of two
 // [T, H, D] tensors) into SwzTile layout, spread over the NW waves of a
-// workgroup.  Load u of a lane fills LDS block u NW + wave (1 KB: 64 lanes x
-// 16 bytes); the lane that lands on LDS row p, chunk pc fetches source row
+// workgroup.  Load u of a lane fills one LDS block (1 KB: 64 lanes x 16
+// bytes): block wave N + u when every wave has the same number N > 1 of
+// loads (so a wave's loads of one tensor share one M0 value), else u NW +
+// wave; the lane that lands on LDS row p, chunk pc fetches source row
 // swap_bits23(p), chunk pc ^ swz(p).  The lane's byte offsets relative to the
 // tile's first row are computed once, so a tile costs one scalar base
 // pointer per tensor.  Near the end of a document, rows at or past n_valid
@@ -139,7 +174,12 @@ struct PairLoader {
   static constexpr int RPL = 64 / NCH;         // rows per 1 KB block
   static constexpr int BLKS = ROWS / RPL;
   static constexpr int N = (BLKS + NW - 1) / NW;   // loads per lane per tensor
+  static constexpr bool kGrouped = N > 1 && BLKS == N * NW;
   uint32_t voff[N];
+
+  __device__ __forceinline__ static int block(int u, int wave) {
+    return kGrouped ? wave * N + u : u * NW + wave;
+  }
 
   // wave-uniform: whether load u of this wave exists
   __device__ __forceinline__ static bool has(int u, int wave) {
@@ -147,25 +187,32 @@ struct PairLoader {
   }
 
   __device__ __forceinline__ static int src_row(int u, int wave, int lane) {
-    return swap_bits23((u * NW + wave) * RPL + lane / NCH);
+    return swap_bits23(block(u, wave) * RPL + lane / NCH);
   }
   __device__ __forceinline__ static uint32_t col_bytes(int u, int wave, int lane) {
-    const int p = (u * NW + wave) * RPL + lane / NCH;
+    const int p = block(u, wave) * RPL + lane / NCH;
     return uint32_t(((lane % NCH) ^ SwzTile<D>::swz(p)) << 4);
   }
   __device__ __forceinline__ PairLoader(int wave, int lane, uint32_t row_bytes) {
 #pragma unroll
     for (int u = 0; u < N; ++u)
-      voff[u] = uint32_t(src_row(u, wave, lane)) * row_bytes + col_bytes(u, wave, lane);
+      voff[u] = uint32_t(src_row(u, wave, lane)) * row_bytes + col_bytes(u, wave, lane) +
+                (kGrouped ? uint32_t(1024 * (N - 1 - u)) : 0u);
   }
   // a, b: first row of the tile in each tensor (wave-uniform)
   __device__ __forceinline__ void issue(const uint16_t* a, const uint16_t* b, uint32_t da,
                                         uint32_t db, int wave) const {
+    if constexpr (kGrouped) {
+      const uint32_t top = uint32_t((wave * N + N - 1) * 1024);
+      load_lds16_group<N>(a, voff, da + top);
+      load_lds16_group<N>(b, voff, db + top);
+    } else {
 #pragma unroll
-    for (int u = 0; u < N; ++u) {
-      if (!has(u, wave)) continue;
-      load_lds16(a, voff[u], da + (u * NW + wave) * 1024);
-      load_lds16(b, voff[u], db + (u * NW + wave) * 1024);
+      for (int u = 0; u < N; ++u) {
+        if (!has(u, wave)) continue;
+        load_lds16(a, voff[u], da + block(u, wave) * 1024);
+        load_lds16(b, voff[u], db + block(u, wave) * 1024);
+      }
     }
   }
   __device__ __forceinline__ void issue_clamped(const uint16_t* a, const uint16_t* b, uint32_t da,
@@ -176,9 +223,19 @@ struct PairLoader {
       if (!has(u, wave)) continue;
       const uint32_t o = uint32_t(min(src_row(u, wave, lane), n_valid - 1)) * row_bytes +
                          col_bytes(u, wave, lane);
-      load_lds16(a, o, da + (u * NW + wave) * 1024);
-      load_lds16(b, o, db + (u * NW + wave) * 1024);
+      load_lds16(a, o, da + block(u, wave) * 1024);
+      load_lds16(b, o, db + block(u, wave) * 1024);
     }
+  }
+  // a tile whose first rows are at a, b, with n_left rows of the document
+  // from there on
+  __device__ __forceinline__ void load_from(const uint16_t* a, const uint16_t* b, int n_left,
+                                            uint32_t row_bytes, uint32_t da, uint32_t db,
+                                            int wave, int lane) const {
+    if (n_left >= ROWS)
+      issue(a, b, da, db, wave);
+    else
+      issue_clamped(a, b, da, db, wave, lane, n_left, row_bytes);
   }
   // tile of rows row0 .. row0 + ROWS - 1 of a document with n_rows rows;
   // a, b point at the document's first row
