@@ -333,6 +333,28 @@ VL_API int varlen_schedule_export(const int32_t* cu_seqlens_q, const int32_t* cu
                            int32_t* bq, int32_t* bk);
 
 /*
+ * varlen_schedule_export_dkdv - host-only: the dK/dV work list as the kernel
+ * runs it, with its q-head split.  A kv tile whose group of Hq / Hkv q heads
+ * (each `count` query steps) would outlast the average per-CU share of the
+ * pass, Hq times the summed counts over n_cu, is cut into 2 or 4 slices of
+ * those heads (at most min(4, Hq / Hkv), a power of two dividing it), the
+ * fewest that bring a slice within that share; the other tiles stay whole.
+ *
+ *   entries      host int32 [6 * cap], or NULL to query *n_entries only:
+ *                (doc, kv_tile, first q tile, q tiles, slice, n_slices),
+ *                longest first by q tiles x Hq / (Hkv n_slices)
+ *   n_cu         compute units the pass spreads over (the library uses the
+ *                device's count)
+ * The largest n_slices is the number of fp32 dK/dV partials the backward
+ * workspace holds.  Errors: VL_EINVAL, VL_ESEQLENS, VL_ESHAPE (head counts),
+ * VL_EWORKSPACE (cap too small).
+ */
+VL_API int varlen_schedule_export_dkdv(const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
+                                int32_t n_docs, int32_t causal, int32_t n_heads_q,
+                                int32_t n_heads_kv, int32_t n_cu, int32_t* entries, int64_t cap,
+                                int64_t* n_entries);
+
+/*
  * varlen_ring_block - host-only: one (query chunk, key chunk) block of ring
  * attention over a packed causal batch.  The packed token axis is cut into
  * contiguous chunks, one per ring rank, and every block of the chunk grid has

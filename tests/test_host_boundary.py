@@ -75,6 +75,59 @@ def test_schedule_matches_oracle_random(rng):
             _check_against_oracle(_cu(lq), _cu(lk), causal, 128 if rng.random() < 0.5 else 64)
 
 
+def _check_dkdv_split(cq, ck, causal, hq, hkv, n_cu):
+    """The dK/dV list with its q-head split: every q head of every kv tile
+    exactly once, only tiles over the per-CU share cut, into the fewest
+    power-of-two slices that fit (at most min(4, group)), longest first."""
+    ent = vl.varlen_schedule_export_dkdv(cq, ck, causal, hq, hkv, n_cu)
+    items = osched.bwd_items(cq, ck, causal, 32, 128).reshape(-1, 4)
+    grp = hq // hkv
+    max_split = 1
+    while max_split < grp and grp % (2 * max_split) == 0 and 2 * max_split <= 4:
+        max_split *= 2
+    per_cu = grp * hkv * int(items[:, 3].sum()) / n_cu
+    by_tile = {}
+    for doc, tile, first, count, sl, ns in ent.tolist():
+        by_tile.setdefault((doc, tile, first, count), []).append((sl, ns))
+    assert sorted(by_tile) == sorted(map(tuple, items.tolist()))
+    for (doc, tile, first, count), sl in by_tile.items():
+        ns = sl[0][1]
+        assert all(n == ns for _, n in sl) and sorted(s for s, _ in sl) == list(range(ns))
+        assert ns <= max_split and grp % ns == 0
+        want = 1
+        while want < max_split and count * grp / want > per_cu:
+            want *= 2
+        assert ns == want, (doc, tile, count, ns, want)
+    work = ent[:, 3].astype(np.int64) * grp // ent[:, 5]
+    assert np.all(work[:-1] >= work[1:])
+    return int(ent[:, 5].max()) if len(ent) else 1
+
+
+def test_dkdv_split_schedule():
+    for w in (workloads.longtail_16k(), workloads.mixed_128k(), workloads.tiny()):
+        cu = w.cu
+        top = _check_dkdv_split(cu, cu, True, w.hq, w.hkv, 256)
+        # the backward workspace holds as many fp32 partials as the largest cut
+        delta = _align256(w.total * w.hq * 4)
+        part = _align256(top * 2 * w.total * w.hkv * w.d * 4) if top > 1 else 0
+        assert vl.bwd_workspace_bytes_cu(cu, cu, w.hq, w.hkv, w.d) == delta + part, w.name
+    # the long-tail batch cuts only its longest key tiles
+    cu = workloads.longtail_16k().cu
+    ent = vl.varlen_schedule_export_dkdv(cu, cu, True, 32, 4, 256)
+    cut = {(d, t) for d, t, *_, ns in ent.tolist() if ns > 1}
+    assert 0 < len(cut) < len({(d, t) for d, t, *_ in ent.tolist()}) // 2
+    rng = np.random.default_rng(5)
+    for _ in range(40):
+        n = int(rng.integers(1, 12))
+        lq = rng.integers(0, 3000, size=n)
+        hkv = int(rng.choice([1, 2, 4]))
+        hq = hkv * int(rng.choice([1, 2, 3, 4, 8]))
+        _check_dkdv_split(_cu(lq), _cu(lq), bool(rng.integers(0, 2)), hq, hkv,
+                          int(rng.choice([8, 64, 256])))
+    with pytest.raises(vl.VarlenError):
+        vl.varlen_schedule_export_dkdv(_cu([5]), _cu([5]), True, 6, 4, 256)
+
+
 def test_tiny_schedule_values():
     r = vl.varlen_schedule_export(_cu([17, 64, 128, 47]), _cu([17, 64, 128, 47]), True, 0, 64)
     assert r["useful_pairs"] == 11617

@@ -16,6 +16,7 @@ Entry points (same names as the C ABI in ``include/varlen.h``):
   nsp_route(lengths, n_gpus, sp_max, cost, token_budget, prefix, beam) -> dict (host only)
   nsp_plan_cost(lengths, plan, n_gpus, sp_max, cost) -> dict (host only)
   varlen_schedule_export(cu_q, cu_k, causal, pass_, head_dim) -> dict (host only)
+  varlen_schedule_export_dkdv(cu_q, cu_k, causal, hq, hkv, n_cu) -> int32 [n, 6] (host only)
   varlen_ring_block(cu, q_range, k_range) -> (cu_q, cu_k, causal, cls) (host only)
 """
 from __future__ import annotations
@@ -37,6 +38,7 @@ STATUS = {0: "VL_OK", -1: "VL_EINVAL", -2: "VL_ESHAPE", -3: "VL_ESEQLENS",
 EXPORTS = ["varlen_attn_fwd", "varlen_attn_bwd_workspace_size", "varlen_attn_bwd_workspace_size_cu",
            "varlen_attn_bwd", "varlen_attn_bwd_noalloc",
            "attn_lse_merge", "sp_seq2head", "sp_head2seq", "varlen_schedule_export",
+           "varlen_schedule_export_dkdv",
            "varlen_last_error", "varlen_cache_clear", "varlen_set_plan_cache", "varlen_version",
            "varlen_profile_enable", "varlen_profile_read", "varlen_ring_block", "varlen_attn_fwd_acc", "sp_qkv_seq2head",
            "sp_qkv_head2seq", "basp_shard", "nsp_route", "nsp_plan_cost", "varlen_mfma_probe"]
@@ -115,6 +117,8 @@ def lib():
     L.varlen_schedule_export.argtypes = [pi32, pi32, i32, i32, i32, i32, pi32, i64, pi64, pi64,
                                          pi64, pi32, pi32]
     L.varlen_schedule_export.restype = ctypes.c_int
+    L.varlen_schedule_export_dkdv.argtypes = [pi32, pi32, i32, i32, i32, i32, i32, pi32, i64, pi64]
+    L.varlen_schedule_export_dkdv.restype = ctypes.c_int
     L.varlen_ring_block.argtypes = [pi32, i32, i64, i64, i64, i64, pi32, pi32, pi32, pi32]
     L.varlen_ring_block.restype = ctypes.c_int
     L.varlen_last_error.argtypes = []
@@ -549,6 +553,20 @@ def varlen_schedule_export(cu_q, cu_k, causal: bool, pass_: int, head_dim: int) 
                                     ctypes.byref(bk)))
     return {"items": items[:n.value], "useful_pairs": useful.value, "issued_pairs": issued.value,
             "bq": bq.value, "bk": bk.value}
+
+
+def varlen_schedule_export_dkdv(cu_q, cu_k, causal: bool, n_heads_q: int, n_heads_kv: int,
+                                n_cu: int) -> np.ndarray:
+    """Host-only: the dK/dV work list with its q-head split, rows (doc, kv_tile,
+    first, count, slice, n_slices) in launch order (no GPU needed)."""
+    cq, ck = _cu_host(cu_q), _cu_host(cu_k)
+    n = ctypes.c_int64(0)
+    L = lib()
+    args = (_iptr(cq), _iptr(ck), len(cq) - 1, int(causal), n_heads_q, n_heads_kv, n_cu)
+    _check(L.varlen_schedule_export_dkdv(*args, None, 0, ctypes.byref(n)))
+    out = np.zeros((max(n.value, 1), 6), dtype=np.int32)
+    _check(L.varlen_schedule_export_dkdv(*args, _iptr(out), n.value, ctypes.byref(n)))
+    return out[:n.value]
 
 
 def varlen_ring_block(cu, q_range, k_range):

@@ -33,22 +33,25 @@ int hip_fail(hipError_t e, const char* what) {
 
 // ------------------------------------------------------------ work-list cache
 struct Plan {
-  vl::DevItem* dev = nullptr;   // the items in XCD slot order (rows * kXcds entries)
+  vl::DevItem* dev = nullptr;   // the entries in XCD slot order (rows * kXcds)
   int32_t n = 0;
-  int32_t rows = 0;             // items of the longest XCD list
+  int32_t rows = 0;             // entries of the longest XCD list
   int32_t max_count = 0;
   int64_t total_count = 0;
-  vl::ItemMap map() const { return vl::ItemMap{dev, rows}; }
+  int32_t max_slices = 1;       // the most slices any item is cut into
+  int32_t split_rows = 0;       // rows up to the last one holding a cut item
+  vl::ItemMap map() const { return vl::ItemMap{dev, rows, split_rows}; }
 };
 
 std::mutex g_mu;
 constexpr size_t kMaxPlans = 4096;
 vl::PlanCache<Plan> g_plans(kMaxPlans);
 
+// The dK/dV list (pass 1) also depends on the head counts (its q-head split).
 std::string plan_key(int dev, int pass, int causal, const int32_t* cu_q, const int32_t* cu_k,
-                     int32_t n_docs) {
+                     int32_t n_docs, int32_t hq, int32_t hkv) {
   std::string key;
-  const int32_t hdr[4] = {dev, pass, causal, n_docs};
+  const int32_t hdr[6] = {dev, pass, causal, n_docs, pass == 1 ? hq : 0, pass == 1 ? hkv : 0};
   key.append(reinterpret_cast<const char*>(hdr), sizeof(hdr));
   key.append(reinterpret_cast<const char*>(cu_q), sizeof(int32_t) * size_t(n_docs + 1));
   key.append(reinterpret_cast<const char*>(cu_k), sizeof(int32_t) * size_t(n_docs + 1));
@@ -64,18 +67,25 @@ void release_plan(Plan& p) {
 
 void clear_plans_locked() { g_plans.clear(release_plan); }
 
-// pass 0: forward / dQ list (query tiles); pass 1: dK/dV list (key tiles).
-// Builds the list on the host in XCD slot order (a workgroup reads its item
-// with one load; an empty slot has doc = -1) and fills the plan's counts.
+int max_head_split(int32_t hq, int32_t hkv);
+int device_cus();
+
+// pass 0: forward / dQ list (query tiles); pass 1: dK/dV list (key tiles,
+// cut by the q-head split).  Builds the list on the host in XCD slot order (a
+// workgroup reads its entry with one load; an empty slot has n_slices = 0)
+// and fills the plan's counts.
 void build_list(int pass, int causal, const int32_t* cu_q, const int32_t* cu_k, int32_t n_docs,
-                std::vector<vl::DevItem>& host, Plan& p) {
+                int32_t hq, int32_t hkv, std::vector<vl::DevItem>& host, Plan& p) {
   const std::vector<vl::Doc> docs = vl::doc_table(cu_q, cu_k, n_docs);
   const std::vector<vl::Item> items =
       pass == 0 ? vl::fwd_items(docs, causal != 0, vl::kFwdBQ, vl::kFwdBK)
                 : vl::bwd_items(docs, causal != 0, vl::kBwdBQ, vl::kBwdBK);
-  const std::vector<vl::DevItem> di = vl::device_items(docs, items);
+  const std::vector<vl::Entry> entries =
+      pass == 0 ? vl::fwd_entries(items)
+                : vl::bwd_entries(items, hq / hkv, hkv, device_cus(), max_head_split(hq, hkv));
+  const std::vector<vl::DevItem> di = vl::device_items(docs, entries);
   int32_t rows = 0;
-  const std::vector<int32_t> slots = vl::xcd_slots(items, vl::kXcds, rows);
+  const std::vector<int32_t> slots = vl::xcd_slots(entries, vl::kXcds, rows);
   p = Plan{};
   p.n = int32_t(di.size());
   p.rows = rows;
@@ -85,21 +95,20 @@ void build_list(int pass, int causal, const int32_t* cu_q, const int32_t* cu_k, 
   }
   host.assign(di.empty() ? 0 : slots.size(), vl::DevItem{});
   for (size_t j = 0; j < host.size(); ++j) {
-    if (slots[j] >= 0) {
-      host[j] = di[size_t(slots[j])];
-    } else {
-      host[j].doc = -1;
-    }
+    if (slots[j] < 0) continue;
+    host[j] = di[size_t(slots[j])];
+    p.max_slices = std::max<int32_t>(p.max_slices, host[j].n_slices);
+    if (host[j].n_slices > 1) p.split_rows = int32_t(j / vl::kXcds) + 1;
   }
 }
 
 // capturing: the caller's stream is being captured (the plan gets pinned).
 int get_plan(int pass, int causal, const int32_t* cu_q, const int32_t* cu_k, int32_t n_docs,
-             bool capturing, Plan& out) {
+             int32_t hq, int32_t hkv, bool capturing, Plan& out) {
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
-  const std::string key = plan_key(dev, pass, causal, cu_q, cu_k, n_docs);
+  const std::string key = plan_key(dev, pass, causal, cu_q, cu_k, n_docs, hq, hkv);
   std::lock_guard<std::mutex> lock(g_mu);
   if (const Plan* hit = g_plans.find(key, capturing)) {
     out = *hit;
@@ -110,7 +119,7 @@ int get_plan(int pass, int causal, const int32_t* cu_q, const int32_t* cu_k, int
                 "a new cu_seqlens pattern under stream capture: run the call once before capturing");
   std::vector<vl::DevItem> host;
   Plan p;
-  build_list(pass, causal, cu_q, cu_k, n_docs, host, p);
+  build_list(pass, causal, cu_q, cu_k, n_docs, hq, hkv, host, p);
   if (!host.empty()) {
     // a new pattern: when the cache is full, drain the device and release the
     // plans no captured graph holds
@@ -233,15 +242,15 @@ class CallPlans {
     }
   }
 
-  int get(int causal, const int32_t* cu_q, const int32_t* cu_k, int32_t n_docs,
-          hipStream_t st, int n_pass, const int* passes, Plan* out) {
+  int get(int causal, const int32_t* cu_q, const int32_t* cu_k, int32_t n_docs, int32_t hq,
+          int32_t hkv, hipStream_t st, int n_pass, const int* passes, Plan* out) {
     if (n_pass < 1 || n_pass > 2) return fail(VL_EINVAL, "internal: one or two work lists per call");
     hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
     const bool capturing =
         hipStreamIsCapturing(st, &cs) == hipSuccess && cs != hipStreamCaptureStatusNone;
     if (g_cache_on.load()) {
       for (int i = 0; i < n_pass; ++i) {
-        const int rc = get_plan(passes[i], causal, cu_q, cu_k, n_docs, capturing, out[i]);
+        const int rc = get_plan(passes[i], causal, cu_q, cu_k, n_docs, hq, hkv, capturing, out[i]);
         if (rc) return rc;
       }
       return VL_OK;
@@ -255,7 +264,7 @@ class CallPlans {
     std::vector<vl::DevItem> host[2];
     size_t at[2] = {0, 0}, total = 0;
     for (int i = 0; i < n_pass; ++i) {
-      build_list(passes[i], causal, cu_q, cu_k, n_docs, host[i], out[i]);
+      build_list(passes[i], causal, cu_q, cu_k, n_docs, hq, hkv, host[i], out[i]);
       at[i] = total;
       total += align256(host[i].size() * sizeof(vl::DevItem));
     }
@@ -337,24 +346,18 @@ int device_cus() {
   return n_cu;
 }
 
-// The q-head split of the dK/dV pass: the q heads of a group go to 2-4
-// workgroups when one item would otherwise outlast the average per-CU share
-// of the whole pass (only the item counts of the dK/dV list matter).
+// The most slices the dK/dV list cuts any item into (the q heads of a group
+// go to 2-4 workgroups for the items that would otherwise outlast the
+// average per-CU share of the pass): the number of fp32 partials the
+// workspace holds.
 int choose_split(const int32_t* cu_q, const int32_t* cu_k, int32_t n_docs, int causal,
                  int32_t hq, int32_t hkv, int n_cu) {
   const std::vector<vl::Doc> docs = vl::doc_table(cu_q, cu_k, n_docs);
   const std::vector<vl::Item> items = vl::bwd_items(docs, causal != 0, vl::kBwdBQ, vl::kBwdBK);
-  int64_t total_count = 0;
   int32_t max_count = 0;
-  for (const auto& it : items) {
-    total_count += it.count;
-    max_count = std::max(max_count, it.count);
-  }
-  const int grp = hq / hkv;
-  const double per_cu = double(total_count) * grp * hkv / double(std::max(n_cu, 1));
-  int split = 1;
-  while (split < max_head_split(hq, hkv) && double(max_count) * grp / split > per_cu) split *= 2;
-  return split;
+  for (const auto& it : items) max_count = std::max(max_count, it.count);
+  return vl::item_head_split(max_count, hq / hkv, vl::bwd_per_cu(items, hq / hkv, hkv, n_cu),
+                             max_head_split(hq, hkv));
 }
 
 // Workspace of one backward call: D [Hq, Tq] fp32, then the fp32 dK/dV
@@ -397,7 +400,7 @@ int varlen_attn_fwd(const void* q, const void* k, const void* v, const int32_t* 
     Plan p;
     CallPlans plans;
     const int pass0 = 0;
-    rc = plans.get(causal != 0, cu_seqlens_q, cu_seqlens_k, n_docs,
+    rc = plans.get(causal != 0, cu_seqlens_q, cu_seqlens_k, n_docs, n_heads_q, n_heads_kv,
                    reinterpret_cast<hipStream_t>(stream), 1, &pass0, &p);
     if (rc) return rc;
     vl::AttnShape s{total_q, total_k, n_heads_q, n_heads_kv, head_dim,
@@ -429,7 +432,7 @@ int varlen_attn_fwd_acc(const void* q, const void* k, const void* v, const int32
     Plan p;
     CallPlans plans;
     const int pass0 = 0;
-    rc = plans.get(causal != 0, cu_seqlens_q, cu_seqlens_k, n_docs,
+    rc = plans.get(causal != 0, cu_seqlens_q, cu_seqlens_k, n_docs, n_heads_q, n_heads_kv,
                    reinterpret_cast<hipStream_t>(stream), 1, &pass0, &p);
     if (rc) return rc;
     vl::AttnShape s{total_q, total_k, n_heads_q, n_heads_kv, head_dim,
@@ -503,7 +506,8 @@ int varlen_attn_bwd(const void* q, const void* k, const void* v, const void* out
     Plan pp[2];
     CallPlans plans;
     const int passes[2] = {0, 1};
-    rc = plans.get(causal != 0, cu_seqlens_q, cu_seqlens_k, n_docs, st, 2, passes, pp);
+    rc = plans.get(causal != 0, cu_seqlens_q, cu_seqlens_k, n_docs, n_heads_q, n_heads_kv, st, 2,
+                   passes, pp);
     if (rc) return rc;
     const Plan& pf = pp[0];
     const Plan& pb = pp[1];
@@ -513,6 +517,7 @@ int varlen_attn_bwd(const void* q, const void* k, const void* v, const void* out
                                               align256(size_t(total_q) * size_t(n_heads_q) * 4));
     vl::AttnShape s{total_q, total_k, n_heads_q, n_heads_kv, head_dim,
                     resolve_scale(softmax_scale, head_dim), causal != 0};
+    if (pb.max_slices > split) return fail(VL_EHIP, "internal: the dK/dV list outgrew its workspace");
     hipError_t e = vl::launch_attn_bwd(s, q, k, v, out, dout, lse, pf.map(), pb.map(), split, dq,
                                        dk, dv, delta, dkv_acc, st);
     if (e != hipSuccess) return hip_fail(e, "attn_bwd launch");
@@ -549,7 +554,8 @@ int varlen_attn_bwd_noalloc(const void* q, const void* k, const void* v, const v
     std::vector<vl::DevItem> host[2];
     Plan pl[2];
     for (int i = 0; i < 2; ++i)
-      build_list(i, causal != 0, cu_seqlens_q, cu_seqlens_k, n_docs, host[i], pl[i]);
+      build_list(i, causal != 0, cu_seqlens_q, cu_seqlens_k, n_docs, n_heads_q, n_heads_kv,
+                 host[i], pl[i]);
     const size_t off0 = ws;
     const size_t off1 = off0 + align256(host[0].size() * sizeof(vl::DevItem));
     const size_t need = off1 + align256(host[1].size() * sizeof(vl::DevItem));
@@ -581,6 +587,7 @@ int varlen_attn_bwd_noalloc(const void* q, const void* k, const void* v, const v
     float* dkv_acc = reinterpret_cast<float*>(sc + align256(size_t(total_q) * size_t(n_heads_q) * 4));
     vl::AttnShape s{total_q, total_k, n_heads_q, n_heads_kv, head_dim,
                     resolve_scale(softmax_scale, head_dim), causal != 0};
+    if (pl[1].max_slices > split) return fail(VL_EHIP, "internal: the dK/dV list outgrew its scratch");
     e = vl::launch_attn_bwd(s, q, k, v, out, dout, lse, pl[0].map(), pl[1].map(), split, dq, dk,
                             dv, delta, dkv_acc, st);
     if (e != hipSuccess) return hip_fail(e, "attn_bwd launch");
@@ -949,6 +956,42 @@ int varlen_schedule_export(const int32_t* cu_seqlens_q, const int32_t* cu_seqlen
         items[4 * i + 1] = list[i].tile;
         items[4 * i + 2] = list[i].first;
         items[4 * i + 3] = list[i].count;
+      }
+    }
+    return VL_OK;
+  } catch (const std::exception& ex) {
+    return fail(VL_EINVAL, std::string("internal error: ") + ex.what());
+  }
+}
+
+int varlen_schedule_export_dkdv(const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
+                                int32_t n_docs, int32_t causal, int32_t n_heads_q,
+                                int32_t n_heads_kv, int32_t n_cu, int32_t* entries, int64_t cap,
+                                int64_t* n_entries) {
+  try {
+    g_err.clear();
+    if (!cu_seqlens_q || !cu_seqlens_k || !n_entries) return fail(VL_EINVAL, "null argument");
+    if (n_docs < 0) return fail(VL_EINVAL, "n_docs must be >= 0");
+    if (n_cu <= 0) return fail(VL_EINVAL, "n_cu must be positive");
+    if (n_heads_q <= 0 || n_heads_kv <= 0 || n_heads_q % n_heads_kv)
+      return fail(VL_ESHAPE, "n_heads_q must be a positive multiple of n_heads_kv");
+    std::string err;
+    if (!vl::validate_cu(cu_seqlens_q, n_docs, cu_seqlens_q[n_docs], err))
+      return fail(VL_ESEQLENS, "cu_seqlens_q: " + err);
+    if (!vl::validate_cu(cu_seqlens_k, n_docs, cu_seqlens_k[n_docs], err))
+      return fail(VL_ESEQLENS, "cu_seqlens_k: " + err);
+    const auto docs = vl::doc_table(cu_seqlens_q, cu_seqlens_k, n_docs);
+    const auto items = vl::bwd_items(docs, causal != 0, vl::kBwdBQ, vl::kBwdBK);
+    const auto list = vl::bwd_entries(items, n_heads_q / n_heads_kv, n_heads_kv, n_cu,
+                                      max_head_split(n_heads_q, n_heads_kv));
+    *n_entries = int64_t(list.size());
+    if (entries) {
+      if (cap < int64_t(list.size())) return fail(VL_EWORKSPACE, "entries capacity too small");
+      for (size_t i = 0; i < list.size(); ++i) {
+        const vl::Entry& e = list[i];
+        const int32_t row[6] = {e.item.doc, e.item.tile, e.item.first, e.item.count, e.slice,
+                                e.n_slices};
+        for (int f = 0; f < 6; ++f) entries[6 * i + f] = row[f];
       }
     }
     return VL_OK;

@@ -7,7 +7,7 @@
 //   dS_ij = P_ij (dP_ij - D_i),
 //   dV_j = sum_i P_ij dO_i,  dK_j = scale sum_i dS_ij Q_i,  dQ_i = scale sum_j dS_ij K_j.
 //
-// Two kernels (three with a q-head split), no atomics:
+// Two kernels (three when a key tile's q heads are split), no atomics:
 //   1. dq: the forward's mapping (a lane owns one query): S^T = K Q^T and
 //      dP^T = V dO^T per 64-key tile, then dQ^T += K^T dS^T; the Q, dO and O
 //      tiles arrive in LDS by direct loads and dQ leaves through LDS, all in
@@ -21,10 +21,12 @@
 //      Scores are computed as S = Q K^T so a lane owns one key; the query rows
 //      of the A operand are permuted so P and dS come out of the MFMA already
 //      in the A-operand layout of dV += P^T dO and dK += dS^T Q.
-//   With the q heads of a group split over workgroups, each split stores its
-//   fp32 dK/dV partial and a third kernel adds the partials in split order
-//   (plain stores run at several times the rate of fp32 atomic adds, and the
-//   sum is deterministic).
+//   A key tile whose q-head group would outlast the average per-CU share of
+//   the pass is cut into 2-4 slices of its q heads, one workgroup each; each
+//   slice stores its fp32 dK/dV partial and a third kernel adds the partials
+//   of those tiles in slice order (plain stores run at several times the rate
+//   of fp32 atomic adds, and the sum is deterministic).  The other tiles
+//   write bf16 dK/dV directly.
 // The extra two contractions of (1) replace a zeroed fp32 dQ accumulator, its
 // atomics and a conversion pass, and keep dQ deterministic.
 #include <hip/hip_runtime.h>
@@ -41,18 +43,32 @@ namespace {
 
 constexpr int kThreads = 256;
 
-// dK and dV of a split q-head group: the sum of the splits' fp32 partials
-// ([split][dK, dV][T, H, D]), added in split order (deterministic), -> bf16
+// dK and dV of the kv tiles whose q-head group the dK/dV list cut into
+// slices: the sum of the slices' fp32 partials ([slice][dK, dV][T, H, D]),
+// added in slice order (deterministic), -> bf16.  kConvChunks workgroups per
+// list entry; entries that are not a tile's first slice of several exit.
+constexpr int kConvChunks = 32;
+template <int D>
 __global__ void __launch_bounds__(kThreads)
-f32_to_bf16_kernel(const f32x4* __restrict__ src, u32x2* __restrict__ dk, u32x2* __restrict__ dv,
-                   int64_t n4, int n_split) {
-  for (int64_t i = int64_t(blockIdx.x) * kThreads + threadIdx.x; i < 2 * n4;
-       i += int64_t(gridDim.x) * kThreads) {
-    const int t = i >= n4;
-    const int64_t j = i - t * n4;
-    f32x4 x = src[int64_t(t) * n4 + j];
-    for (int sp = 1; sp < n_split; ++sp) {
-      const f32x4 y = src[(int64_t(sp) * 2 + t) * n4 + j];
+dkv_convert_kernel(const DevItem* __restrict__ items, const f32x4* __restrict__ src,
+                   u32x2* __restrict__ dk, u32x2* __restrict__ dv, int64_t total_k, int hkv) {
+  const DevItem it = items[blockIdx.x / kConvChunks];
+  const int chunk = blockIdx.x % kConvChunks;
+  if (it.n_slices <= 1 || it.slice != 0) return;
+  const int j0 = it.tile * kBwdBK;
+  const int nk = min(kBwdBK, it.lk - j0);
+  if (nk <= 0) return;
+  const int64_t row4 = int64_t(hkv) * (D / 4);            // float4 per key row
+  const int64_t base = (int64_t(it.k_start) + j0) * row4;  // the tile's first key
+  const int64_t n4 = int64_t(nk) * row4;                   // per tensor
+  const int64_t plane = total_k * row4;
+  const int64_t end = 2 * n4 * (chunk + 1) / kConvChunks;
+  for (int64_t i = 2 * n4 * chunk / kConvChunks + threadIdx.x; i < end; i += kThreads) {
+    const int t = i >= n4;                                 // 0: dK, 1: dV
+    const int64_t j = base + (i - t * n4);
+    f32x4 x = src[int64_t(t) * plane + j];
+    for (int sp = 1; sp < it.n_slices; ++sp) {
+      const f32x4 y = src[(int64_t(sp) * 2 + t) * plane + j];
 #pragma unroll
       for (int e = 0; e < 4; ++e) x[e] += y[e];
     }
@@ -129,22 +145,23 @@ attn_bwd_dkdv_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
                      const uint16_t* __restrict__ v, const uint16_t* __restrict__ dout,
                      const float* __restrict__ lse, const float* __restrict__ delta,
                      const DevItem* __restrict__ items,
-                     int hq, int hkv, int head_split, float scale, int causal, int64_t total_q,
+                     int hq, int hkv, float scale, int causal, int64_t total_q,
                      uint16_t* __restrict__ dk, uint16_t* __restrict__ dv,
                      float* __restrict__ dkv_acc, int64_t total_k) {
   constexpr int NKS = D / 16;
   constexpr int NCB = D / 32;
   __shared__ KvSmem<D> sm;
 
-  // workgroup -> (item, kv head, q-head slice) on XCD b % 8's item list
+  // workgroup -> (entry, kv head) on XCD b % 8's entry list; the entry is
+  // its item's q-head slice `split` of n_slices
   const int b = blockIdx.x;
   const int xcd = b & (kXcds - 1);
   const int r = b / kXcds;
-  const int per_item = hkv * head_split;
-  const DevItem it = items[(r / per_item) * kXcds + xcd];
-  const int g = __builtin_amdgcn_readfirstlane((r % per_item) / head_split);
-  const int split = __builtin_amdgcn_readfirstlane(r % head_split);
-  if (it.doc < 0) return;
+  const DevItem it = items[(r / hkv) * kXcds + xcd];
+  const int g = __builtin_amdgcn_readfirstlane(r % hkv);
+  if (it.n_slices == 0) return;   // empty slot
+  const int split = __builtin_amdgcn_readfirstlane(it.slice);
+  const int head_split = __builtin_amdgcn_readfirstlane(it.n_slices);
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -464,7 +481,7 @@ attn_bwd_dq_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ 
   const int r = b / kXcds;
   const DevItem it = items[(r / hq) * kXcds + xcd];
   const int h = __builtin_amdgcn_readfirstlane(r % hq);
-  if (it.doc < 0) return;
+  if (it.n_slices == 0) return;   // empty slot
   const int g = __builtin_amdgcn_readfirstlane(h / (hq / hkv));
 
   const int tid = threadIdx.x;
@@ -690,19 +707,18 @@ hipError_t run_bwd(const AttnShape& s, const uint16_t* q, const uint16_t* k, con
                        s.total_q, dq);
   }
   if (bwd_map.rows > 0) {
-    const dim3 grid(unsigned(bwd_map.rows) * unsigned(kXcds) * unsigned(s.hkv * head_split));
+    const dim3 grid(unsigned(bwd_map.rows) * unsigned(kXcds) * unsigned(s.hkv));
     ProfScope prof("bwd_dkdv", stream);
     hipLaunchKernelGGL((attn_bwd_dkdv_kernel<D>), grid, dim3(kKvThreads), 0, stream, q, k, v, dout,
-                       lse, delta, bwd_map.items, s.hq, s.hkv, head_split, s.scale,
+                       lse, delta, bwd_map.items, s.hq, s.hkv, s.scale,
                        s.causal, s.total_q, dk, dv, dkv_acc, s.total_k);
   }
-  if (head_split > 1 && kv_elems > 0) {
-    const int64_t n4 = kv_elems / 4;
-    const int blocks = int(std::max<int64_t>(1, (2 * n4 + kThreads - 1) / kThreads));
+  if (head_split > 1 && bwd_map.split_rows > 0 && kv_elems > 0) {
+    const dim3 grid(unsigned(bwd_map.split_rows) * unsigned(kXcds) * unsigned(kConvChunks));
     ProfScope prof("bwd_dkv_convert", stream);
-    hipLaunchKernelGGL(f32_to_bf16_kernel, dim3(blocks), dim3(kThreads), 0, stream,
+    hipLaunchKernelGGL((dkv_convert_kernel<D>), grid, dim3(kThreads), 0, stream, bwd_map.items,
                        reinterpret_cast<const f32x4*>(dkv_acc), reinterpret_cast<u32x2*>(dk),
-                       reinterpret_cast<u32x2*>(dv), n4, int(head_split));
+                       reinterpret_cast<u32x2*>(dv), s.total_k, s.hkv);
   }
   return hipGetLastError();
 }

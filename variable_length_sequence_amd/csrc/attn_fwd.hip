@@ -74,7 +74,7 @@ attn_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
   const int r = b / kXcds;
   const DevItem it = items[(r / hq) * kXcds + xcd];
   const int h = __builtin_amdgcn_readfirstlane(r % hq);
-  if (it.doc < 0) return;
+  if (it.n_slices == 0) return;   // empty slot
   const int g = __builtin_amdgcn_readfirstlane(h / (hq / hkv));
 
   const int tid = threadIdx.x;

@@ -55,6 +55,7 @@ constexpr int kXcds = 8;
 struct ItemMap {
   const DevItem* items;  // [rows * kXcds]
   int32_t rows;          // items of the longest XCD list
+  int32_t split_rows;    // dK/dV list: rows up to the last one with a cut item
 };
 
 struct AttnShape {
@@ -72,9 +73,10 @@ hipError_t launch_attn_fwd(const AttnShape& s, const void* q, const void* k, con
                            hipStream_t stream);
 
 // Backward: dQ over the query-tile list, which also stores D_i = dO_i . O_i
-// in delta ([hq, total_q] fp32), then dK/dV over the kv-tile list.  When the q heads of one group are split over
-// head_split > 1 workgroups, dkv_acc holds their fp32 partials
-// [head_split][dK, dV][total_k, hkv, d], summed by a conversion kernel.
+// in delta ([hq, total_q] fp32), then dK/dV over the kv-tile list.  Entries
+// of the dK/dV list cut into n_slices > 1 slices of their q heads (at most
+// head_split) store fp32 partials in dkv_acc, [head_split][dK, dV][total_k,
+// hkv, d], which a conversion kernel adds for those kv tiles.
 constexpr int kMaxHeadSplit = 4;
 hipError_t launch_attn_bwd(const AttnShape& s, const void* q, const void* k, const void* v,
                            const void* o, const void* dout, const float* lse,

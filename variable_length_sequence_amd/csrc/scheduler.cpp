@@ -111,24 +111,61 @@ int64_t issued_pairs(const std::vector<Item>& items, int bq, int bk) {
   return n * int64_t(bq) * bk;
 }
 
-std::vector<DevItem> device_items(const std::vector<Doc>& docs, const std::vector<Item>& items) {
-  std::vector<DevItem> out(items.size());
-  for (size_t i = 0; i < items.size(); ++i) {
-    const Item& it = items[i];
+std::vector<Entry> fwd_entries(const std::vector<Item>& items) {
+  std::vector<Entry> out;
+  out.reserve(items.size());
+  for (const Item& it : items) out.push_back(Entry{it, 0, 1, int64_t(it.count) + 1});
+  return out;
+}
+
+double bwd_per_cu(const std::vector<Item>& items, int grp, int hkv, int n_cu) {
+  int64_t total = 0;
+  for (const Item& it : items) total += it.count;
+  return double(total) * grp * hkv / double(std::max(n_cu, 1));
+}
+
+int item_head_split(int64_t count, int grp, double per_cu, int max_split) {
+  int split = 1;
+  while (split < max_split && double(count) * grp / split > per_cu) split *= 2;
+  return split;
+}
+
+std::vector<Entry> bwd_entries(const std::vector<Item>& items, int grp, int hkv, int n_cu,
+                               int max_split) {
+  const double per_cu = bwd_per_cu(items, grp, hkv, n_cu);
+  std::vector<Entry> out;
+  out.reserve(items.size());
+  for (const Item& it : items) {
+    const int n = item_head_split(it.count, grp, per_cu, max_split);
+    const int64_t work = int64_t(it.count) * (grp / n);
+    for (int s = 0; s < n; ++s) out.push_back(Entry{it, s, n, work + kBwdEntryStartup});
+  }
+  // longest first by the entries' own work (the items came longest first by
+  // count, which is kept among equal weights)
+  std::stable_sort(out.begin(), out.end(),
+                   [](const Entry& a, const Entry& b) { return a.weight > b.weight; });
+  return out;
+}
+
+std::vector<DevItem> device_items(const std::vector<Doc>& docs, const std::vector<Entry>& entries) {
+  std::vector<DevItem> out(entries.size());
+  for (size_t i = 0; i < entries.size(); ++i) {
+    const Item& it = entries[i].item;
     const Doc& d = docs[size_t(it.doc)];
     out[i] = DevItem{int32_t(d.q_start), int32_t(d.lq), int32_t(d.k_start), int32_t(d.lk),
-                     it.tile, it.first, it.count, it.doc};
+                     it.tile, it.first, it.count, int16_t(entries[i].slice),
+                     int16_t(entries[i].n_slices)};
   }
   return out;
 }
 
-std::vector<int32_t> xcd_slots(const std::vector<Item>& items, int n_xcd, int32_t& rows) {
+std::vector<int32_t> xcd_slots(const std::vector<Entry>& entries, int n_xcd, int32_t& rows) {
   std::vector<std::vector<int32_t>> lists(size_t(std::max(n_xcd, 1)));
   std::vector<int64_t> load(lists.size(), 0);
-  for (size_t i = 0; i < items.size(); ++i) {
+  for (size_t i = 0; i < entries.size(); ++i) {
     const size_t x = size_t(std::min_element(load.begin(), load.end()) - load.begin());
     lists[x].push_back(int32_t(i));
-    load[x] += int64_t(items[i].count) + 1;
+    load[x] += entries[i].weight;
   }
   rows = 0;
   for (const auto& l : lists) rows = std::max(rows, int32_t(l.size()));

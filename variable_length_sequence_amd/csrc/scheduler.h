@@ -29,10 +29,22 @@ struct Item {
   int32_t doc, tile, first, count;
 };
 
-// What a kernel reads per work item (self-contained, 32 bytes).
+// What a kernel reads per work item (self-contained, 32 bytes).  On the
+// dK/dV list an item may be cut into n_slices entries that each take slice
+// `slice` of the q heads of its kv head's group; n_slices == 0 marks an empty
+// slot of the XCD layout.
 struct DevItem {
   int32_t q_start, lq, k_start, lk;
-  int32_t tile, first, count, doc;
+  int32_t tile, first, count;
+  int16_t slice, n_slices;
+};
+
+// One entry of a work list: an item, the slice of its q-head group it takes
+// (of n_slices), and its weight for the assignment to XCDs.
+struct Entry {
+  Item item;
+  int32_t slice, n_slices;
+  int64_t weight;
 };
 
 // Validates one cumulative-length array: n_docs + 1 entries, cu[0] == 0,
@@ -49,16 +61,37 @@ int64_t visible_pairs(const std::vector<Doc>& docs, bool causal);
 // Pairs covered by issued tiles per head (full tile area).
 int64_t issued_pairs(const std::vector<Item>& items, int bq, int bk);
 
-std::vector<DevItem> device_items(const std::vector<Doc>& docs, const std::vector<Item>& items);
+// The forward / dQ list as entries: one per item (its q heads are separate
+// workgroups anyway), weight count + 1 (its key tiles plus its start-up).
+std::vector<Entry> fwd_entries(const std::vector<Item>& items);
 
-// Assignment of an LPT-ordered item list to the n_xcd XCDs of the device:
-// each item, in list order, goes to the XCD with the least work so far
-// (weight count + 1: its tiles plus its start-up), so every XCD keeps the
-// longest-first order and all XCDs end within about one short item of each
-// other (round-robin dealing would give the first XCD the longest item of
-// every round).  Returns slots[j * n_xcd + x] = index of the j-th item of XCD
-// x, or -1; rows = the longest XCD list.
-std::vector<int32_t> xcd_slots(const std::vector<Item>& items, int n_xcd, int32_t& rows);
+// The q-head split of the dK/dV pass, item by item.  A dK/dV workgroup runs
+// `count` query steps for every q head of its slice of a kv head's group of
+// grp heads.  per_cu is the average per-CU share of the whole pass, grp hkv
+// times the summed counts over n_cu.  An item whose group would outlast it is
+// cut into 2 or 4 slices of its q heads (at most max_split, a power of two
+// dividing grp) until a slice no longer does; the other items stay whole, so
+// only the cut ones leave fp32 partials for a conversion pass to add.
+double bwd_per_cu(const std::vector<Item>& items, int grp, int hkv, int n_cu);
+int item_head_split(int64_t count, int grp, double per_cu, int max_split);
+
+// The dK/dV list as entries (item_head_split per item, slices in order),
+// ordered by their work count grp / n_slices, longest first, with weight
+// that work plus kBwdEntryStartup (the measured start-up and epilogue of an
+// entry, in query steps of one q head).
+constexpr int64_t kBwdEntryStartup = 2;
+std::vector<Entry> bwd_entries(const std::vector<Item>& items, int grp, int hkv, int n_cu,
+                               int max_split);
+
+std::vector<DevItem> device_items(const std::vector<Doc>& docs, const std::vector<Entry>& entries);
+
+// Assignment of a longest-first entry list to the n_xcd XCDs of the device:
+// each entry, in list order, goes to the XCD with the least weight so far,
+// so every XCD keeps the longest-first order and all XCDs end within about
+// one short entry of each other (round-robin dealing would give the first
+// XCD the longest entry of every round).  Returns slots[j * n_xcd + x] =
+// index of the j-th entry of XCD x, or -1; rows = the longest XCD list.
+std::vector<int32_t> xcd_slots(const std::vector<Entry>& entries, int n_xcd, int32_t& rows);
 
 // One (query chunk, key chunk) block of ring attention over a packed causal
 // batch (HSAP page, Section 3.2, Figure 3).  Fills per-document token counts
