@@ -90,14 +90,19 @@ def test_fp32_output_and_softmax_range():
 
 @pytest.mark.parametrize("d,hq,hkv", [(64, 8, 2), (128, 8, 2)])
 def test_head_split_batches(d, hq, hkv):
-    """One long document among short ones: the dK/dV pass splits each q-head
-    group over workgroups (fp32 partials summed by the convert kernel), for
-    both head dims; full tensors against the oracle."""
+    """One long document among short ones: the dK/dV pass cuts the q-head
+    group of the long document's early key tiles into slices (fp32 partials
+    summed by the convert kernel) while the other tiles keep theirs whole
+    (bf16 written directly), for both head dims; full tensors against the
+    oracle."""
     dev = require_gpu()
     lens = [3000, 257, 131, 64, 500, 1]
     cu = workloads.cu_seqlens(lens)
     d_only = (sum(lens) * hq * 4 + 255) // 256 * 256
     assert vl.bwd_workspace_bytes_cu(cu, cu, hq, hkv, d) > d_only   # the split path runs
+    n_cu = torch.cuda.get_device_properties(0).multi_processor_count
+    cuts = vl.varlen_schedule_export_dkdv(cu, cu, True, hq, hkv, n_cu)[:, 5]
+    assert (cuts > 1).any() and (cuts == 1).any(), "both kinds of key tile"
     w = workloads.Workload(f"split_d{d}", lens, hq=hq, hkv=hkv, d=d, seed=11)
     q, k, v, do = workloads.make_tensors(w)
     say(f"case lens={lens} hq={hq} hkv={hkv} d={d}")

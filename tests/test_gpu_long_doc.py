@@ -6,8 +6,9 @@ plain per-document softmax and its analytic gradient), so the longest
 accumulations are checked element by element: the first key tile's dK/dV
 sum over all 512 query tiles of 32 rows x 8 q heads, and the last query
 tile's O and dQ over 256 key tiles.  With a group of 8 q heads on one kv
-head the backward splits the group over 4 workgroups (their fp32 partials
-added in a fixed order), the path the 393216-token Ulysses share takes at
+head the backward cuts the group of the early key tiles into 4 slices and
+of the middle ones into 2 (their fp32 partials added in a fixed order) and
+keeps the late ones whole, the mix the 393216-token Ulysses share takes at
 full size.  The attention is the one the pages define per document (BASP
 page, Section II-A; HSAP page, Section 2.2.1); its gradient is recomputed
 from the saved LSE (NSP page, Sections 2.3 and 4.2.2).
@@ -32,7 +33,7 @@ def test_one_16k_document_full_tensors():
     q, k, v, do = workloads.make_tensors(w)
     cu = w.cu
     say(f"{w.name}: one document of {w.total} tokens, {w.hq}/{w.hkv} heads, d {w.d}")
-    # the backward takes the split path: D plus four fp32 dK/dV partials
+    # the backward takes the split path: D plus room for four fp32 dK/dV partials
     delta = (w.total * w.hq * 4 + 255) // 256 * 256
     part = (4 * 2 * w.total * w.hkv * w.d * 4 + 255) // 256 * 256
     assert vl.bwd_workspace_bytes_cu(cu, cu, w.hq, w.hkv, w.d) == delta + part

@@ -39,8 +39,8 @@ def _noalloc(q, k, v, o, do, lse, cu, causal=True):
 @pytest.mark.gpu
 def test_noalloc_backward_matches_workspace_backward():
     dev = require_gpu()
-    # one 4096-token document with 32/4 heads (its q-head groups are split:
-    # the scratch holds D and the fp32 dK/dV partials), then a smaller ragged
+    # one 4096-token document with 32/4 heads (the q-head groups of its early
+    # key tiles are cut: the scratch holds D and the fp32 dK/dV partials), then a smaller ragged
     # GQA batch
     big = workloads.Workload("doc4k", [4096], hq=32, hkv=4, d=128, seed=4)
     small = workloads.Workload("ragged", [1, 37, 129, 300, 64], hq=8, hkv=2, d=64, seed=3)
