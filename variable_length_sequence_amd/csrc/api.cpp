@@ -39,8 +39,8 @@ struct Plan {
   int32_t max_count = 0;
   int64_t total_count = 0;
   int32_t max_slices = 1;       // the most slices any item is cut into
-  int32_t split_rows = 0;       // rows up to the last one holding a cut item
-  vl::ItemMap map() const { return vl::ItemMap{dev, rows, split_rows}; }
+  int32_t n_cut = 0;            // cut key tiles, listed after the slots
+  vl::ItemMap map() const { return vl::ItemMap{dev, rows, n_cut}; }
 };
 
 std::mutex g_mu;
@@ -72,8 +72,9 @@ int device_cus();
 
 // pass 0: forward / dQ list (query tiles); pass 1: dK/dV list (key tiles,
 // cut by the q-head split).  Builds the list on the host in XCD slot order (a
-// workgroup reads its entry with one load; an empty slot has n_slices = 0)
-// and fills the plan's counts.
+// workgroup reads its entry with one load; an empty slot has n_slices = 0),
+// followed on the dK/dV list by the first slice of every cut key tile (the
+// conversion pass's list), and fills the plan's counts.
 void build_list(int pass, int causal, const int32_t* cu_q, const int32_t* cu_k, int32_t n_docs,
                 int32_t hq, int32_t hkv, std::vector<vl::DevItem>& host, Plan& p) {
   const std::vector<vl::Doc> docs = vl::doc_table(cu_q, cu_k, n_docs);
@@ -98,7 +99,12 @@ void build_list(int pass, int causal, const int32_t* cu_q, const int32_t* cu_k, 
     if (slots[j] < 0) continue;
     host[j] = di[size_t(slots[j])];
     p.max_slices = std::max<int32_t>(p.max_slices, host[j].n_slices);
-    if (host[j].n_slices > 1) p.split_rows = int32_t(j / vl::kXcds) + 1;
+  }
+  for (const vl::DevItem& e : di) {
+    if (e.n_slices > 1 && e.slice == 0) {
+      host.push_back(e);
+      ++p.n_cut;
+    }
   }
 }
 

@@ -45,16 +45,18 @@ constexpr int kThreads = 256;
 
 // dK and dV of the kv tiles whose q-head group the dK/dV list cut into
 // slices: the sum of the slices' fp32 partials ([slice][dK, dV][T, H, D]),
-// added in slice order (deterministic), -> bf16.  kConvChunks workgroups per
-// list entry; entries that are not a tile's first slice of several exit.
-constexpr int kConvChunks = 32;
+// added in slice order (deterministic), -> bf16.  `cut` lists the first
+// slice of every cut tile; `chunks` workgroups per tile, enough for about one
+// 16-byte group of each tensor per thread, so every load of a tile is in
+// flight at once (the pass is short and latency-bound).
 template <int D>
 __global__ void __launch_bounds__(kThreads)
-dkv_convert_kernel(const DevItem* __restrict__ items, const f32x4* __restrict__ src,
-                   u32x2* __restrict__ dk, u32x2* __restrict__ dv, int64_t total_k, int hkv) {
-  const DevItem it = items[blockIdx.x / kConvChunks];
-  const int chunk = blockIdx.x % kConvChunks;
-  if (it.n_slices <= 1 || it.slice != 0) return;
+dkv_convert_kernel(const DevItem* __restrict__ cut, const f32x4* __restrict__ src,
+                   u32x2* __restrict__ dk, u32x2* __restrict__ dv, int64_t total_k, int hkv,
+                   int chunks) {
+  const DevItem it = cut[blockIdx.x / chunks];
+  const int chunk = blockIdx.x % chunks;
+  if (it.n_slices <= 1) return;
   const int j0 = it.tile * kBwdBK;
   const int nk = min(kBwdBK, it.lk - j0);
   if (nk <= 0) return;
@@ -62,8 +64,8 @@ dkv_convert_kernel(const DevItem* __restrict__ items, const f32x4* __restrict__ 
   const int64_t base = (int64_t(it.k_start) + j0) * row4;  // the tile's first key
   const int64_t n4 = int64_t(nk) * row4;                   // per tensor
   const int64_t plane = total_k * row4;
-  const int64_t end = 2 * n4 * (chunk + 1) / kConvChunks;
-  for (int64_t i = 2 * n4 * chunk / kConvChunks + threadIdx.x; i < end; i += kThreads) {
+  const int64_t end = 2 * n4 * (chunk + 1) / chunks;
+  for (int64_t i = 2 * n4 * chunk / chunks + threadIdx.x; i < end; i += kThreads) {
     const int t = i >= n4;                                 // 0: dK, 1: dV
     const int64_t j = base + (i - t * n4);
     f32x4 x = src[int64_t(t) * plane + j];
@@ -713,12 +715,15 @@ hipError_t run_bwd(const AttnShape& s, const uint16_t* q, const uint16_t* k, con
                        lse, delta, bwd_map.items, s.hq, s.hkv, s.scale,
                        s.causal, s.total_q, dk, dv, dkv_acc, s.total_k);
   }
-  if (head_split > 1 && bwd_map.split_rows > 0 && kv_elems > 0) {
-    const dim3 grid(unsigned(bwd_map.split_rows) * unsigned(kXcds) * unsigned(kConvChunks));
+  if (head_split > 1 && bwd_map.n_cut > 0 && kv_elems > 0) {
+    // 2 kBwdBK hkv D / 4 groups of a tile over kThreads-thread workgroups
+    const int chunks = std::max(1, int(2 * kBwdBK * s.hkv * (D / 4) / kThreads));
+    const dim3 grid(unsigned(bwd_map.n_cut) * unsigned(chunks));
     ProfScope prof("bwd_dkv_convert", stream);
-    hipLaunchKernelGGL((dkv_convert_kernel<D>), grid, dim3(kThreads), 0, stream, bwd_map.items,
+    hipLaunchKernelGGL((dkv_convert_kernel<D>), grid, dim3(kThreads), 0, stream,
+                       bwd_map.items + size_t(bwd_map.rows) * kXcds,
                        reinterpret_cast<const f32x4*>(dkv_acc), reinterpret_cast<u32x2*>(dk),
-                       reinterpret_cast<u32x2*>(dv), s.total_k, s.hkv);
+                       reinterpret_cast<u32x2*>(dv), s.total_k, s.hkv, chunks);
   }
   return hipGetLastError();
 }

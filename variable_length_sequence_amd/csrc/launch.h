@@ -55,7 +55,7 @@ constexpr int kXcds = 8;
 struct ItemMap {
   const DevItem* items;  // [rows * kXcds]
   int32_t rows;          // items of the longest XCD list
-  int32_t split_rows;    // dK/dV list: rows up to the last one with a cut item
+  int32_t n_cut;         // dK/dV list: cut key tiles, at items[rows * kXcds ..]
 };
 
 struct AttnShape {
