@@ -122,11 +122,11 @@ VL_API size_t varlen_attn_bwd_workspace_size(int64_t total_q, int64_t total_k,
 
 /*
  * varlen_attn_bwd_workspace_size_cu - the device workspace varlen_attn_bwd
- * needs for this batch on the current device: D plus the partials of the
- * q-head split it will choose for these cu_seqlens (none when it does not
- * split; the split depends on the batch's key-tile counts and the device's
- * compute-unit count).  Host only.  Arguments as varlen_attn_bwd; 0 for
- * invalid arguments.
+ * needs for this batch on the current device: D plus one fp32 dK/dV partial
+ * per slice of the most finely cut key tile of its q-head split (none when
+ * no tile is cut; which tiles are cut depends on the batch's key-tile counts
+ * and the device's compute-unit count, see varlen_schedule_export_dkdv).
+ * Host only.  Arguments as varlen_attn_bwd; 0 for invalid arguments.
  */
 VL_API size_t varlen_attn_bwd_workspace_size_cu(const int32_t* cu_seqlens_q,
                                          const int32_t* cu_seqlens_k, int32_t n_docs,
@@ -156,7 +156,9 @@ VL_API size_t varlen_attn_bwd_workspace_size_cu(const int32_t* cu_seqlens_q,
  *                it for any batch), 256-byte aligned; contents on entry are
  *                ignored
  * No atomics: results are bitwise deterministic for given inputs (the dK/dV
- * sums over a kv group's q heads run in a fixed order).
+ * sums over a kv group's q heads run in a fixed order, the partials of a cut
+ * key tile are added in slice order).  D is computed by the dQ pass and kept
+ * in the workspace for the dK/dV pass.
  * Errors: as the forward, plus VL_EWORKSPACE.
  */
 VL_API int varlen_attn_bwd(const void* q, const void* k, const void* v,
