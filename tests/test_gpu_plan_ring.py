@@ -128,3 +128,34 @@ def test_plan_cache_off_two_streams():
     for name, i, res in got:
         for key, val in res.items():
             assert torch.equal(val, ref[i][key]), f"{name}: {key} differs"
+
+
+def test_plan_cache_keys_the_head_layout():
+    # the dK/dV list depends on the head counts (which key tiles have their
+    # q-head group cut), so one cu_seqlens pattern with two head layouts gets
+    # two cached lists: each layout's outputs equal its per-call result
+    dev = require_gpu()
+    lens = [3000, 257, 131, 64, 500, 1]
+    cu = workloads.cu_seqlens(lens)
+    n_cu = torch.cuda.get_device_properties(0).multi_processor_count
+    layouts = [(8, 2), (8, 8), (8, 1)]
+    cuts = [int(vl.varlen_schedule_export_dkdv(cu, cu, True, hq, hkv, n_cu)[:, 5].max())
+            for hq, hkv in layouts]
+    assert len(set(cuts)) > 1, cuts   # the layouts really cut differently
+    cases = []
+    for i, (hq, hkv) in enumerate(layouts):
+        w = workloads.Workload(f"heads_{hq}_{hkv}", lens, hq=hq, hkv=hkv, d=128, seed=30 + i)
+        q, k, v, do = (t.to(dev) for t in workloads.make_tensors(w))
+        cases.append((w.name, lens, lens, q, k, v, do, True))
+    prev = vl.set_plan_cache(False)
+    try:
+        ref = {c[0]: _run(c, dev) for c in cases}
+        vl.set_plan_cache(True)
+        vl.cache_clear()
+        got = {c[0]: _run(c, dev) for c in cases + cases}
+    finally:
+        vl.set_plan_cache(prev)
+    for name, res in got.items():
+        for key, val in res.items():
+            assert torch.equal(val, ref[name][key]), f"{name}: {key} differs"
+    say(f"plan cache with head layouts {layouts} (cuts {cuts}) equal to per-call lists")
