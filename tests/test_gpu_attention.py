@@ -88,8 +88,9 @@ def test_fp32_output_and_softmax_range():
     _compare(res, q, k, v, do, lq, lk, True, "fp32-out", bwd=False)
 
 
-@pytest.mark.parametrize("d,hq,hkv", [(64, 8, 2), (128, 8, 2)])
-def test_head_split_batches(d, hq, hkv):
+@pytest.mark.parametrize("d,hq,hkv,causal", [(64, 8, 2, True), (128, 8, 2, True),
+                                              (128, 8, 2, False)])
+def test_head_split_batches(d, hq, hkv, causal):
     """One long document among short ones: the dK/dV pass cuts the q-head
     group of the long document's early key tiles into slices (fp32 partials
     summed by the convert kernel) while the other tiles keep theirs whole
@@ -99,15 +100,15 @@ def test_head_split_batches(d, hq, hkv):
     lens = [3000, 257, 131, 64, 500, 1]
     cu = workloads.cu_seqlens(lens)
     d_only = (sum(lens) * hq * 4 + 255) // 256 * 256
-    assert vl.bwd_workspace_bytes_cu(cu, cu, hq, hkv, d) > d_only   # the split path runs
+    assert vl.bwd_workspace_bytes_cu(cu, cu, hq, hkv, d, causal=causal) > d_only   # the split path runs
     n_cu = torch.cuda.get_device_properties(0).multi_processor_count
-    cuts = vl.varlen_schedule_export_dkdv(cu, cu, True, hq, hkv, n_cu)[:, 5]
+    cuts = vl.varlen_schedule_export_dkdv(cu, cu, causal, hq, hkv, n_cu)[:, 5]
     assert (cuts > 1).any() and (cuts == 1).any(), "both kinds of key tile"
     w = workloads.Workload(f"split_d{d}", lens, hq=hq, hkv=hkv, d=d, seed=11)
     q, k, v, do = workloads.make_tensors(w)
-    say(f"case lens={lens} hq={hq} hkv={hkv} d={d}")
-    res = _run(q, k, v, do, lens, lens, True, dev)
-    _compare(res, q, k, v, do, lens, lens, True, f"split_d{d}")
+    say(f"case lens={lens} hq={hq} hkv={hkv} d={d} causal={causal}")
+    res = _run(q, k, v, do, lens, lens, causal, dev)
+    _compare(res, q, k, v, do, lens, lens, causal, f"split_d{d}_{'causal' if causal else 'full'}")
 
 
 def test_longtail_16k_full():
