@@ -2,7 +2,8 @@
 
 Small and medium packed batches are compared element by element: the tiny
 4-document batch, randomised ragged batches (zero-length and one-token
-documents, Lq != Lk, non-causal, GQA, head_dim 64 and 128), and the whole
+documents, Lq != Lk, non-causal, GQA, head_dim 64 and 128), a seeded sweep
+of batch shapes, and the whole
 16384-token long-tail batch.  Plus invariants that need no oracle: packing
 invariance and re-run determinism (bitwise), single-token documents.
 """
@@ -77,6 +78,34 @@ def test_random_batches(seed, n_docs, lo, hi, hq, hkv, d, causal, ragged):
     say(f"case seed={seed} lq={lq} lk={lk} hq={hq} hkv={hkv} d={d} causal={causal}")
     res = _run(q, k, v, do, lq, lk, causal, dev)
     _compare(res, q, k, v, do, lq, lk, causal, f"seed{seed}")
+
+
+def _sweep_case(seed):
+    """Draw one batch shape from the seed: head dim, GQA group (1, 2, 3, 4 or
+    8 q heads per kv head), causal or not, equal or ragged key lengths, 1-8
+    documents with lengths up to 40, 300 or 1200 tokens."""
+    rng = np.random.default_rng(1000 + seed)
+    d = int(rng.choice([64, 128]))
+    grp = int(rng.choice([1, 2, 3, 4, 8]))
+    hkv = int(rng.integers(1, 4))
+    causal = bool(rng.integers(0, 2))
+    ragged = bool(rng.integers(0, 2))
+    n_docs = int(rng.integers(1, 9))
+    hi = int(rng.choice([40, 300, 1200]))
+    lo = int(rng.integers(0, 2))
+    return rng, n_docs, lo, hi, grp * hkv, hkv, d, causal, ragged
+
+
+@pytest.mark.parametrize("seed", range(32))
+def test_random_sweep(seed):
+    """Seeded sweep over batch shapes (see _sweep_case), full tensors against
+    the oracle, forward and backward."""
+    dev = require_gpu()
+    rng, n_docs, lo, hi, hq, hkv, d, causal, ragged = _sweep_case(seed)
+    lq, lk, q, k, v, do = random_case(rng, n_docs, lo, hi, hq, hkv, d, ragged_k=ragged, seed=seed)
+    say(f"sweep seed={seed} lq={lq} lk={lk} hq={hq} hkv={hkv} d={d} causal={causal}")
+    res = _run(q, k, v, do, lq, lk, causal, dev)
+    _compare(res, q, k, v, do, lq, lk, causal, f"sweep{seed}")
 
 
 def test_fp32_output_and_softmax_range():
