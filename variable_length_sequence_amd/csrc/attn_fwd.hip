@@ -10,7 +10,12 @@
 // Mapping (one workgroup = one work item x one q head; 4 waves):
 //   * a work item is a 128-row query tile of one document plus the number of
 //     64-row key tiles it needs (tiles past the causal diagonal are never
-//     listed);  wave w owns query rows 32w .. 32w+31 of the tile;
+//     listed); the kernel runs them as 32-key tiles, skipping a last half
+//     that no query of the item sees;  wave w owns query rows 32w .. 32w+31;
+//   * three workgroups share a compute unit (48 KB of LDS and at most 168
+//     VGPRs each), so each SIMD interleaves three waves: a third wave hides
+//     more of each wave's softmax and load latency than pairing matrix and
+//     vector work inside one wave did with 64-key tiles at two waves;
 //   * scores are computed transposed, S^T = K Q^T, on 32x32x16 bf16 MFMAs, so
 //     each lane owns one query (its column) and row statistics need only one
 //     exchange with the other half-wave;
@@ -23,9 +28,9 @@
 //     double-buffered and filled by direct global->LDS loads issued one tile
 //     ahead (one barrier per tile, no staging registers); the tile loop is
 //     unrolled by two so both buffers have fixed addresses;
-//   * the Q tile also arrives by direct loads (whole rows, into the buffer
-//     the second key tile will use) and each wave reads its Q fragments from
-//     LDS; the epilogue stages each wave's 32 x D block of O in LDS and writes
+//   * the Q tile also arrives by direct loads (whole rows, into the second
+//     key buffer and a third one beside it) and each wave reads its Q
+//     fragments from LDS; the epilogue stages each wave's 32 x D block of O in LDS and writes
 //     whole rows of 16-byte chunks (both replace scattered 16- and 8-byte
 //     accesses of 32 rows per instruction);
 //   * work items are ordered longest first and the workgroup id is remapped
@@ -43,21 +48,23 @@ namespace vl {
 namespace {
 
 constexpr int BQ = kFwdBQ;  // 128
-constexpr int BK = kFwdBK;  // 64
+constexpr int BK = kFwdBK / 2;   // 32 keys per tile (the work lists count 64-key tiles)
 constexpr int kThreads = 256;
 
 template <int D>
 struct FwdSmem {
-  // double-buffered K and V tiles, row-major with swizzled chunks; key row r
-  // is kept at LDS row swap_bits23(r) (the row order the MFMA operands want)
-  uint16_t k[2][BK * D];
-  uint16_t v[2][BK * D];
+  // [buffer][K, V]: double-buffered K and V tiles (buffers 0 and 1),
+  // row-major with swizzled chunks; key row r is kept at LDS row
+  // swap_bits23(r) (the row order the MFMA operands want).  Buffers 1 and 2
+  // (64 rows each) take the Q tile before the loop; buffer 2 and the buffer
+  // the last key tile did not use stage the epilogue.
+  uint16_t kv[3][2][BK * D];
 };
 
 // OUT: kOutBf16 / kOutF32 write O and LSE; kOutAcc folds them into fp32
 // running (O, LSE) accumulators (see the epilogue).
 template <int D, int OUT>
-__global__ void __launch_bounds__(kThreads, 2)
+__global__ void __launch_bounds__(kThreads, 3)
 attn_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
                 const uint16_t* __restrict__ v, const DevItem* __restrict__ items,
                 int hq, int hkv, float scale, int causal,
@@ -91,11 +98,11 @@ attn_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
   const int64_t kv_tok = int64_t(hkv) * D;
   const float c = scale * kLog2e;
 
-  // The Q tile arrives by direct loads into LDS buffer 1 (free until the
-  // prefetch of key tile 1): rows 0-63 in its K half, rows 64-127 in its V
-  // half; rows past the document repeat its last row.
-  load_rows128_lds<D>(q + (int64_t(it.q_start) + q0) * q_tok + int64_t(h) * D,
-                      uint32_t(q_tok * 2), lq - q0, lds_addr(sm.k[1]), lds_addr(sm.v[1]), w, lane);
+  // The Q tile arrives by direct loads into LDS buffers 1 (rows 0-63; free
+  // until the prefetch of key tile 1) and 2 (rows 64-127); rows past the
+  // document repeat its last row.
+  load_rows128_lds<D>(q + (int64_t(it.q_start) + q0) * q_tok + int64_t(h) * D, uint32_t(q_tok * 2),
+                      lq - q0, lds_addr(sm.kv[1][0]), lds_addr(sm.kv[2][0]), w, lane);
 
   bf16x8 qf[NKS];
   f32x16 acc[NCB];
@@ -117,6 +124,10 @@ attn_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
   // first and last query rows of this wave (for skipping / masking)
   const int wq_first = q0 + w * 32;
   const int wq_last = min(q0 + w * 32 + 31, lq - 1);
+  // 32-key tiles this item needs: up to the last key its last query sees
+  const int last_q = min(q0 + BQ, lq) - 1;
+  const int kend = causal ? min(lk, last_q + off + 1) : lk;
+  const int n_kv = kend > 0 ? min(2 * it.count, (kend + BK - 1) / BK) : 0;
 
   // one key tile; the buffer index is a compile-time constant so every LDS
   // address is a loop-invariant register plus an immediate offset
@@ -127,56 +138,50 @@ attn_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     // is done with the other buffer (read during tile kt - 1)
     __builtin_amdgcn_s_waitcnt(kWaitAll);
     __syncthreads();
-    if (kt + 1 < it.count) {
-      loader.load_from(knext, vnext, lk - kv0 - BK, uint32_t(kv_tok * 2), lds_addr(sm.k[buf ^ 1]),
-                       lds_addr(sm.v[buf ^ 1]), w, lane);
+    if (kt + 1 < n_kv) {
+      loader.load_from(knext, vnext, lk - kv0 - BK, uint32_t(kv_tok * 2), lds_addr(sm.kv[buf ^ 1][0]),
+                       lds_addr(sm.kv[buf ^ 1][1]), w, lane);
       knext += kv_step;
       vnext += kv_step;
     }
-    const uint16_t* ks = sm.k[buf];
-    const uint16_t* vs = sm.v[buf];
+    const uint16_t* ks = sm.kv[buf][0];
+    const uint16_t* vs = sm.kv[buf][1];
 
     // wave-uniform: skip tiles no query of this wave can see
     const bool wave_live = (wq_first < lq) && (!causal || kv0 <= wq_last + off);
     if (!wave_live) return;
     const bool need_mask = (kv0 + BK > lk) || (causal && kv0 + BK - 1 > wq_first + off);
-    // key kv0 + 32 kb + 8 half + e (e = 16 (i / 8) + i % 8) of S^T half kb
-    // is visible iff e <= lim - kv0 - 32 kb - 8 half
+    // key kv0 + 8 half + e (e = 16 (i / 8) + i % 8) of S^T is visible iff
+    // e <= lim - kv0 - 8 half
     const int lim = causal ? min(lk - 1, qrow + off) : lk - 1;
-    auto mask = [&](f32x16& x, int kb) {
-      const int thr = lim - kv0 - 32 * kb - 8 * half;
+    auto mask = [&](f32x16& x) {
+      const int thr = lim - kv0 - 8 * half;
 #pragma unroll
       for (int i = 0; i < 16; ++i)
         if (16 * (i >> 3) + (i & 7) > thr) x[i] = -INFINITY;
     };
 
-    // The tile runs as four MFMA blocks of eight, each paired with work of
-    // another block so the matrix pipe and the VALU run together:
-    //   A: S^T of keys 0-31          | K reads
-    //   B: S^T of keys 32-63         | K reads, V^T reads, softmax of keys 0-31
-    //   C: O^T += V^T P^T, keys 0-31 | V^T reads, softmax of keys 32-63
-    //   D: O^T += V^T P^T, keys 32-63
-    // Each 32-key half updates the running max on its own (online softmax is
-    // order free), so the rescale decision of a half only waits for its own
-    // scores.
+    // A tile: S^T = K Q^T (8 MFMAs at d = 128), the softmax, O^T += V^T P^T
+    // (8 MFMAs).  K fragments of the score chain are read two ahead and the
+    // V^T fragments of the output chain two ahead, the first two before the
+    // softmax; the other waves of the SIMD fill the gaps.
     auto kfrag = [&](int f) {
-      return as_bf16x8(*reinterpret_cast<const u32x4*>(
-          &ks[SwzTile<D>::chunk((f / NKS) * 32 + l32, 2 * (f % NKS) + half)]));
+      return as_bf16x8(*reinterpret_cast<const u32x4*>(&ks[SwzTile<D>::chunk(l32, 2 * f + half)]));
     };
     // V^T operand of step j (keys 16 j .. 16 j + 15): dims 32 cb + l32
     auto vfrag = [&](int cb, int j) { return tr_frag<D>(vs, lane, 16 * j, 32 * cb); };
 
-    // softmax of one half: P (bf16, two 16-key steps), the half's reference
-    // max and row sum; returns whether the reference max moved
+    // softmax of the tile: P (bf16, two 16-key steps), the reference max and
+    // the tile's row sum; returns whether the reference max moved
     float m_use = m_run, psum = 0.f;
-    auto softmax_half = [&](const f32x16& x, bf16x8* p) {
+    auto softmax = [&](const f32x16& x, bf16x8* p) {
       float mx = -INFINITY;
 #pragma unroll
       for (int i = 0; i < 16; ++i) mx = fmaxf(mx, x[i]);
       mx = halves_max(mx);
       // m_run is the reference max of the exponent.  It moves (and O and l
       // are rescaled) only when the running max exceeds it by more than 2^8
-      // in probability, so p <= 256 and most halves skip the rescale.
+      // in probability, so p <= 256 and most tiles skip the rescale.
       const float m_new = fmaxf(m_run, mx);
       const bool grow = (m_new - m_run) * c > 8.f;   // false while both are -inf
       m_use = grow ? m_new : m_run;
@@ -198,7 +203,7 @@ attn_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     };
     // A lane that has seen no visible key yet holds O = 0 and l = 0, so its
     // first reference max needs no rescale (the first tile of every item).
-    auto commit_half = [&](bool grow) {
+    auto commit = [&](bool grow) {
       const bool scale_acc = grow && m_run != -INFINITY;
       if (__ballot(scale_acc)) {
         const float alpha = scale_acc ? __builtin_amdgcn_exp2f((m_run - m_use) * c) : 1.f;
@@ -212,83 +217,46 @@ attn_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
       l_run += psum;
     };
 
-    constexpr int kPf = 4;   // K fragments in flight
+    constexpr int kPf = 2;   // K fragments in flight
+    constexpr int kVa = 2;   // V^T fragments in flight
     bf16x8 kr[kPf];
-    // Block A is fenced step by step: with only instruction kinds pinned, the
-    // scheduler filled its read slots with later reads and sank each K read
-    // to just before its MFMA (2 % slower on a 32K document).
+    // The score chain is fenced step by step: with only instruction kinds
+    // pinned, the scheduler filled its read slots with later reads and sank
+    // each K read to just before its MFMA.
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int f = 0; f < kPf; ++f) kr[f] = kfrag(f);
     __builtin_amdgcn_sched_barrier(0);
-    // A: S^T of keys 0-31
-    f32x16 s0, s1;
+    f32x16 st;
 #pragma unroll
     for (int f = 0; f < NKS; ++f) {
       const bf16x8 a = kr[f % kPf];
-      s0 = mfma32(a, qf[f], f == 0 ? f32x16{} : s0);
-      kr[f % kPf] = kfrag(f + kPf);
+      st = mfma32(a, qf[f], f == 0 ? f32x16{} : st);
+      if (f + kPf < NKS) kr[f % kPf] = kfrag(f + kPf);
       __builtin_amdgcn_sched_barrier(0);
     }
-    if (need_mask) mask(s0, 0);
-    // B: S^T of keys 32-63, V^T of keys 0-31 requested, softmax of keys 0-31
-    bf16x8 vr[2 * NCB];
-    bf16x8 p0[2];
-    bool g0;
-    {
+    if (need_mask) mask(st);
+    // O^T += V^T P^T: MFMA i takes V^T fragment (cb, j) = (i % NCB, i / NCB)
+    bf16x8 vr[kVa];
 #pragma unroll
-      for (int f = NKS; f < 2 * NKS; ++f) {
-        const bf16x8 a = kr[f % kPf];
-        if (f + kPf < 2 * NKS) kr[f % kPf] = kfrag(f + kPf);
-        s1 = mfma32(a, qf[f - NKS], f == NKS ? f32x16{} : s1);
-      }
+    for (int i = 0; i < kVa; ++i) vr[i] = vfrag(i % NCB, i / NCB);
+    bf16x8 pt[2];
+    commit(softmax(st, pt));
 #pragma unroll
-      for (int i = 0; i < 2 * NCB; ++i) vr[i] = vfrag(i % NCB, i / NCB);
-      g0 = softmax_half(s0, p0);
-      // per MFMA: its K read (first four), two V^T reads, ~10 VALU
-#pragma unroll
-      for (int f = 0; f < NKS; ++f) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
-        if (f < kPf) __builtin_amdgcn_sched_group_barrier(0x100, 1, 1);
-        __builtin_amdgcn_sched_group_barrier(0x100, 2 * (2 * NCB) / NKS, 1);
-        __builtin_amdgcn_sched_group_barrier(0x002, 10, 1);
-      }
+    for (int i = 0; i < 2 * NCB; ++i) {
+      acc[i % NCB] = mfma32(vr[i % kVa], pt[i / NCB], acc[i % NCB]);
+      if (i + kVa < 2 * NCB) vr[i % kVa] = vfrag((i + kVa) % NCB, (i + kVa) / NCB);
     }
-    commit_half(g0);
-    if (need_mask) mask(s1, 1);
-    // C: O^T += V^T P^T for keys 0-31, V^T of keys 32-63 requested, softmax
-    // of keys 32-63
-    bf16x8 p1[2];
-    bool g1;
-    {
-#pragma unroll
-      for (int i = 0; i < 2 * NCB; ++i) {
-        acc[i % NCB] = mfma32(vr[i], p0[i / NCB], acc[i % NCB]);
-        vr[i] = vfrag(i % NCB, 2 + i / NCB);
-      }
-      g1 = softmax_half(s1, p1);
-#pragma unroll
-      for (int i = 0; i < 2 * NCB; ++i) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 2);
-        __builtin_amdgcn_sched_group_barrier(0x100, 2, 2);
-        __builtin_amdgcn_sched_group_barrier(0x002, 10, 2);
-      }
-    }
-    commit_half(g1);
-    // D: O^T += V^T P^T for keys 32-63
-#pragma unroll
-    for (int i = 0; i < 2 * NCB; ++i) acc[i % NCB] = mfma32(vr[i], p1[i / NCB], acc[i % NCB]);
   };
 
-  const int n_kv = it.count;
   if (n_kv > 0)
-    loader.load(kbase, vbase, kv_tok, 0, lk, lds_addr(sm.k[0]), lds_addr(sm.v[0]), w, lane);
+    loader.load(kbase, vbase, kv_tok, 0, lk, lds_addr(sm.kv[0][0]), lds_addr(sm.kv[0][1]), w, lane);
   // Q fragments (B operand of S^T = K Q^T): query l32, dims 16s + 8 half .. +8
   __builtin_amdgcn_s_waitcnt(kWaitAll);
   __syncthreads();
   {
     const int row = w * 32 + l32;
-    const uint16_t* qs = row < 64 ? sm.k[1] : sm.v[1];
+    const uint16_t* qs = row < 64 ? sm.kv[1][0] : sm.kv[2][0];
 #pragma unroll
     for (int s = 0; s < NKS; ++s)
       qf[s] = as_bf16x8(*reinterpret_cast<const u32x4*>(&qs[SwzTile<D>::chunk(row & 63, 2 * s + half)]));
@@ -306,11 +274,14 @@ attn_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
   if constexpr (OUT == kOutBf16) {
     // each wave stages its 32 x D block of O in LDS and writes whole rows of
     // 16-byte chunks (chunk c of row r sits at chunk c ^ (r % (D / 8))).  The
-    // staging goes to the K/V buffer the last key tile did not use: every
-    // wave is done with it since that tile's barrier and no load went into
-    // it, so no wave waits for the others here.
+    // staging goes to buffer 2 (waves 2, 3) and to the K/V buffer the last
+    // key tile did not use (waves 0, 1): every wave is done with both since
+    // that tile's barrier and no load went into them, so no wave waits for
+    // the others here, except in an item without key tiles, whose Q
+    // fragments other waves may still be reading from buffer 2.
     const int fb = n_kv & 1;
-    uint32_t* stg = reinterpret_cast<uint32_t*>(w < 2 ? &sm.k[fb][0] : &sm.v[fb][0]) +
+    if (n_kv == 0) __syncthreads();
+    uint32_t* stg = reinterpret_cast<uint32_t*>(w < 2 ? &sm.kv[fb][0][0] : &sm.kv[2][0][0]) +
                     (w & 1) * (32 * D / 2);
     constexpr int RCH = D / 8;
 #pragma unroll

@@ -41,15 +41,15 @@ hipError_t launch_lse_merge(int32_t n_parts, const void* const* o_parts,
 
 // Tile sizes of the attention kernels (rows of a query tile / key tile).
 constexpr int kFwdBQ = 128;   // forward and dQ kernels: 4 waves x 32 queries
-constexpr int kFwdBK = 64;
+constexpr int kFwdBK = 64;    // key tiles of their work list (the forward runs halves)
 constexpr int kBwdBQ = 32;    // dK/dV kernel: query rows per step
 constexpr int kBwdBK = 128;   // dK/dV kernel: 4 waves x 32 keys
 
 // The work items of one pass, laid out by their assignment to the 8 XCDs:
 // workgroup b runs on XCD b % 8 (dispatch order), and the j-th item of XCD x
-// is items[j * 8 + x] (doc < 0: none), so a workgroup finds its item with one
-// load.  Every item is run for units_per_item consecutive workgroups of its
-// XCD (q heads, or kv heads x head slices).
+// is items[j * 8 + x] (n_slices == 0: none), so a workgroup finds its item
+// with one load.  Every item is run by consecutive workgroups of its XCD, one
+// per q head (forward, dQ) or per kv head (a dK/dV entry, one q-head slice).
 constexpr int kXcds = 8;
 
 struct ItemMap {
