@@ -108,6 +108,24 @@ def test_random_sweep(seed):
     _compare(res, q, k, v, do, lq, lk, causal, f"sweep{seed}")
 
 
+@pytest.mark.parametrize("causal,ragged", [(True, False), (False, False), (True, True), (False, True)])
+def test_tile_boundary_lengths(causal, ragged):
+    """Documents one short of, at and one past the 32-, 64- and 128-row tile
+    edges (the forward runs 32-key tiles from lists of 64-key tiles and drops a
+    last half no query sees); with ragged key lengths the causal diagonal is
+    shifted both ways (Lq < Lk, and Lq > Lk with leading rows that see no
+    key).  Full tensors against the oracle."""
+    dev = require_gpu()
+    lq = [31, 32, 33, 63, 64, 65, 95, 96, 97, 127, 128, 129, 191, 192, 193, 1]
+    lk = [l + d for l, d in zip(lq, [0, 1, -31, 32, -33, 64, 3, -50, 97, 2, -64, 31, 1, 0, -63, 40])] \
+        if ragged else list(lq)
+    w = workloads.Workload("edges", lq, hq=4, hkv=2, d=128, seed=21)
+    q, k, v, do = workloads.make_tensors(w, tq=sum(lq), tk=sum(lk))
+    say(f"edges lq={lq} lk={lk} causal={causal}")
+    res = _run(q, k, v, do, lq, lk, causal, dev)
+    _compare(res, q, k, v, do, lq, lk, causal, f"edges_{'causal' if causal else 'full'}{'_ragged' if ragged else ''}")
+
+
 def test_fp32_output_and_softmax_range():
     dev = require_gpu()
     rng = np.random.default_rng(11)
