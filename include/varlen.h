@@ -320,6 +320,9 @@ VL_API int basp_shard(int32_t rank, int32_t world, int32_t batch, int64_t seq_le
  * visible pair are skipped (the "N" blocks of the HSAP page, Figure 3).
  *
  *   pass 0 (forward):  items[4*i..] = (doc, q_tile, first kv tile, kv tiles)
+ *                      (the forward kernel runs each listed kv tile as two of
+ *                      *bk / 2 keys and skips a last half that no query of
+ *                      the item sees; the dQ kernel runs the same list whole)
  *   pass 1 (backward): items[4*i..] = (doc, kv_tile, first q tile, q tiles)
  *   ordered by decreasing tile count, then doc, then tile.
  *   items        host int32 [4 * cap], or NULL to query *n_items only
